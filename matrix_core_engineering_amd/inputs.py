@@ -1,0 +1,192 @@
+"""Seeded synthetic GEMM inputs, shared by the tests, the smoke check and the
+benchmark.  This module holds no GEMM arithmetic: it only draws numbers and
+stores them in the byte formats the library reads (bf16 bits, E4M3FN codes,
+E8M0 scale bytes, fp32 or bf16 C0), in storage order.
+
+Every draw uses its own ``torch.Generator`` seeded with ``seed*1000 + t``
+(t: A=0, B=1, C0=2, SA=3, SB=4) and fills the operand in its *storage* order,
+so a column-major B is drawn as an N x K array.  Rounding to bf16 / E4M3FN is
+torch's round-to-nearest-even on the CPU.
+
+The five standard workloads:
+  1  single tile      128x128x64, A,B row-major, U[-1,1], fp32 out, a=1 b=0
+  2  square           4096^3, A row, B col, N(0,1), bf16 out, a=1 b=0
+  3  ragged           4093x3001x1027, A,B row, U[-1,1], fp32 out, a=.5 b=1,
+                      C0 ~ U[-1,1] fp32
+  4  large            8192^3, A row, B col, N(0, 0.02^2), bf16 out, a=1 b=0
+  5  MX-fp8           8192^3, A row, B col (K-contiguous), E4M3FN from
+                      U[-448,448], one E8M0 scale per 32 K with exponent
+                      uniform over the integers -8..8, bf16 out, a=1 b=0
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+BF16 = 0
+E4M3FN = 1
+OUT_F32 = 0
+OUT_BF16 = 1
+MX_BLOCK = 32
+
+
+@dataclass
+class Problem:
+    """One GEMM problem in storage form (all arrays are CPU numpy)."""
+    M: int
+    N: int
+    K: int
+    fmt: int                 # BF16 or E4M3FN
+    A: np.ndarray            # uint16 (bf16 bits) or uint8 (E4M3FN codes)
+    lda: int
+    a_col_major: bool
+    B: np.ndarray
+    ldb: int
+    b_col_major: bool
+    C0: Optional[np.ndarray]  # float32 or uint16 (bf16 bits); None when beta==0
+    ldc: int
+    c_col_major: bool
+    c_dtype: int             # OUT_F32 or OUT_BF16
+    alpha: float
+    beta: float
+    SA: Optional[np.ndarray] = None   # uint8 E8M0, M x ld_sa row-major
+    ld_sa: int = 0
+    SB: Optional[np.ndarray] = None   # uint8 E8M0, N x ld_sb row-major
+    ld_sb: int = 0
+    name: str = ""
+    extra: dict = field(default_factory=dict)
+
+    def oracle_kwargs(self):
+        return dict(M=self.M, N=self.N, K=self.K, A=self.A, lda=self.lda,
+                    a_col_major=self.a_col_major, B=self.B, ldb=self.ldb,
+                    b_col_major=self.b_col_major, C0=self.C0, ldc=self.ldc,
+                    c_col_major=self.c_col_major, c_dtype=self.c_dtype,
+                    alpha=self.alpha, beta=self.beta, fmt=self.fmt,
+                    SA=self.SA, ld_sa=self.ld_sa, SB=self.SB, ld_sb=self.ld_sb)
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+
+def _gen(seed, t):
+    return torch.Generator().manual_seed(int(seed) * 1000 + t)
+
+
+def _storage_shape(rows, cols, col_major, ld):
+    """(outer, inner) of a rows x cols matrix stored with leading dim ld."""
+    if col_major:
+        return cols, ld
+    return rows, ld
+
+
+def to_bf16_bits(x):
+    """float tensor -> uint16 numpy array of bf16 bits (RNE)."""
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def to_e4m3fn_codes(x):
+    """float tensor -> uint8 numpy array of E4M3FN codes (RNE, saturating
+    the draw range +-448 exactly onto the largest finite code)."""
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _draw(dist, shape, g, lo=-1.0, hi=1.0, std=1.0):
+    if dist == "uniform":
+        return torch.rand(shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
+    if dist == "normal":
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+    if dist == "int":
+        return torch.randint(int(lo), int(hi) + 1, shape, generator=g).to(torch.float32)
+    raise ValueError(dist)
+
+
+def _operand(rows, cols, col_major, ld, fmt, dist, g, **kw):
+    outer, inner = _storage_shape(rows, cols, col_major, ld)
+    x = _draw(dist, (outer, inner), g, **kw)
+    # padding columns beyond the logical extent hold NaN in bf16 and the NaN
+    # code in fp8, so a kernel that reads them shows up in the result
+    logical_inner = rows if col_major else cols
+    if inner > logical_inner:
+        x[:, logical_inner:] = float("nan")
+    return to_bf16_bits(x) if fmt == BF16 else to_e4m3fn_codes(x)
+
+
+def make_problem(M, N, K, *, fmt=BF16, a_col_major=False, b_col_major=True,
+                 c_col_major=False, c_dtype=OUT_BF16, alpha=1.0, beta=0.0,
+                 lda=None, ldb=None, ldc=None, dist="normal", std=1.0,
+                 lo=-1.0, hi=1.0, c_dist="uniform", seed=0,
+                 scale_exp_lo=-8, scale_exp_hi=8, ld_sa=None, ld_sb=None,
+                 name=""):
+    """Draws one problem.  dist is 'uniform' (U[lo,hi]), 'normal' (N(0,std^2))
+    or 'int' (integers lo..hi).  Leading dimensions default to dense."""
+    a_inner = M if a_col_major else K
+    b_inner = K if b_col_major else N
+    c_inner = M if c_col_major else N
+    lda = a_inner if lda is None else lda
+    ldb = b_inner if ldb is None else ldb
+    ldc = c_inner if ldc is None else ldc
+    lda, ldb, ldc = max(lda, 1), max(ldb, 1), max(ldc, 1)
+    A = _operand(M, K, a_col_major, lda, fmt, dist, _gen(seed, 0), lo=lo, hi=hi, std=std)
+    B = _operand(K, N, b_col_major, ldb, fmt, dist, _gen(seed, 1), lo=lo, hi=hi, std=std)
+    C0 = None
+    if beta != 0.0:
+        outer = N if c_col_major else M
+        c = _draw(c_dist, (outer, ldc), _gen(seed, 2), lo=-1.0, hi=1.0)
+        C0 = c.numpy().astype(np.float32) if c_dtype == OUT_F32 else to_bf16_bits(c)
+    SA = SB = None
+    if fmt == E4M3FN:
+        kb = (K + MX_BLOCK - 1) // MX_BLOCK
+        ld_sa = max(kb, 1) if ld_sa is None else ld_sa
+        ld_sb = max(kb, 1) if ld_sb is None else ld_sb
+        SA = (torch.randint(scale_exp_lo, scale_exp_hi + 1, (M, ld_sa),
+                            generator=_gen(seed, 3)) + 127).to(torch.uint8).numpy()
+        SB = (torch.randint(scale_exp_lo, scale_exp_hi + 1, (N, ld_sb),
+                            generator=_gen(seed, 4)) + 127).to(torch.uint8).numpy()
+    else:
+        ld_sa = ld_sb = 0
+    return Problem(M=M, N=N, K=K, fmt=fmt, A=A, lda=lda, a_col_major=a_col_major,
+                   B=B, ldb=ldb, b_col_major=b_col_major, C0=C0, ldc=ldc,
+                   c_col_major=c_col_major, c_dtype=c_dtype, alpha=float(alpha),
+                   beta=float(beta), SA=SA, ld_sa=ld_sa, SB=SB, ld_sb=ld_sb,
+                   name=name)
+
+
+# The five standard workloads, as keyword arguments of make_problem.
+CONFIGS = {
+    1: dict(M=128, N=128, K=64, a_col_major=False, b_col_major=False,
+            c_dtype=OUT_F32, alpha=1.0, beta=0.0, dist="uniform",
+            name="single_tile_128x128x64_bf16"),
+    2: dict(M=4096, N=4096, K=4096, a_col_major=False, b_col_major=True,
+            c_dtype=OUT_BF16, alpha=1.0, beta=0.0, dist="normal", std=1.0,
+            name="square_4096_bf16"),
+    3: dict(M=4093, N=3001, K=1027, a_col_major=False, b_col_major=False,
+            c_dtype=OUT_F32, alpha=0.5, beta=1.0, dist="uniform",
+            name="ragged_4093x3001x1027_bf16"),
+    4: dict(M=8192, N=8192, K=8192, a_col_major=False, b_col_major=True,
+            c_dtype=OUT_BF16, alpha=1.0, beta=0.0, dist="normal", std=0.02,
+            name="large_8192_bf16"),
+    5: dict(M=8192, N=8192, K=8192, fmt=E4M3FN, a_col_major=False,
+            b_col_major=True, c_dtype=OUT_BF16, alpha=1.0, beta=0.0,
+            dist="uniform", lo=-448.0, hi=448.0, name="mx_fp8_8192"),
+}
+
+
+def config_problem(idx, seed=None):
+    """The standard workload idx (1..5), seeded with idx unless given."""
+    kw = dict(CONFIGS[idx])
+    return make_problem(seed=idx if seed is None else seed, **kw)
+
+
+def integer_problem(M, N, K, *, fmt=BF16, seed=0, **kw):
+    """Exact-integer inputs: entries in -4..4 (and MX scale exponents 0..2),
+    so every partial sum is an integer well below 2^24 and any summation
+    order gives the same fp32 value."""
+    kw.setdefault("dist", "int")
+    kw.setdefault("lo", -4)
+    kw.setdefault("hi", 4)
+    if fmt == E4M3FN:
+        kw.setdefault("scale_exp_lo", 0)
+        kw.setdefault("scale_exp_hi", 2)
+    return make_problem(M, N, K, fmt=fmt, seed=seed, **kw)

@@ -1,0 +1,147 @@
+"""Plain fp64 CPU reference GEMM -- test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It loads ``liboracle.so`` (built by gcc from
+``oracle.c`` alone) and shares nothing with the HIP library.
+
+What it computes is the plain definition C <- alpha*op(A)*op(B) + beta*C0 with
+exact fp64 decoding of bf16 / E4M3FN / E8M0 inputs and fp64 sums over k in
+order (the baseline contract of "B200 GEMM Optimization Ladder", section E
+step 1; block-scaled operands as in "B200 TMEM Lifecycle Planner", section A1
+case 2).  ``check`` applies the acceptance bound to a GPU result.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH, build_oracle
+
+BF16 = 0
+E4M3FN = 1
+OUT_F32 = 0
+OUT_BF16 = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build_oracle()
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    common = [i64, i64, i64,
+              i32, vp, i64, i32, vp, i64,
+              i32, vp, i64, i32, vp, i64,
+              vp, i64, i32, i32, f32, f32]
+    lib.oracle_gemm_rows.argtypes = common + [i64, i64, vp, vp]
+    lib.oracle_gemm_rows.restype = i32
+    lib.oracle_gemm_entries.argtypes = common + [i64, vp, vp, vp, vp]
+    lib.oracle_gemm_entries.restype = i32
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
+    lib.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_to_f64.restype = ctypes.c_double
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def num_threads():
+    return _load().oracle_num_threads()
+
+
+def bf16_to_f64(code):
+    return _load().oracle_bf16_to_f64(int(code))
+
+
+def e4m3fn_to_f64(code):
+    return _load().oracle_e4m3fn_to_f64(int(code))
+
+
+def e8m0_to_f64(code):
+    return _load().oracle_e8m0_to_f64(int(code))
+
+
+def _arr(x, dtype):
+    """Host numpy view of x (numpy array or CPU torch tensor) with the given
+    storage dtype; returns (array, pointer) with the array kept alive."""
+    if x is None:
+        return None, None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().contiguous().numpy()
+    x = np.ascontiguousarray(x)
+    if x.dtype != dtype:
+        x = x.view(dtype)
+    return x, x.ctypes.data
+
+
+def _args(M, N, K, fmt, A, lda, a_col_major, SA, ld_sa, B, ldb, b_col_major,
+          SB, ld_sb, C0, ldc, c_col_major, c_dtype, alpha, beta):
+    el = np.uint16 if fmt == BF16 else np.uint8
+    a, pa = _arr(A, el)
+    b, pb = _arr(B, el)
+    sa, psa = _arr(SA, np.uint8)
+    sb, psb = _arr(SB, np.uint8)
+    c0, pc0 = _arr(C0, np.float32 if c_dtype == OUT_F32 else np.uint16)
+    keep = (a, b, sa, sb, c0)
+    args = [M, N, K,
+            fmt, pa, lda, int(a_col_major), psa, ld_sa,
+            fmt, pb, ldb, int(b_col_major), psb, ld_sb,
+            pc0, ldc, int(c_col_major), int(c_dtype),
+            float(alpha), float(beta)]
+    return keep, args
+
+
+def gemm_rows(M, N, K, A, lda, a_col_major, B, ldb, b_col_major,
+              C0=None, ldc=0, c_col_major=False, c_dtype=OUT_F32,
+              alpha=1.0, beta=0.0, fmt=BF16, SA=None, ld_sa=0, SB=None,
+              ld_sb=0, row_begin=0, row_end=None):
+    """Reference rows [row_begin, row_end) of C; returns (Cref, T) as
+    float64 arrays of shape (rows, N)."""
+    if row_end is None:
+        row_end = M
+    keep, args = _args(M, N, K, fmt, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                       b_col_major, SB, ld_sb, C0, ldc, c_col_major, c_dtype,
+                       alpha, beta)
+    rows = row_end - row_begin
+    cref = np.zeros((max(rows, 0), N), dtype=np.float64)
+    tsum = np.zeros((max(rows, 0), N), dtype=np.float64)
+    rc = _load().oracle_gemm_rows(*args, row_begin, row_end,
+                                  cref.ctypes.data, tsum.ctypes.data)
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rows failed with code {rc}")
+    return cref, tsum
+
+
+def gemm_entries(M, N, K, A, lda, a_col_major, B, ldb, b_col_major, ii, jj,
+                 C0=None, ldc=0, c_col_major=False, c_dtype=OUT_F32,
+                 alpha=1.0, beta=0.0, fmt=BF16, SA=None, ld_sa=0, SB=None,
+                 ld_sb=0):
+    """Reference values and T at the entries (ii[t], jj[t])."""
+    keep, args = _args(M, N, K, fmt, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                       b_col_major, SB, ld_sb, C0, ldc, c_col_major, c_dtype,
+                       alpha, beta)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("ii and jj must have the same shape")
+    out = np.zeros(ii.shape, dtype=np.float64)
+    tsum = np.zeros(ii.shape, dtype=np.float64)
+    rc = _load().oracle_gemm_entries(*args, ii.size, ii.ctypes.data,
+                                     jj.ctypes.data, out.ctypes.data,
+                                     tsum.ctypes.data)
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_entries failed with code {rc}")
+    return out, tsum
+
+
+from .check import check, tolerance  # noqa: E402,F401

@@ -1,0 +1,381 @@
+"""Pins for the fp64 oracle, each against something other than the oracle
+itself: published format code points (tests/golden/formats.txt), torch's own
+fp8/bf16 decoders, hand-worked products (tests/golden/gemm_small.txt), closed
+forms that are exact in fp64, bitwise invariances, numpy float64 matmul, and
+the BLAS alpha/beta/K rules."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from matrix_core_engineering_amd.inputs import (BF16, E4M3FN, OUT_BF16, OUT_F32,
+                                                make_problem, to_bf16_bits,
+                                                to_e4m3fn_codes)
+from helpers import (bf16_bits_to_f64, numpy_reference, oracle_entries,
+                     oracle_full, torch_decode_elements, torch_decode_scales)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def parse_value(s):
+    s = s.strip()
+    if s == "nan":
+        return float("nan")
+    if s in ("inf", "-inf"):
+        return float(s)
+    if s == "-0":
+        return -0.0
+    if "p" in s:
+        m, e = s.split("p")
+        return math.ldexp(float(m), int(e))
+    return float(s)
+
+
+def same(a, b):
+    """Bitwise-equal doubles (NaN equals NaN, -0 differs from +0)."""
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b and math.copysign(1.0, a) == math.copysign(1.0, b)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_golden_format_points(oracle_lib):
+    dec = {"e4m3fn": oracle.e4m3fn_to_f64, "e8m0": oracle.e8m0_to_f64,
+           "bf16": oracle.bf16_to_f64}
+    n = 0
+    with open(os.path.join(GOLDEN, "formats.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            fmt, code, value = line.split()
+            got = dec[fmt](int(code, 16))
+            assert same(got, parse_value(value)), (fmt, code, got, value)
+            n += 1
+    assert n >= 30
+
+
+def test_bf16_all_codes_match_torch(oracle_lib):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch_decode_elements(codes, BF16)
+    got = np.array([oracle.bf16_to_f64(c) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3fn_all_codes_match_torch(oracle_lib):
+    codes = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    ref = torch_decode_elements(codes, E4M3FN)
+    got = np.array([oracle.e4m3fn_to_f64(c) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(got).sum() == 2          # only S.1111.111
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert np.nanmax(got) == 448.0
+
+
+def test_e8m0_all_codes_match_torch(oracle_lib):
+    codes = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    ref = torch_decode_scales(codes)
+    got = np.array([oracle.e8m0_to_f64(c) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(got[ok], np.ldexp(1.0, codes[ok].astype(np.int64) - 127))
+
+
+# ---------------------------------------------------------- small problems
+
+def bf16_matrix(rows):
+    """list of lists of exact values -> uint16 bf16 bits (row-major)."""
+    return to_bf16_bits(torch.tensor(rows, dtype=torch.float32))
+
+
+def parse_matrix(s):
+    return [[float(v) for v in r.split(",")] for r in s.split(";")]
+
+
+def test_golden_small_gemm(oracle_lib):
+    with open(os.path.join(GOLDEN, "gemm_small.txt")) as f:
+        cases = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    assert len(cases) == 3
+    for name, alpha, beta, a, b, c0, want, tw in cases:
+        A = bf16_matrix(parse_matrix(a))
+        B = bf16_matrix(parse_matrix(b))
+        C0 = None if c0 == "-" else np.array(parse_matrix(c0), dtype=np.float32)
+        cref, tsum = oracle.gemm_rows(2, 2, 3, A, 3, False, B, 2, False, C0=C0,
+                                      ldc=2, c_dtype=OUT_F32,
+                                      alpha=float(alpha), beta=float(beta))
+        assert np.array_equal(cref, np.array(parse_matrix(want))), name
+        assert np.array_equal(tsum, np.array(parse_matrix(tw))), name
+
+
+def _bf16_problem(A, B, **kw):
+    """Problem from logical float matrices (exact in bf16), A row-major,
+    B row-major unless overridden."""
+    M, K = A.shape
+    N = B.shape[1]
+    a_cm = kw.pop("a_col_major", False)
+    b_cm = kw.pop("b_col_major", False)
+    Ast = bf16_matrix(A.T.tolist() if a_cm else A.tolist())
+    Bst = bf16_matrix(B.T.tolist() if b_cm else B.tolist())
+    return dict(M=M, N=N, K=K, A=Ast, lda=(M if a_cm else K), a_col_major=a_cm,
+                B=Bst, ldb=(K if b_cm else N), b_col_major=b_cm, **kw)
+
+
+@pytest.mark.parametrize("a_cm,b_cm", [(False, False), (False, True), (True, False), (True, True)])
+def test_identity_gives_b(oracle_lib, a_cm, b_cm):
+    g = torch.Generator().manual_seed(7)
+    Bf = torch.randn(13, 9, generator=g).to(torch.bfloat16).to(torch.float64).numpy()
+    A = np.eye(13)
+    cref, tsum = oracle.gemm_rows(**_bf16_problem(A, Bf, a_col_major=a_cm, b_col_major=b_cm))
+    assert np.array_equal(cref, Bf)
+    assert np.array_equal(tsum, np.abs(Bf))
+
+
+def test_permutation_permutes_rows(oracle_lib):
+    g = torch.Generator().manual_seed(8)
+    Bf = torch.randn(11, 6, generator=g).to(torch.bfloat16).to(torch.float64).numpy()
+    perm = torch.randperm(11, generator=g).numpy()
+    P = np.eye(11)[perm]
+    cref, _ = oracle.gemm_rows(**_bf16_problem(P, Bf, b_col_major=True))
+    assert np.array_equal(cref, Bf[perm])
+
+
+def test_rank_one_closed_form(oracle_lib):
+    u = np.array([1., -2., 3., 0.5, -1.])
+    v = np.array([2., 1., -1., 4.])
+    w = np.array([-1., 3., 2., 0.25])
+    z = np.array([1., 2., -3.])
+    A = np.outer(u, v)
+    B = np.outer(w, z)
+    cref, tsum = oracle.gemm_rows(**_bf16_problem(A, B))
+    assert np.array_equal(cref, np.outer(u, z) * float(v @ w))
+    assert np.array_equal(tsum, np.outer(np.abs(u), np.abs(z)) * float(np.abs(v) @ np.abs(w)))
+
+
+def test_k1_outer_product(oracle_lib):
+    a = np.array([[1.5], [-2.], [0.25]])
+    b = np.array([[4., -0.5, 3., 1.]])
+    cref, tsum = oracle.gemm_rows(**_bf16_problem(a, b))
+    assert np.array_equal(cref, a @ b)
+    assert np.array_equal(tsum, np.abs(a @ b))
+
+
+def test_all_ones_gives_k(oracle_lib):
+    M, N, K = 5, 7, 37
+    cref, tsum = oracle.gemm_rows(**_bf16_problem(np.ones((M, K)), np.ones((K, N))))
+    assert np.all(cref == K) and np.all(tsum == K)
+
+
+def test_alpha_beta_closed_form(oracle_lib):
+    Bv = np.array([[1., 2.], [3., 4.], [-5., 6.]])
+    C0 = np.array([[8., -2.], [0.5, 4.], [1., 1.]], dtype=np.float32)
+    cref, _ = oracle.gemm_rows(**_bf16_problem(np.eye(3), Bv, C0=C0, ldc=2,
+                                               alpha=2.0, beta=-0.5))
+    assert np.array_equal(cref, 2.0 * Bv - 0.5 * C0.astype(np.float64))
+
+
+def test_beta_zero_does_not_read_c0(oracle_lib):
+    C0 = np.full((3, 2), np.nan, dtype=np.float32)
+    cref, _ = oracle.gemm_rows(**_bf16_problem(np.eye(3), np.ones((3, 2)),
+                                               C0=C0, ldc=2, beta=0.0))
+    assert np.array_equal(cref, np.ones((3, 2)))
+    cref2, _ = oracle.gemm_rows(**_bf16_problem(np.eye(3), np.ones((3, 2)), beta=0.0))
+    assert np.array_equal(cref2, cref)
+
+
+def test_alpha_zero_and_k_zero_do_not_read_ab(oracle_lib):
+    A = np.full((3, 4), np.nan)
+    C0 = np.arange(6, dtype=np.float32).reshape(3, 2)
+    cref, tsum = oracle.gemm_rows(**_bf16_problem(A, np.ones((4, 2)), C0=C0,
+                                                  ldc=2, alpha=0.0, beta=3.0))
+    assert np.array_equal(cref, 3.0 * C0) and np.all(tsum == 0)
+    cref, tsum = oracle.gemm_rows(3, 2, 0, None, 1, False, None, 2, False,
+                                  C0=C0, ldc=2, alpha=1.0, beta=-1.0)
+    assert np.array_equal(cref, -C0.astype(np.float64)) and np.all(tsum == 0)
+
+
+def test_nan_and_inf_propagate(oracle_lib):
+    A = np.ones((2, 3))
+    A[0, 1] = np.inf
+    A[1, 2] = np.nan
+    cref, _ = oracle.gemm_rows(**_bf16_problem(A, np.ones((3, 2))))
+    assert np.all(np.isposinf(cref[0])) and np.all(np.isnan(cref[1]))
+
+
+def test_bad_arguments_are_rejected(oracle_lib):
+    with pytest.raises(ValueError):
+        oracle.gemm_rows(-1, 2, 2, np.zeros(4, np.uint16), 2, False,
+                         np.zeros(4, np.uint16), 2, False)
+    with pytest.raises(ValueError):   # beta != 0 needs C0
+        oracle.gemm_rows(2, 2, 2, np.zeros(4, np.uint16), 2, False,
+                         np.zeros(4, np.uint16), 2, False, beta=1.0)
+
+
+# ------------------------------------------------------ invariances / numpy
+
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+@pytest.mark.parametrize("fmt", [BF16, E4M3FN])
+def test_transposition_invariance_bitwise(oracle_lib, fmt):
+    """(A B)^T = B^T A^T computed by the oracle from the same bytes, bitwise:
+    the k order and every product are the same."""
+    for seed, (a_cm, b_cm) in enumerate(LAYOUTS):
+        p = make_problem(19, 23, 70, fmt=fmt, a_col_major=a_cm, b_col_major=b_cm,
+                         c_dtype=OUT_F32, alpha=0.75, beta=-1.25, seed=50 + seed,
+                         dist="uniform")
+        cref, tsum = oracle_full(p)
+        # C^T = B^T A^T: B^T is the storage of B with the layout flag flipped
+        ct, tt = oracle.gemm_rows(p.N, p.M, p.K, p.B, p.ldb, not p.b_col_major,
+                                  p.A, p.lda, not p.a_col_major, C0=p.C0,
+                                  ldc=p.ldc, c_col_major=not p.c_col_major,
+                                  c_dtype=p.c_dtype, alpha=p.alpha, beta=p.beta,
+                                  fmt=fmt, SA=p.SB, ld_sa=p.ld_sb, SB=p.SA,
+                                  ld_sb=p.ld_sa)
+        assert np.array_equal(ct, cref.T)
+        assert np.array_equal(tt, tsum.T)
+
+
+def test_layout_invariance_bitwise(oracle_lib):
+    """One logical matrix stored four ways (row/col-major, padded ld) gives
+    bitwise the same result."""
+    base = make_problem(17, 12, 33, a_col_major=False, b_col_major=False,
+                        c_dtype=OUT_F32, seed=3, dist="uniform")
+    Alog = base.A[:17, :33]
+    Blog = base.B[:33, :12]
+    ref, _ = oracle_full(base)
+    for a_cm, b_cm in LAYOUTS:
+        for pad in (0, 5):
+            As = (Alog.T if a_cm else Alog)
+            Bs = (Blog.T if b_cm else Blog)
+            As = np.pad(As, ((0, 0), (0, pad)), constant_values=0x7FC0)
+            Bs = np.pad(Bs, ((0, 0), (0, pad)), constant_values=0x7FC0)
+            cref, _ = oracle.gemm_rows(17, 12, 33, np.ascontiguousarray(As),
+                                       As.shape[1], a_cm, np.ascontiguousarray(Bs),
+                                       Bs.shape[1], b_cm)
+            assert np.array_equal(cref, ref), (a_cm, b_cm, pad)
+
+
+@pytest.mark.parametrize("fmt", [BF16, E4M3FN])
+def test_matches_numpy_float64_on_random_tiny_shapes(oracle_lib, fmt):
+    rng = np.random.default_rng(11 + fmt)
+    for t in range(24):
+        M, N, K = (int(x) for x in rng.integers(1, 48, size=3))
+        a_cm, b_cm = LAYOUTS[t % 4]
+        c_cm = bool(t & 4)
+        out_bf16 = bool(t & 8)
+        beta = [0.0, 1.0, -0.5][t % 3]
+        p = make_problem(M, N, K, fmt=fmt, a_col_major=a_cm, b_col_major=b_cm,
+                         c_col_major=c_cm, c_dtype=OUT_BF16 if out_bf16 else OUT_F32,
+                         alpha=[1.0, 0.5, -2.0][t % 3], beta=beta,
+                         lda=(M if a_cm else K) + t % 3, ldb=(K if b_cm else N) + t % 2,
+                         dist="uniform", lo=-4.0, hi=4.0, seed=100 + t)
+        cref, tsum = oracle_full(p)
+        nref, ntsum = numpy_reference(p)
+        scale = np.abs(nref).max() + ntsum.max() + 1.0
+        assert np.abs(cref - nref).max() <= 1e-12 * scale, (M, N, K, t)
+        assert np.abs(tsum - ntsum).max() <= 1e-12 * (ntsum.max() + 1.0)
+
+
+def test_mx_block_scales_closed_form(oracle_lib):
+    """Data all 1.0 (E4M3FN 0x38); A row 0 has scale bytes [127, 130] over
+    two 32-element blocks, B's scales are 127: the dot product is
+    32*1 + 32*2^3 = 288.  Row 1 uses [119, 127]: 32*2^-8 + 32 = 32.125."""
+    M, N, K = 2, 3, 64
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x38, np.uint8)          # column-major B, K-contiguous
+    SA = np.array([[127, 130], [119, 127]], np.uint8)
+    SB = np.full((N, 2), 127, np.uint8)
+    cref, tsum = oracle.gemm_rows(M, N, K, A, K, False, B, K, True, fmt=E4M3FN,
+                                  SA=SA, ld_sa=2, SB=SB, ld_sb=2)
+    assert np.all(cref[0] == 288.0) and np.all(cref[1] == 32.125)
+    assert np.array_equal(cref, tsum)
+
+
+def test_mx_partial_last_block(oracle_lib):
+    """K = 40: the second block has 8 elements and its scale applies to
+    exactly k = 32..39."""
+    M, N, K = 1, 1, 40
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x40, np.uint8)          # 2.0
+    SA = np.array([[127, 128]], np.uint8)
+    SB = np.array([[126, 127]], np.uint8)
+    cref, _ = oracle.gemm_rows(M, N, K, A, K, False, B, K, True, fmt=E4M3FN,
+                               SA=SA, ld_sa=2, SB=SB, ld_sb=2)
+    assert cref[0, 0] == 32 * 1 * 2 * 0.5 + 8 * 1 * 2 * 2 * 1
+
+
+def test_entries_equal_rows_bitwise(oracle_lib):
+    p = make_problem(37, 29, 130, a_col_major=True, b_col_major=False, c_dtype=OUT_BF16,
+                     beta=0.5, seed=21, dist="normal")
+    cref, tsum = oracle_full(p)
+    rng = np.random.default_rng(0)
+    ii = rng.integers(0, 37, 200)
+    jj = rng.integers(0, 29, 200)
+    v, t = oracle_entries(p, ii, jj)
+    assert np.array_equal(v, cref[ii, jj]) and np.array_equal(t, tsum[ii, jj])
+    part, _ = oracle_full(p, 10, 20)
+    assert np.array_equal(part, cref[10:20])
+
+
+# ---------------------------------------------------------- the checker
+
+def test_check_bound():
+    cref = np.array([1.0, 2.0, -3.0])
+    tsum = np.array([10.0, 10.0, 10.0])
+    ok, worst, bad = oracle.check(cref + 1.999e-3, cref, tsum, out_bf16=False)
+    assert ok and abs(worst - 0.9995) < 1e-6 and bad == 0
+    ok, _, bad = oracle.check(cref + 2.1e-3, cref, tsum, out_bf16=False)
+    assert not ok and bad == 3
+    # bf16 adds 2^-8 |Cref|
+    ok, _, _ = oracle.check(cref + 2e-3 + 2.0 ** -8 * np.abs(cref) * 0.99, cref,
+                            tsum, out_bf16=True)
+    assert ok
+    ok, _, _ = oracle.check(np.array([np.nan, 2.0, -3.0]), cref, tsum, False)
+    assert not ok
+    ok, _, _ = oracle.check(np.array([np.inf, -np.inf]), np.array([np.inf, np.inf]),
+                            np.array([1.0, 1.0]), False)
+    assert not ok
+    ok, _, _ = oracle.check(np.array([np.inf, np.nan]), np.array([np.inf, np.nan]),
+                            np.array([1.0, 1.0]), False)
+    assert ok
+    ok, _, _ = oracle.check(np.array([1.0 + 1e-7]), np.array([1.0]), np.array([0.0]), False)
+    assert not ok
+    ok, _, _ = oracle.check(np.array([1.0 + 1e-7]), np.array([1.0]), np.array([0.0]),
+                            False, fp32_slack=np.array([1.0]))
+    assert ok
+
+
+# ---------------------------------------------------------- generators
+
+def test_generators_deterministic_and_shaped():
+    from matrix_core_engineering_amd.inputs import config_problem, integer_problem
+    p1 = make_problem(33, 17, 65, lda=70, seed=5, beta=1.0, c_dtype=OUT_F32)
+    p2 = make_problem(33, 17, 65, lda=70, seed=5, beta=1.0, c_dtype=OUT_F32)
+    p3 = make_problem(33, 17, 65, lda=70, seed=6, beta=1.0, c_dtype=OUT_F32)
+    assert np.array_equal(p1.A, p2.A) and np.array_equal(p1.B, p2.B)
+    assert np.array_equal(p1.C0, p2.C0)
+    assert not np.array_equal(p1.A, p3.A)
+    assert p1.A.shape == (33, 70) and p1.B.shape == (17, 65)
+    assert np.all(np.isnan(bf16_bits_to_f64(p1.A[:, 65:])))    # padding is NaN
+    c1 = config_problem(1)
+    assert (c1.M, c1.N, c1.K, c1.lda, c1.ldb, c1.ldc) == (128, 128, 64, 64, 128, 128)
+    vals = bf16_bits_to_f64(c1.A)
+    assert vals.min() >= -1.0 and vals.max() <= 1.0
+    q = integer_problem(8, 8, 64, fmt=E4M3FN)
+    dec = torch_decode_elements(q.A, E4M3FN)
+    assert np.array_equal(dec, np.round(dec)) and np.abs(dec).max() <= 4
+    assert q.SA.min() >= 127 and q.SA.max() <= 129
+    m = make_problem(8, 8, 96, fmt=E4M3FN, dist="uniform", lo=-448, hi=448, seed=9)
+    assert m.SA.shape == (8, 3) and m.SA.min() >= 119 and m.SA.max() <= 135
+    assert np.abs(torch_decode_elements(m.A, E4M3FN)).max() <= 448
+    assert np.array_equal(to_e4m3fn_codes(torch.tensor([448.0, -448.0])),
+                          np.array([0x7E, 0xFE], np.uint8))
