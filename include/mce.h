@@ -1,0 +1,151 @@
+/*
+ * mce.h -- C ABI of the gfx950 (MI355X) tiled GEMM library.
+ *
+ *     C <- alpha * op(A) * op(B) + beta * C
+ *
+ * op(A) is the logical M x K operand and op(B) the logical K x N operand; C is
+ * M x N.  Products accumulate in fp32 on the matrix cores; C is written as
+ * fp32 or as bf16 rounded to nearest even.
+ *
+ * The operation is the dense GEMM whose construction the page "B200 GEMM
+ * Optimization Ladder" describes level by level (section A1, the nine-level
+ * route; section E, steps 1-10): section E step 1 asks that the math
+ * definition, layout and dtype be fixed first, and this header is that
+ * contract.  The math definition is the ordinary BLAS one.  The block-scaled
+ * fp8 entry points follow "B200 TMEM Lifecycle Planner", section A1 case 2
+ * (block-scaled MMA: data and scale factors staged separately, scale layout
+ * distinct from the accumulator layout), with the OCP MX formats: E4M3FN
+ * elements and one E8M0 scale per 32 consecutive K elements.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing, keeps no per-call state and holds no pointer after it
+ *    returns.  Calls on different streams may run concurrently.
+ *  - Leading dimensions are counted in elements.  a(i,k) is A[i*lda + k] when
+ *    a_col_major == 0 (row-major, K contiguous) and A[k*lda + i] otherwise;
+ *    b(k,j) is B[k*ldb + j] when b_col_major == 0 (row-major, N contiguous)
+ *    and B[j*ldb + k] otherwise; c(i,j) is C[i*ldc + j] when c_col_major == 0
+ *    and C[j*ldc + i] otherwise.  Elements outside the logical extent (the
+ *    padding up to the leading dimension) are never read or written.
+ *  - c_dtype is MCE_OUT_F32 (C holds float) or MCE_OUT_BF16 (C holds bf16
+ *    bits).  When beta != 0, C is read in the same dtype before it is
+ *    overwritten.
+ *  - BLAS rules: when beta == 0, C is not read (NaN/Inf in C do not
+ *    propagate); when alpha == 0 or K == 0, A and B (and the scales) are not
+ *    read and C <- beta * C; when M == 0 or N == 0 nothing is launched.
+ *  - stream is a hipStream_t (NULL = the null stream).  Every call is
+ *    asynchronous: argument errors are reported synchronously by the return
+ *    code, device faults only at the caller's next synchronisation.
+ *  - The kernels exist only for gfx950.  On any other device every entry
+ *    point returns MCE_EUNSUPPORTED without launching.
+ *
+ * Errors (the return value; no exception or abort crosses the ABI)
+ * ------
+ *  MCE_OK            success (work enqueued, or nothing to do)
+ *  MCE_EINVAL        negative size; NULL pointer that the call would use;
+ *                    leading dimension below the contiguous extent or < 1;
+ *                    c_dtype not MCE_OUT_F32/MCE_OUT_BF16; C overlapping A, B
+ *                    or a scale array; an operand spanning 2^31 bytes or more
+ *  MCE_EUNSUPPORTED  device is not gfx950; a level that cannot take this
+ *                    problem (see gemm_bf16_level); MX operand not
+ *                    K-contiguous
+ *  MCE_ELAUNCH       the kernel launch itself failed (hipGetLastError)
+ */
+#ifndef MCE_H
+#define MCE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MCE_OK = 0,
+    MCE_EINVAL = 1,
+    MCE_EUNSUPPORTED = 2,
+    MCE_ELAUNCH = 3
+} mce_status;
+
+enum { MCE_OUT_F32 = 0, MCE_OUT_BF16 = 1 };
+
+/*
+ * bf16 GEMM.  A: bf16 bits (uint16), B: bf16 bits, fp32 accumulate.
+ * Picks the fastest level that accepts the problem.
+ * ("B200 GEMM Optimization Ladder", section E steps 1-8.)
+ */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void *A, int64_t lda, int a_col_major,
+              const void *B, int64_t ldb, int b_col_major,
+              void *C, int64_t ldc, int c_col_major, int c_dtype,
+              float alpha, float beta, void *stream);
+
+/*
+ * MX block-scaled fp8 GEMM.  A and B hold E4M3FN codes (one byte each).
+ * SA is M x ceil(K/32) E8M0 bytes, row-major with leading dimension ld_sa:
+ * a(i,k) = e4m3(A(i,k)) * 2^(SA[i*ld_sa + k/32] - 127).  SB is N x ceil(K/32)
+ * bytes, row-major with leading dimension ld_sb, scaling b(k,j) the same way.
+ * Both operands must be K-contiguous (a_col_major == 0, b_col_major == 1),
+ * else MCE_EUNSUPPORTED.  The scale byte 0xFF (NaN) propagates NaN.
+ * ("B200 TMEM Lifecycle Planner", section A1 case 2: block-scaled MMA.)
+ */
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
+               const void *A, int64_t lda, int a_col_major,
+               const void *SA, int64_t ld_sa,
+               const void *B, int64_t ldb, int b_col_major,
+               const void *SB, int64_t ld_sb,
+               void *C, int64_t ldc, int c_col_major, int c_dtype,
+               float alpha, float beta, void *stream);
+
+/*
+ * Runs one specific level of the ladder, so that every level stays callable
+ * and comparable ("B200 GEMM Optimization Ladder", section I: keep the
+ * version at every level; section E step 11: compare with the previous
+ * level).  Same arguments and semantics as gemm_bf16 / gemm_mxfp8.
+ *
+ *   level 1  single 128x128 output tile, one K tile, synchronous copies
+ *            (section E step 2): needs M <= 128, N <= 128, K <= 64
+ *   level 2  + K loop with tail (step 3): needs M <= 128, N <= 128
+ *   level 3  + grid of workgroups over M/N with boundary masks (step 4)
+ *   level 4  + direct global->LDS operand loads with an XOR swizzle and a
+ *            store epilogue (step 5)
+ *   level 5  + multi-stage LDS ring with ready/free stages (step 6)
+ *   level 6  + persistent grid with a tile-order scheduler (step 7)
+ *   level 7  + role-specialised waves (step 8)
+ *
+ * Levels 4-7 need both operands K-contiguous (A row-major, B column-major),
+ * 16-byte aligned base pointers, lda and ldb multiples of 8 and K a multiple
+ * of 8; otherwise they return MCE_EUNSUPPORTED.  gemm_mxfp8_level accepts
+ * levels 3 and 5-6 (same meaning; its level 3 also takes any K).
+ */
+int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda, int a_col_major,
+                    const void *B, int64_t ldb, int b_col_major,
+                    void *C, int64_t ldc, int c_col_major, int c_dtype,
+                    float alpha, float beta, void *stream);
+
+int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, int a_col_major,
+                     const void *SA, int64_t ld_sa,
+                     const void *B, int64_t ldb, int b_col_major,
+                     const void *SB, int64_t ld_sb,
+                     void *C, int64_t ldc, int c_col_major, int c_dtype,
+                     float alpha, float beta, void *stream);
+
+/* Level gemm_bf16 / gemm_mxfp8 would run for this problem (0 if none). */
+int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, int a_col_major,
+                         const void *B, int64_t ldb, int b_col_major);
+int gemm_mxfp8_pick_level(int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda, int a_col_major,
+                          const void *B, int64_t ldb, int b_col_major);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char *gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCE_H */

@@ -1,0 +1,366 @@
+// The C ABI boundary: argument validation, the BLAS special cases, the
+// column-major-C transposition, level choice and the launch on the caller's
+// stream.  No allocation, no state beyond a per-device architecture check.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/mce.h"
+#include "launch.hpp"
+
+namespace {
+
+using mce::GemmArgs;
+
+enum Fmt { FMT_BF16 = 0, FMT_MXFP8 = 1 };
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;   // 32-bit buffer offsets
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];            // 0 unknown, 1 gfx950, 2 other
+
+bool device_is_gfx950()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return false;
+    int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        state = 2;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+            state = 1;
+        g_arch_ok[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1;
+}
+
+// Bytes spanned by a rows x cols matrix with the given contiguous extent.
+int64_t span_bytes(int64_t outer, int64_t inner, int64_t ld, int64_t elt)
+{
+    if (outer == 0 || inner == 0)
+        return 0;
+    return ((outer - 1) * ld + inner) * elt;
+}
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0)
+        return false;
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+struct Call {
+    int level;   // 0 = pick
+    Fmt fmt;
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    int a_cm;
+    const void *SA;
+    int64_t ld_sa;
+    const void *B;
+    int64_t ldb;
+    int b_cm;
+    const void *SB;
+    int64_t ld_sb;
+    void *C;
+    int64_t ldc;
+    int c_cm;
+    int c_dtype;
+    float alpha, beta;
+    hipStream_t stream;
+};
+
+// Levels 4-7 read operands with 16-byte direct loads: both operands
+// K-contiguous, 16-byte aligned rows, K a whole number of 16-byte chunks.
+bool fast_eligible(const Call &c)
+{
+    int64_t elt = c.fmt == FMT_BF16 ? 2 : 1;
+    int64_t per_chunk = 16 / elt;
+    return c.a_cm == 0 && c.b_cm == 1 && (c.lda % per_chunk) == 0 && (c.ldb % per_chunk) == 0 &&
+           (c.K % per_chunk) == 0 && ((uintptr_t)c.A % 16) == 0 && ((uintptr_t)c.B % 16) == 0;
+}
+
+bool mx_scales_eligible(const Call &c)
+{
+    // the pipelined MX kernels read four scale bytes per 32-bit load
+    return (c.ld_sa % 4) == 0 && (c.ld_sb % 4) == 0 && ((uintptr_t)c.SA % 4) == 0 &&
+           ((uintptr_t)c.SB % 4) == 0;
+}
+
+constexpr int kBestBf16Level = 3;     // raised as faster levels land
+constexpr int kBestMxLevel = 3;
+
+int pick_level(const Call &c)
+{
+    if (c.fmt == FMT_BF16) {
+        if (kBestBf16Level >= 4 && fast_eligible(c))
+            return kBestBf16Level;
+        return 3;
+    }
+    if (kBestMxLevel >= 5 && fast_eligible(c) && mx_scales_eligible(c))
+        return kBestMxLevel;
+    return 3;
+}
+
+// Whether `level` can run this (already normalised) problem.
+bool level_accepts(const Call &c, int level)
+{
+    if (c.fmt == FMT_BF16) {
+        switch (level) {
+        case 1: return c.M <= 128 && c.N <= 128 && c.K <= 64;
+        case 2: return c.M <= 128 && c.N <= 128;
+        case 3: return true;
+        case 4: case 5: case 6: case 7: return fast_eligible(c);
+        default: return false;
+        }
+    }
+    switch (level) {
+    case 3: return true;
+    case 5: case 6: return fast_eligible(c) && mx_scales_eligible(c);
+    default: return false;
+    }
+}
+
+int validate(const Call &c)
+{
+    if (c.M < 0 || c.N < 0 || c.K < 0)
+        return MCE_EINVAL;
+    if (c.M > INT32_MAX / 2 || c.N > INT32_MAX / 2 || c.K > INT32_MAX / 2)
+        return MCE_EINVAL;
+    if (c.c_dtype != MCE_OUT_F32 && c.c_dtype != MCE_OUT_BF16)
+        return MCE_EINVAL;
+    if (c.fmt == FMT_MXFP8 && !(c.a_cm == 0 && c.b_cm == 1))
+        return MCE_EUNSUPPORTED;
+    const int64_t elt = c.fmt == FMT_BF16 ? 2 : 1;
+    const int64_t celt = c.c_dtype == MCE_OUT_F32 ? 4 : 2;
+    // leading dimensions: at least the contiguous extent, and at least 1
+    auto ld_ok = [](int64_t ld, int64_t extent) { return ld >= 1 && ld >= extent; };
+    if (!ld_ok(c.lda, c.a_cm ? c.M : c.K) || !ld_ok(c.ldb, c.b_cm ? c.K : c.N) ||
+        !ld_ok(c.ldc, c.c_cm ? c.M : c.N))
+        return MCE_EINVAL;
+    const int64_t nblk = (c.K + 31) / 32;
+    if (c.fmt == FMT_MXFP8 && (!ld_ok(c.ld_sa, nblk) || !ld_ok(c.ld_sb, nblk)))
+        return MCE_EINVAL;
+    if (c.M == 0 || c.N == 0)
+        return MCE_OK;
+    const bool reads_ab = c.alpha != 0.0f && c.K > 0;
+    if (!c.C)
+        return MCE_EINVAL;
+    const int64_t nc = c.c_cm ? span_bytes(c.N, c.M, c.ldc, celt) : span_bytes(c.M, c.N, c.ldc, celt);
+    if (nc >= kMaxBytes)
+        return MCE_EINVAL;
+    if (!reads_ab)
+        return MCE_OK;
+    if (!c.A || !c.B)
+        return MCE_EINVAL;
+    const int64_t na = c.a_cm ? span_bytes(c.K, c.M, c.lda, elt) : span_bytes(c.M, c.K, c.lda, elt);
+    const int64_t nb = c.b_cm ? span_bytes(c.N, c.K, c.ldb, elt) : span_bytes(c.K, c.N, c.ldb, elt);
+    if (na >= kMaxBytes || nb >= kMaxBytes)
+        return MCE_EINVAL;
+    if (overlaps(c.C, nc, c.A, na) || overlaps(c.C, nc, c.B, nb))
+        return MCE_EINVAL;
+    if (c.fmt == FMT_MXFP8) {
+        if (!c.SA || !c.SB)
+            return MCE_EINVAL;
+        const int64_t nsa = span_bytes(c.M, nblk, c.ld_sa, 1);
+        const int64_t nsb = span_bytes(c.N, nblk, c.ld_sb, 1);
+        if (nsa >= kMaxBytes || nsb >= kMaxBytes)
+            return MCE_EINVAL;
+        if (overlaps(c.C, nc, c.SA, nsa) || overlaps(c.C, nc, c.SB, nsb))
+            return MCE_EINVAL;
+    }
+    return MCE_OK;
+}
+
+// A column-major C is the row-major C^T = B^T A^T: swap the operands (and
+// their scales), swap M and N, and flip both operand layout flags.
+Call normalise(Call c)
+{
+    if (!c.c_cm)
+        return c;
+    Call t = c;
+    t.M = c.N;
+    t.N = c.M;
+    t.A = c.B;
+    t.lda = c.ldb;
+    t.a_cm = !c.b_cm;
+    t.SA = c.SB;
+    t.ld_sa = c.ld_sb;
+    t.B = c.A;
+    t.ldb = c.lda;
+    t.b_cm = !c.a_cm;
+    t.SB = c.SA;
+    t.ld_sb = c.ld_sa;
+    t.c_cm = 0;
+    return t;
+}
+
+GemmArgs kernel_args(const Call &c)
+{
+    GemmArgs p;
+    p.M = (int)c.M;
+    p.N = (int)c.N;
+    p.K = (int)c.K;
+    p.A = c.A;
+    p.lda = (int)c.lda;
+    p.a_cm = c.a_cm;
+    p.B = c.B;
+    p.ldb = (int)c.ldb;
+    p.b_cm = c.b_cm;
+    p.SA = (const uint8_t *)c.SA;
+    p.ld_sa = (int)c.ld_sa;
+    p.SB = (const uint8_t *)c.SB;
+    p.ld_sb = (int)c.ld_sb;
+    p.C = c.C;
+    p.ldc = (int)c.ldc;
+    p.c_dtype = c.c_dtype;
+    p.alpha = c.alpha;
+    p.beta = c.beta;
+    return p;
+}
+
+int run(const Call &in)
+{
+    int st = validate(in);
+    if (st != MCE_OK)
+        return st;
+    if (!device_is_gfx950())
+        return MCE_EUNSUPPORTED;
+    Call c = normalise(in);
+    if (in.level != 0 && !level_accepts(c, in.level))
+        return MCE_EUNSUPPORTED;
+    if (c.M == 0 || c.N == 0)
+        return MCE_OK;
+    GemmArgs p = kernel_args(c);
+    hipError_t err;
+    if (c.alpha == 0.0f || c.K == 0) {
+        err = mce::launch_scale_c(p, c.stream);
+    } else {
+        int level = in.level != 0 ? in.level : pick_level(c);
+        if (c.fmt == FMT_BF16)
+            err = level <= 3 ? mce::launch_simple_bf16(level, p, c.stream)
+                             : mce::launch_fast_bf16(level, p, c.stream);
+        else
+            err = level <= 3 ? mce::launch_simple_mxfp8(p, c.stream)
+                             : mce::launch_fast_mxfp8(level, p, c.stream);
+        if (err == hipErrorInvalidValue && level >= 4)
+            return MCE_EUNSUPPORTED;
+    }
+    return err == hipSuccess ? MCE_OK : MCE_ELAUNCH;
+}
+
+Call make_call(int level, Fmt fmt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+               int a_cm, const void *SA, int64_t ld_sa, const void *B, int64_t ldb, int b_cm,
+               const void *SB, int64_t ld_sb, void *C, int64_t ldc, int c_cm, int c_dtype,
+               float alpha, float beta, void *stream)
+{
+    Call c;
+    c.level = level;
+    c.fmt = fmt;
+    c.M = M;
+    c.N = N;
+    c.K = K;
+    c.A = A;
+    c.lda = lda;
+    c.a_cm = a_cm ? 1 : 0;
+    c.SA = SA;
+    c.ld_sa = ld_sa;
+    c.B = B;
+    c.ldb = ldb;
+    c.b_cm = b_cm ? 1 : 0;
+    c.SB = SB;
+    c.ld_sb = ld_sb;
+    c.C = C;
+    c.ldc = ldc;
+    c.c_cm = c_cm ? 1 : 0;
+    c.c_dtype = c_dtype;
+    c.alpha = alpha;
+    c.beta = beta;
+    c.stream = (hipStream_t)stream;
+    return c;
+}
+
+} // namespace
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_col_major,
+              const void *B, int64_t ldb, int b_col_major, void *C, int64_t ldc, int c_col_major,
+              int c_dtype, float alpha, float beta, void *stream)
+{
+    return run(make_call(0, FMT_BF16, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
+                         b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta,
+                         stream));
+}
+
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_col_major,
+               const void *SA, int64_t ld_sa, const void *B, int64_t ldb, int b_col_major,
+               const void *SB, int64_t ld_sb, void *C, int64_t ldc, int c_col_major, int c_dtype,
+               float alpha, float beta, void *stream)
+{
+    return run(make_call(0, FMT_MXFP8, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                         b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
+                         stream));
+}
+
+int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                    int a_col_major, const void *B, int64_t ldb, int b_col_major, void *C,
+                    int64_t ldc, int c_col_major, int c_dtype, float alpha, float beta,
+                    void *stream)
+{
+    if (level < 1 || level > 7)
+        return MCE_EUNSUPPORTED;
+    return run(make_call(level, FMT_BF16, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
+                         b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta,
+                         stream));
+}
+
+int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                     int a_col_major, const void *SA, int64_t ld_sa, const void *B, int64_t ldb,
+                     int b_col_major, const void *SB, int64_t ld_sb, void *C, int64_t ldc,
+                     int c_col_major, int c_dtype, float alpha, float beta, void *stream)
+{
+    if (level < 1 || level > 7)
+        return MCE_EUNSUPPORTED;
+    return run(make_call(level, FMT_MXFP8, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                         b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
+                         stream));
+}
+
+int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                         int a_col_major, const void *B, int64_t ldb, int b_col_major)
+{
+    Call c = make_call(0, FMT_BF16, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb, b_col_major,
+                       nullptr, 0, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
+    if (M < 0 || N < 0 || K < 0)
+        return 0;
+    return pick_level(c);
+}
+
+int gemm_mxfp8_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                          int a_col_major, const void *B, int64_t ldb, int b_col_major)
+{
+    Call c = make_call(0, FMT_MXFP8, M, N, K, A, lda, a_col_major, nullptr, 4, B, ldb, b_col_major,
+                       nullptr, 4, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
+    if (M < 0 || N < 0 || K < 0 || a_col_major != 0 || b_col_major != 1)
+        return 0;
+    return pick_level(c);
+}
+
+const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case MCE_OK: return "MCE_OK: success";
+    case MCE_EINVAL: return "MCE_EINVAL: invalid argument";
+    case MCE_EUNSUPPORTED: return "MCE_EUNSUPPORTED: device, level or layout not supported";
+    case MCE_ELAUNCH: return "MCE_ELAUNCH: kernel launch failed";
+    default: return "unknown mce status";
+    }
+}
+
+} // extern "C"

@@ -1,0 +1,64 @@
+// Tile order and LDS swizzle: pure integer functions, usable on the host
+// (tests link a host build of this header) and on the device.
+//
+// Tile order ("B200 GEMM Optimization Ladder", section E step 7: a fixed set
+// of resident workgroups processes many tiles; check the tail and the tile
+// order).  Workgroups are dispatched round-robin over the 8 XCDs of an
+// MI355X, each XCD with its own L2.  The order below (1) renumbers workgroup
+// ids so that the ids resident on one XCD are consecutive, then (2) walks
+// the M x N tile grid in groups of `group_m` tile rows, column by column
+// inside a group, so that the tiles one XCD holds at a time share a few A
+// row-panels and B column-panels in that XCD's L2.
+#pragma once
+
+#ifdef __HIPCC__
+#define MCE_HD __host__ __device__ __forceinline__
+#else
+#define MCE_HD inline
+#endif
+
+namespace mce {
+
+constexpr int kNumXcd = 8;
+
+// Workgroup id -> position in an XCD-major order.  Bijection on [0, nwg).
+MCE_HD int xcd_major(int wg, int nwg)
+{
+    int q = nwg / kNumXcd, r = nwg % kNumXcd;
+    int xcd = wg % kNumXcd, local = wg / kNumXcd;
+    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Linear tile id -> (tile row, tile column), grouped by `group_m` tile rows.
+// Bijection from [0, tiles_m * tiles_n) onto the tile grid.
+MCE_HD void grouped_tile(int id, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
+{
+    int per_group = group_m * tiles_n;
+    int g = id / per_group;
+    int first_m = g * group_m;
+    int rows = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    int in_group = id - g * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
+// The r-th tile of workgroup `wg` in a persistent grid of `nwg` workgroups
+// (r = 0, 1, ... while the result is < tiles_m * tiles_n).
+MCE_HD int persistent_tile_id(int wg, int nwg, int r)
+{
+    return r * nwg + xcd_major(wg, nwg);
+}
+
+// XOR swizzle of the 16-byte chunk index inside one 128-byte LDS row (8
+// chunks): the chunk stored at physical slot (c ^ swz(row)).  Rows r and r+1
+// ... r+7 map one logical chunk to 8 distinct slots, and rows r and r+8 map
+// it to slots of opposite parity, so 8 or 16 consecutive rows read at one
+// logical chunk hit distinct banks ("B200 TMA Pipeline Designer", section B:
+// a swizzle that does not match the matrix-core read pattern is a failure
+// mode; here the reader and the writer use this one function).
+MCE_HD int swz8(int row)
+{
+    return (row & 7) ^ ((row >> 3) & 1);
+}
+
+} // namespace mce

@@ -39,8 +39,8 @@ def check(c, cref, tsum, out_bf16, fp32_slack=None):
     inf_bad = (inf_c != inf_r) | (inf_c & inf_r & (np.sign(c) != np.sign(cref)))
     finite = np.isfinite(c) & np.isfinite(cref)
     tol = tolerance(cref, tsum, out_bf16, fp32_slack)
-    err = np.where(finite, np.abs(c - cref), 0.0)
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        err = np.where(finite, np.abs(c - cref), 0.0)
         ratio = np.where(err == 0.0, 0.0, err / tol)
     ratio = np.where(finite, ratio, 0.0)
     bad = nan_bad | inf_bad | (finite & (err > tol))

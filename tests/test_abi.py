@@ -1,0 +1,94 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+that include/mce.h declares, and rejects bad arguments synchronously before
+touching the device.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_core_engineering_amd as mce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mce.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(mce.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mce.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    mce.load()
+
+
+def test_status_strings():
+    for st in (mce.MCE_OK, mce.MCE_EINVAL, mce.MCE_EUNSUPPORTED, mce.MCE_ELAUNCH):
+        s = mce.gemm_status_string(st)
+        assert s.startswith("MCE_")
+    assert mce.gemm_status_string(99) == "unknown mce status"
+
+
+FAKE_A, FAKE_B, FAKE_C = 0x10000000, 0x20000000, 0x30000000
+
+
+def bf16(M, N, K, lda, a_cm, ldb, b_cm, ldc, c_cm=0, c_dtype=0, alpha=1.0, beta=0.0,
+         A=FAKE_A, B=FAKE_B, C=FAKE_C, level=None):
+    if level is None:
+        return mce.gemm_bf16(M, N, K, A, lda, a_cm, B, ldb, b_cm, C, ldc, c_cm, c_dtype,
+                             alpha, beta, stream=0, raise_on_error=False)
+    return mce.gemm_bf16_level(level, M, N, K, A, lda, a_cm, B, ldb, b_cm, C, ldc, c_cm,
+                               c_dtype, alpha, beta, stream=0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("args", [
+    dict(M=-1, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4),         # negative size
+    dict(M=4, N=4, K=4, lda=3, a_cm=0, ldb=4, b_cm=1, ldc=4),          # lda < K
+    dict(M=4, N=4, K=4, lda=4, a_cm=1, ldb=3, b_cm=1, ldc=4),          # ldb < K
+    dict(M=4, N=5, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4),          # ldc < N
+    dict(M=5, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, c_cm=1),  # ldc < M (col C)
+    dict(M=4, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, c_dtype=7),
+    dict(M=4, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, A=0),      # A NULL
+    dict(M=4, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, C=0),      # C NULL
+    dict(M=4, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, C=FAKE_A + 8),  # C overlaps A
+    dict(M=1 << 16, N=4, K=1 << 15, lda=1 << 15, a_cm=0, ldb=1 << 15, b_cm=1, ldc=4),  # A >= 2 GiB
+])
+def test_invalid_arguments_rejected_on_host(args):
+    assert bf16(**args) == mce.MCE_EINVAL
+
+
+def test_level_out_of_range():
+    assert bf16(4, 4, 4, 4, 0, 4, 1, 4, level=0) == mce.MCE_EUNSUPPORTED
+    assert bf16(4, 4, 4, 4, 0, 4, 1, 4, level=8) == mce.MCE_EUNSUPPORTED
+
+
+def test_mx_rejects_mn_major_operands_and_short_scale_ld():
+    def mx(a_cm, b_cm, ld_sa=1, ld_sb=1, K=32):
+        return mce.gemm_mxfp8(4, 4, K, FAKE_A, 4 if a_cm else K, a_cm, 0x40000000, ld_sa,
+                              FAKE_B, K if b_cm else 4, b_cm, 0x50000000, ld_sb, FAKE_C, 4, 0,
+                              0, 1.0, 0.0, stream=0, raise_on_error=False)
+    assert mx(1, 1) == mce.MCE_EUNSUPPORTED
+    assert mx(0, 0) == mce.MCE_EUNSUPPORTED
+    assert mx(0, 1, ld_sa=1, K=64) == mce.MCE_EINVAL     # needs ceil(64/32) = 2
+
+
+def test_pick_level_reports_a_level():
+    assert mce.gemm_bf16_pick_level(4096, 4096, 4096, FAKE_A, 4096, 0, FAKE_B, 4096, 1) >= 3
+    assert mce.gemm_bf16_pick_level(4093, 3001, 1027, FAKE_A, 1027, 0, FAKE_B, 3001, 0) == 3
+    assert mce.gemm_mxfp8_pick_level(8192, 8192, 8192, FAKE_A, 8192, 0, FAKE_B, 8192, 1) >= 3
+    assert mce.gemm_mxfp8_pick_level(8, 8, 64, FAKE_A, 8, 1, FAKE_B, 64, 1) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(mce, "_lib", None)
+    monkeypatch.setattr(mce, "lib_path", lambda: str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        mce.load()
