@@ -92,7 +92,7 @@ bool mx_scales_eligible(const Call &c)
            ((uintptr_t)c.SB % 4) == 0;
 }
 
-constexpr int kBestBf16Level = 3;     // raised as faster levels land
+constexpr int kBestBf16Level = 6;     // the persistent pipelined kernel
 constexpr int kBestMxLevel = 3;
 
 int pick_level(const Call &c)
