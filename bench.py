@@ -1,0 +1,240 @@
+"""Benchmark of the GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  1. the 8192^3 bf16 GEMM (A row-major, B column-major, entries N(0, 0.02^2)
+     rounded to bf16, fp32 accumulate, bf16 output), and
+  2. the 8192^3 MX block-scaled fp8 GEMM (E4M3 entries from U[-448, 448],
+     one E8M0 scale per 32 K elements with exponents uniform in -8..8,
+     fp32 accumulate, bf16 output),
+each through the library's default entry point (gemm_bf16 / gemm_mxfp8).
+
+Prints ONE JSON line.  `value` is the step's GEMM throughput (4 * 8192^3
+flops per step / step time) in TFLOP/s; `per_workload` gives each GEMM's own
+TFLOP/s and fraction of its dense matrix-core peak; `roofline` covers the
+dominant (longest) kernel, timed with HIP events on the stream it runs on;
+`cpu_baseline` times the fp64 oracle on a bounded row sample of the bf16
+GEMM on the host cores and checks those rows of the GPU result.
+
+Modes for profiling (no JSON): --only bf16|mxfp8|copy --reps R runs just
+that kernel R times after one warm-up (copy: a 1 GiB device-to-device copy,
+the calibration of the HBM byte counters).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2516.6     # TFLOP/s dense: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8 = 5033.2      # TFLOP/s dense: 256 CU x 8192 flop/clk x 2.4 GHz
+PEAK_HBM = 8000.0      # GB/s
+METRIC = "GEMM TFLOP/s and % of dense MFMA peak (bf16, MX-fp8) at 8192³ on 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_8192.txt")
+KERNEL_SOURCES = ["matrix_core_engineering_amd/csrc/k_fast.hip",
+                  "matrix_core_engineering_amd/csrc/common.hpp",
+                  "matrix_core_engineering_amd/csrc/sched.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy"], default=None)
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Workload:
+    """One standard workload's operands resident on the device."""
+
+    def __init__(self, cfg, dev):
+        import torch
+        from matrix_core_engineering_amd.inputs import config_problem
+        self.p = p = config_problem(cfg)
+
+        def up(a):
+            v = {1: np.uint8, 2: np.int16, 4: np.int32}[a.dtype.itemsize]
+            return torch.from_numpy(np.ascontiguousarray(a).view(v)).to(dev)
+
+        self.A, self.B = up(p.A), up(p.B)
+        self.SA = up(p.SA) if p.SA is not None else None
+        self.SB = up(p.SB) if p.SB is not None else None
+        self.C = torch.zeros((p.M, p.ldc), dtype=torch.int16 if p.c_dtype == 1 else torch.float32,
+                             device=dev)
+
+    def run(self, stream):
+        import matrix_core_engineering_amd as mce
+        p = self.p
+        if p.SA is None:
+            return mce.gemm_bf16(p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.B, p.ldb,
+                                 p.b_col_major, self.C, p.ldc, p.c_col_major, p.c_dtype,
+                                 p.alpha, p.beta, stream=stream)
+        return mce.gemm_mxfp8(p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.SA, p.ld_sa,
+                              self.B, p.ldb, p.b_col_major, self.SB, p.ld_sb, self.C, p.ldc,
+                              p.c_col_major, p.c_dtype, p.alpha, p.beta, stream=stream)
+
+    def level(self):
+        import matrix_core_engineering_amd as mce
+        p = self.p
+        if p.SA is None:
+            return mce.gemm_bf16_pick_level(p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.B,
+                                            p.ldb, p.b_col_major)
+        return mce.gemm_mxfp8_pick_level(p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.B,
+                                         p.ldb, p.b_col_major)
+
+
+def read_traffic():
+    """HBM bytes per launch of the bf16 kernel from the committed counter
+    summary, or None if it is missing or was taken on other kernel code."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(work, target_s):
+    """Times the oracle on rows [0, R) of the bf16 workload (R sized for
+    about target_s seconds) and checks those rows of the GPU result."""
+    import oracle
+    import torch
+    p = work.p
+    kw = p.oracle_kwargs()
+    # two calibration runs separate the fixed cost (decoding all of B) from
+    # the per-row cost; then the sample
+    t0 = time.perf_counter()
+    oracle.gemm_rows(row_begin=0, row_end=16, **kw)
+    t16 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gemm_rows(row_begin=0, row_end=64, **kw)
+    t64 = time.perf_counter() - t0
+    per_row = max((t64 - t16) / 48, 1e-5)
+    fixed = max(t16 - 16 * per_row, 0.0)
+    rows = int(min(p.M, max(64, (target_s - fixed) / per_row)))
+    t0 = time.perf_counter()
+    cref, tsum = oracle.gemm_rows(row_begin=0, row_end=rows, **kw)
+    secs = time.perf_counter() - t0
+    got_bits = work.C[:rows, :p.N].cpu().numpy().view(np.uint16)
+    got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ok, worst, bad = oracle.check(got, cref, tsum, out_bf16=True)
+    flops = 2.0 * rows * p.N * p.K
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the 8192^3 bf16 GEMM (all 8192 columns, full K), "
+                      f"fp64, {secs:.1f} s",
+            "seconds": secs, "sample_rows_checked_ok": bool(ok),
+            "sample_worst_err_over_tol": worst}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU split of the GEMM is a design note, not a measured path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import matrix_core_engineering_amd as mce
+    mce.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.reps + 1):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {args.reps + 1} x {n} bytes", flush=True)
+        return
+    if args.only:
+        work = Workload(4 if args.only == "bf16" else 5, dev)
+        for _ in range(args.reps + 1):
+            work.run(stream)
+        torch.cuda.synchronize()
+        print(f"ran {args.only} level {work.level()} x {args.reps + 1}", flush=True)
+        return
+
+    works = {"bf16_8192": Workload(4, dev), "mxfp8_8192": Workload(5, dev)}
+    names = list(works)
+    for _ in range(args.warmup):
+        for w in works.values():
+            w.run(stream)
+    torch.cuda.synchronize()
+
+    # events on the library's stream around every launch of the timed steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, n in enumerate(names):
+            works[n].run(stream)
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]
+    per_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+              for i, n in enumerate(names)}
+    ms_per_step = float(np.sum(step_ms) / args.steps)
+    flops = {n: works[n].p.flops for n in names}
+    value = sum(flops.values()) / (ms_per_step * 1e-3) / 1e12
+
+    per_workload = {}
+    for n in names:
+        peak = PEAK_BF16 if n.startswith("bf16") else PEAK_FP8
+        tf = flops[n] / (per_ms[n] * 1e-3) / 1e12
+        per_workload[n] = {"us_per_launch": per_ms[n] * 1e3, "tflops": tf,
+                           "peak_tflops": peak, "frac_of_peak": tf / peak,
+                           "level": works[n].level()}
+    dom = max(names, key=lambda n: per_ms[n])
+    traffic = read_traffic() if dom.startswith("bf16") else None
+    roofline = {"bound": "mfma", "achieved": per_workload[dom]["tflops"],
+                "peak": per_workload[dom]["peak_tflops"], "unit": "TFLOP/s",
+                "frac": per_workload[dom]["frac_of_peak"], "traffic": traffic,
+                "kernel": f"{dom} (level {per_workload[dom]['level']})",
+                "flops_per_launch": flops[dom], "us_per_launch": per_ms[dom] * 1e3}
+
+    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 and mxfp8-e4m3 operands, fp32 accumulate", "data": "synthetic",
+           "config": {"workload": "8192^3 bf16 GEMM + 8192^3 MX-fp8 GEMM per step",
+                      "M": 8192, "N": 8192, "K": 8192, "a": "row-major", "b": "column-major",
+                      "out": "bf16", "alpha": 1.0, "beta": 0.0},
+           "per_workload": per_workload, "roofline": roofline,
+           "wall_s_timed": wall}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(works["bf16_8192"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

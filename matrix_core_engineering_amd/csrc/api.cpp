@@ -93,7 +93,7 @@ bool mx_scales_eligible(const Call &c)
 }
 
 constexpr int kBestBf16Level = 6;     // the persistent pipelined kernel
-constexpr int kBestMxLevel = 3;
+constexpr int kBestMxLevel = 6;
 
 int pick_level(const Call &c)
 {

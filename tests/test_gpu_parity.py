@@ -28,7 +28,7 @@ from gpu_util import DeviceProblem, expected_bits, run_problem
 pytestmark = pytest.mark.gpu
 
 BF16_LEVELS = [1, 2, 3, 4, 5, 6]
-MX_LEVELS = [3]
+MX_LEVELS = [3, 5, 6]
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 
 
@@ -250,6 +250,33 @@ def test_mx_scale_semantics(level):
         want += 32.0 * np.exp2(ea[:, b][:, None] + eb[:, b][None, :])
     r = run_level(p, level)
     assert np.array_equal(r[0], want)
+
+
+@pytest.mark.parametrize("level", MX_LEVELS + [None])
+@pytest.mark.parametrize("shape", [(300, 270, 1040), (257, 513, 96), (256, 256, 128),
+                                   (520, 300, 4112)], ids=lambda s: "x".join(map(str, s)))
+def test_mx_padded_scale_rows_partial_k_tile(level, shape):
+    """Scale rows padded to a multiple of 4 bytes (the pipelined levels read
+    one 32-bit word per row and K tile); K not a multiple of the 128-wide K
+    tile, so the last tile has fewer than four scale blocks.  The unused
+    padding bytes hold the NaN code 0xFF, which must not reach the result."""
+    M, N, K = shape
+    nblk = (K + 31) // 32
+    ld = (nblk + 3) // 4 * 4
+    for out in (OUT_F32, OUT_BF16):
+        p = make_problem(M, N, K, fmt=E4M3FN, c_dtype=out, dist="uniform", lo=-448, hi=448,
+                         ld_sa=ld, ld_sb=ld, seed=7000 + K)
+        p.SA[:, nblk:] = 0xFF
+        p.SB[:, nblk:] = 0xFF
+        r = run_level(p, level)
+        if r is not None:
+            assert_close(p, r[0])
+        q = integer_problem(M, N, K, fmt=E4M3FN, c_dtype=out, ld_sa=ld, ld_sb=ld, seed=7100 + K)
+        q.SA[:, nblk:] = 0xFF
+        q.SB[:, nblk:] = 0xFF
+        r = run_level(q, level)
+        if r is not None:
+            assert_bitwise(q, r[1])
 
 
 def test_mx_column_major_c_and_alpha_beta():
