@@ -121,7 +121,7 @@ bool level_accepts(const Call &c, int level)
     }
     switch (level) {
     case 3: return true;
-    case 5: case 6: return fast_eligible(c) && mx_scales_eligible(c);
+    case 5: case 6: case 7: return fast_eligible(c) && mx_scales_eligible(c);
     default: return false;
     }
 }

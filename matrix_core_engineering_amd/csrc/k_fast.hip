@@ -40,6 +40,8 @@
 #include "launch.hpp"
 #include "sched.hpp"
 
+#include <type_traits>
+
 namespace mce {
 namespace {
 
@@ -109,7 +111,107 @@ struct Geometry {
     static_assert(!Op::MX || (NSA == 1 && NSB == 1), "MX scale staging assumes 256-row tiles");
 };
 
-template <class Op, int BM, int BN, int STAGES, bool PERSIST>
+// Epilogue of one workgroup tile: out = alpha*acc + beta*C0, written straight
+// from the accumulators (C^T layout: lane l owns row l % 32 and four groups
+// of four consecutive columns per 32x32 block).  Interior tiles with
+// vector-aligned C take the branch-free vector path (one uniform test per
+// tile); edge tiles mask per element.
+// Epilogue variants, chosen on the host per call: EPI_BF16_WHOLE when C is
+// bf16, beta == 0, M and N are whole tiles and C rows are 8-byte aligned
+// (one branch-free path); EPI_ANY otherwise.  Keeping the choice out of the
+// kernel's run-time branches lets the compiler move accumulators to stores
+// one block at a time.
+enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1 };
+
+template <int EPI, class G, int BM, int BN>
+__device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
+                                           int m_tile, int n_tile, int wm, int wn, int h, int l32)
+{
+    const int mbase = m_tile + wm * G::WM + l32;
+    const int nbase = n_tile + wn * G::WN + 4 * h;
+    const bool vec_c = (p.ldc % 4) == 0 &&
+                       ((uintptr_t)p.C % (p.c_dtype == OUT_F32 ? 16 : 8)) == 0;
+    const bool full = vec_c && m_tile + BM <= p.M && n_tile + BN <= p.N;
+    if (EPI == EPI_BF16_WHOLE || (full && p.c_dtype == OUT_BF16 && p.beta == 0.0f)) {
+        // the common case: one row pointer per 32-row block, columns as
+        // immediate offsets, no C read
+#pragma unroll
+        for (int i = 0; i < G::TI; ++i) {
+            uint16_t *row = (uint16_t *)p.C + (size_t)(mbase + i * 32) * p.ldc + nbase;
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx16 &a = acc[i][j];
+                    *(u16x4 *)(row + j * 32 + q * 8) =
+                        u16x4{f32_to_bf16_rne(p.alpha * a[4 * q]), f32_to_bf16_rne(p.alpha * a[4 * q + 1]),
+                              f32_to_bf16_rne(p.alpha * a[4 * q + 2]), f32_to_bf16_rne(p.alpha * a[4 * q + 3])};
+                }
+                // one 32x32 block at a time: keeps the scheduler from pulling
+                // every accumulator into VGPRs at once
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else if (EPI == EPI_BF16_WHOLE) {
+        // unreachable: the host only picks this variant for whole bf16 tiles
+    } else if (full && p.c_dtype == OUT_F32) {
+#pragma unroll
+        for (int i = 0; i < G::TI; ++i) {
+            float *row = (float *)p.C + (size_t)(mbase + i * 32) * p.ldc + nbase;
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx16 &a = acc[i][j];
+                    floatx4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    v *= p.alpha;
+                    floatx4 *dst = (floatx4 *)(row + j * 32 + q * 8);
+                    if (p.beta != 0.0f)
+                        v += p.beta * *dst;
+                    *dst = v;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else if (full) {
+        // bf16 output with beta != 0
+#pragma unroll
+        for (int i = 0; i < G::TI; ++i) {
+            uint16_t *row = (uint16_t *)p.C + (size_t)(mbase + i * 32) * p.ldc + nbase;
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx16 &a = acc[i][j];
+                    u16x4 *dst = (u16x4 *)(row + j * 32 + q * 8);
+                    const u16x4 c0 = *dst;
+                    u16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c0[e]), p.alpha * a[4 * q + e]));
+                    *dst = o;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < G::TI; ++i)
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = mbase + i * 32;
+                    const int n = nbase + j * 32 + (r >> 2) * 8 + (r & 3);
+                    if (m < p.M && n < p.N)
+                        store_c(p, m, n, acc[i][j][r]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+}
+
+template <class Op, int BM, int BN, int STAGES, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fast(GemmArgs p, int group_m)
 {
@@ -272,60 +374,10 @@ void gemm_fast(GemmArgs p, int group_m)
         }
     };
 
-    const bool vec_c = (p.ldc % 4) == 0 &&
-                       ((uintptr_t)p.C % (p.c_dtype == OUT_F32 ? 16 : 8)) == 0;
-
-    // Epilogue: out = alpha*acc + beta*C0, written straight from the
-    // accumulators.  Interior tiles with vector-aligned C take the branch-free
-    // vector path (one uniform test per tile); edge tiles mask per element.
     auto epilogue = [&](int tile_id) {
         int tm, tn;
         grouped_tile(tile_id, tiles_m, tiles_n, group_m, tm, tn);
-        const int m_tile = tm * BM, n_tile = tn * BN;
-        const int mbase = m_tile + wm * G::WM + l32;
-        const int nbase = n_tile + wn * G::WN + 4 * h;
-        const bool full = vec_c && m_tile + BM <= p.M && n_tile + BN <= p.N;
-        if (full) {
-#pragma unroll
-            for (int i = 0; i < G::TI; ++i)
-#pragma unroll
-                for (int j = 0; j < G::TJ; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const size_t idx = (size_t)(mbase + i * 32) * p.ldc + nbase + j * 32 + q * 8;
-                        floatx4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                     acc[i][j][4 * q + 3]};
-                        v *= p.alpha;
-                        if (p.c_dtype == OUT_F32) {
-                            floatx4 *dst = (floatx4 *)((float *)p.C + idx);
-                            if (p.beta != 0.0f)
-                                v += p.beta * *dst;
-                            *dst = v;
-                        } else {
-                            u16x4 *dst = (u16x4 *)((uint16_t *)p.C + idx);
-                            if (p.beta != 0.0f) {
-                                u16x4 c0 = *dst;
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    v[e] += p.beta * bf16_to_f32(c0[e]);
-                            }
-                            *dst = u16x4{f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1]),
-                                         f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])};
-                        }
-                    }
-        } else {
-#pragma unroll
-            for (int i = 0; i < G::TI; ++i)
-#pragma unroll
-                for (int j = 0; j < G::TJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = mbase + i * 32;
-                        const int n = nbase + j * 32 + (r >> 2) * 8 + (r & 3);
-                        if (m < p.M && n < p.N)
-                            store_c(p, m, n, acc[i][j][r]);
-                    }
-        }
+        store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
     };
 
     // ------------------------------------------------------------ K loop
@@ -384,7 +436,674 @@ void gemm_fast(GemmArgs p, int group_m)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Levels 5 and 6, scheduled: a four-stage ring of narrow K tiles (32 bf16 or
+// 64 E4M3 values = 64 bytes per LDS row), one barrier per K tile placed
+// before the K tile's last k-step:
+//   - the loads of K tile g+4 go into the stage released at iteration g's
+//     barrier, so each load has about three K tiles of time to land and a
+//     K tile's loads (32 KiB per workgroup) are spread thinly enough for the
+//     direct-load path;
+//   - fragments of the next k-step are read under the matrix-core
+//     instructions of the current one (two fragment register sets), and the
+//     next K tile's first fragments are read right after the barrier;
+//   - every load address is a branch-free select of precomputed per-tile
+//     offsets (row bounds folded in) with K in the scalar offset.
+// Instruction interleaving inside each barrier-free region is fixed with
+// scheduling-group barriers.  Needs at least four K tiles.
+constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
+
+struct Bf16Ring {
+    static constexpr bool MX = false;
+    static constexpr int ELT = 2;
+    static constexpr int BK = 32;     // K elements per K tile
+    static constexpr int NKS = 2;     // 32x32x16 k-steps per K tile
+};
+struct Mxfp8Ring {
+    static constexpr bool MX = true;
+    static constexpr int ELT = 1;
+    static constexpr int BK = 64;
+    static constexpr int NKS = 1;     // one 32x32x64 k-step per K tile
+};
+
+template <class Op, int BM, int BN, int S>
+struct RingGeometry {
+    static constexpr int ROWB = Op::BK * Op::ELT;          // 64 bytes per LDS row
+    static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
+    static constexpr int RPL = 1024 / ROWB;                // rows per direct load
+    static constexpr int EPC = 16 / Op::ELT;               // K elements per chunk
+    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int TI = WM / 32, TJ = WN / 32;
+    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    // one aligned 4-byte scale word per row (blocks 4*(kt/2) .. +3: this K
+    // tile's two blocks and its neighbour's); a direct load of any size
+    // fills one 4-byte LDS slot per lane
+    static constexpr int SA_BYTES = Op::MX ? BM * 4 : 0;
+    static constexpr int SB_BYTES = Op::MX ? BN * 4 : 0;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int NA = BM / RPL / 4;                // direct loads per wave per K tile
+    static constexpr int NB = BN / RPL / 4;
+    static constexpr int NSA = Op::MX ? 1 : 0;             // 4-byte scale loads: 64 rows each
+    static constexpr int NSB = Op::MX ? 1 : 0;
+    static constexpr int LOADS = NA + NB + NSA + NSB;
+    static_assert(ROWB == 64 && CH == 4 && RPL == 16, "64-byte LDS rows");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((S - 2) * LOADS < 64, "vmcnt range");
+    static_assert(!Op::MX || (BM == 256 && BN == 256), "MX scale loads assume 256-row tiles");
+};
+
+template <int LOADS>
+__device__ __forceinline__ void wait_tiles_after(int n)
+{
+    if (n <= 0)
+        wait_vmcnt<0>();
+    else if (n == 1)
+        wait_vmcnt<LOADS>();
+    else
+        wait_vmcnt<2 * LOADS>();
+}
+
+template <class Op, int BM, int BN, int S, bool PERSIST, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_ring(GemmArgs p, int group_m)
+{
+    using G = RingGeometry<Op, BM, BN, S>;
+    constexpr int NKS = Op::NKS;
+    constexpr int RPF = Op::MX ? 2 : 1;                    // LDS reads per fragment
+    constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
+    static_assert(S == 4, "the wait helper covers up to two K tiles in flight after the next");
+    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int ntiles = tiles_m * tiles_n;
+    const int nk = (p.K + Op::BK - 1) / Op::BK;            // >= S (host guarantees)
+    const int nwg = gridDim.x, wg = blockIdx.x;
+    const int first = xcd_major(wg, nwg);
+    const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
+    const int total = my_tiles * nk;
+
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        make_rsrc(p.A, (uint32_t)(((size_t)(p.M - 1) * p.lda + p.K) * Op::ELT));
+    const __amdgpu_buffer_rsrc_t rsrc_b =
+        make_rsrc(p.B, (uint32_t)(((size_t)(p.N - 1) * p.ldb + p.K) * Op::ELT));
+    const int nblk = (p.K + 31) / 32;
+    __amdgpu_buffer_rsrc_t rsrc_sa = rsrc_a, rsrc_sb = rsrc_b;
+    if constexpr (Op::MX) {
+        // scale rows are 4-byte aligned: the last row's final word may pass
+        // ceil(K/32) but stays inside its aligned word
+        const int nblk4 = (nblk + 3) & ~3;
+        rsrc_sa = make_rsrc(p.SA, (uint32_t)((size_t)(p.M - 1) * p.ld_sa + nblk4));
+        rsrc_sb = make_rsrc(p.SB, (uint32_t)((size_t)(p.N - 1) * p.ld_sb + nblk4));
+    }
+
+    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
+
+    // Direct-load geometry: load t of this wave fills 1 KiB = 16 rows of
+    // 64 bytes; lane l writes row (wave*N + t)*16 + l/4 at physical chunk
+    // l%4.  The row's low four bits are l/4, so swz4(row) = swz4(l/4) and the
+    // lane fetches the same logical chunk in every load.
+    const int lrow = lane >> 2;
+    const int lchunk = (lane & 3) ^ swz4(lrow);
+    const int kc_lane = lchunk * G::EPC;
+    uint32_t a_cur[G::NA], a_nxt[G::NA], b_cur[G::NB], b_nxt[G::NB];
+    uint32_t sa_cur = OOB_OFFSET, sa_nxt = OOB_OFFSET, sb_cur = OOB_OFFSET, sb_nxt = OOB_OFFSET;
+    auto bases = [&](int r, uint32_t (&ab)[G::NA], uint32_t (&bb)[G::NB], uint32_t &sab,
+                     uint32_t &sbb) {
+        int m0 = p.M, n0 = p.N;                            // past the end: all rows invalid
+        if (r < my_tiles) {
+            int tm, tn;
+            grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
+            m0 = tm * BM;
+            n0 = tn * BN;
+        }
+#pragma unroll
+        for (int t = 0; t < G::NA; ++t) {
+            const int row = m0 + (wave * G::NA + t) * G::RPL + lrow;
+            ab[t] = row < p.M ? (uint32_t)(row * p.lda + kc_lane) * Op::ELT : OOB_OFFSET;
+        }
+#pragma unroll
+        for (int t = 0; t < G::NB; ++t) {
+            const int row = n0 + (wave * G::NB + t) * G::RPL + lrow;
+            bb[t] = row < p.N ? (uint32_t)(row * p.ldb + kc_lane) * Op::ELT : OOB_OFFSET;
+        }
+        if constexpr (Op::MX) {
+            const int ra = m0 + wave * 64 + lane, rb = n0 + wave * 64 + lane;
+            sab = ra < p.M ? (uint32_t)(ra * p.ld_sa) : OOB_OFFSET;
+            sbb = rb < p.N ? (uint32_t)(rb * p.ld_sb) : OOB_OFFSET;
+        }
+    };
+
+    // Direct loads of K tile kt of the current (next) tile into `stage`, in
+    // two halves (part 0: the first half of the A and B loads and the scale
+    // words; part 1: the rest) so that a K tile's loads spread over two
+    // k-steps; `on` false turns every lane out of range (nothing is fetched).
+    auto issue = [&](bool next, int kt, int stage, bool on, int part) {
+        const int k0 = kt * Op::BK;
+        const bool ok = on && k0 + kc_lane < p.K;
+        const int soff = k0 * Op::ELT;
+        char *base = smem + stage * G::STAGE_BYTES;
+#pragma unroll
+        for (int t = part * G::NA / 2; t < (part + 1) * G::NA / 2; ++t) {
+            const uint32_t voff = ok ? (next ? a_nxt[t] : a_cur[t]) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (lds_ptr_t)(base + (wave * G::NA + t) * 1024), 16, voff, soff, 0, 0);
+        }
+#pragma unroll
+        for (int t = part * G::NB / 2; t < (part + 1) * G::NB / 2; ++t) {
+            const uint32_t voff = ok ? (next ? b_nxt[t] : b_cur[t]) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (lds_ptr_t)(base + G::A_BYTES + (wave * G::NB + t) * 1024), 16, voff, soff,
+                0, 0);
+        }
+        if (Op::MX && part == 0) {
+            // the aligned scale word holding blocks 2kt and 2kt+1 of each row
+            char *sbase = base + G::A_BYTES + G::B_BYTES;
+            const uint32_t va = on ? (next ? sa_nxt : sa_cur) : OOB_OFFSET;
+            const uint32_t vb = on ? (next ? sb_nxt : sb_cur) : OOB_OFFSET;
+            const int sw = (2 * kt) & ~3;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sa, (lds_ptr_t)(sbase + wave * 256), 4,
+                                                     va, sw, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_sb, (lds_ptr_t)(sbase + G::SA_BYTES + wave * 256), 4, vb, sw, 0, 0);
+        }
+    };
+
+    typedef typename std::conditional<Op::MX, intx8, bf16x8>::type Frag;
+    Frag fa[2][G::TI], fb[2][G::TJ];
+    int sc_a[G::TI], sc_b[G::TJ];      // MX scale bytes of the K tile being consumed
+    int sn_a[G::TI], sn_b[G::TJ];      // ... of the next K tile
+    const int swz_lane = swz4(l32 & 15);   // rows a lane reads differ by multiples of 16
+
+    auto read_frags = [&](int set, int stage, int ks) {
+        const char *As = smem + stage * G::STAGE_BYTES;
+        const char *Bs = As + G::A_BYTES;
+        if constexpr (!Op::MX) {
+            const int chunk = ((2 * ks + h) ^ swz_lane) * 16;
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i)
+                fa[set][i] = *(const bf16x8 *)(As + (wm * G::WM + i * 32 + l32) * G::ROWB + chunk);
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                fb[set][j] = *(const bf16x8 *)(Bs + (wn * G::WN + j * 32 + l32) * G::ROWB + chunk);
+        } else {
+            // lane (l32, h): k = 16h..16h+15 and 32+16h..32+16h+15 of the K tile
+            const int c_lo = (h ^ swz_lane) * 16;
+            const int c_hi = ((2 + h) ^ swz_lane) * 16;
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i) {
+                const char *row = As + (wm * G::WM + i * 32 + l32) * G::ROWB;
+                intx4 lo = *(const intx4 *)(row + c_lo), hi = *(const intx4 *)(row + c_hi);
+                fa[set][i] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+                const char *row = Bs + (wn * G::WN + j * 32 + l32) * G::ROWB;
+                intx4 lo = *(const intx4 *)(row + c_lo), hi = *(const intx4 *)(row + c_hi);
+                fb[set][j] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        }
+    };
+
+    // MX: the scale byte of each lane's block (block 2kt + h of its row); a
+    // block at or past ceil(K/32) holds zero data and gets 127 (x1).
+    auto read_scales = [&](int stage, int kt) {
+        if constexpr (Op::MX) {
+            const uint32_t *SAs =
+                (const uint32_t *)(smem + stage * G::STAGE_BYTES + G::A_BYTES + G::B_BYTES);
+            const uint32_t *SBs = SAs + BM;
+            const bool past = 2 * kt + h >= nblk;
+            const int shift = 8 * (2 * (kt & 1) + h);
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i) {
+                const uint32_t w = SAs[wm * G::WM + i * 32 + l32];
+                sn_a[i] = past ? 127 : (int)((w >> shift) & 0xFF);
+            }
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+                const uint32_t w = SBs[wn * G::WN + j * 32 + l32];
+                sn_b[j] = past ? 127 : (int)((w >> shift) & 0xFF);
+            }
+        }
+    };
+
+    floatx16 acc[G::TI][G::TJ];
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int i = 0; i < G::TI; ++i)
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+                if constexpr (!Op::MX)
+                    acc[i][j] = mfma_bf16(fb[set][j], fa[set][i], acc[i][j]);
+                else
+                    acc[i][j] = mfma_mxfp8<0>(fb[set][j], fa[set][i], acc[i][j], sc_b[j], sc_a[i]);
+            }
+    };
+
+    // ---------------------------------------------------------- prologue
+    bases(0, a_cur, b_cur, sa_cur, sb_cur);
+    bases(1, a_nxt, b_nxt, sa_nxt, sb_nxt);
+    // K tiles 0..S-2 whole and the first half of K tile S-1 (nk >= S: all in
+    // tile 0); that tile's second half is the first iteration's pending half.
+    // A direct load always writes LDS (zeros when out of range), so no
+    // placeholder load may target a stage in use.
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) {
+        issue(false, q, q, true, 0);
+        issue(false, q, q, true, 1);
+    }
+    issue(false, S - 1, S - 1, true, 0);
+    constexpr int P0 = (G::NA + G::NB) / 2 + G::NSA + G::NSB;   // loads in a first half
+    wait_vmcnt<(S - 2) * G::LOADS + P0>();         // K tile 0 landed
+    barrier();
+    read_frags(0, 0, 0);
+    read_scales(0, 0);
+#pragma unroll
+    for (int i = 0; i < G::TI; ++i)
+        sc_a[i] = sn_a[i];
+#pragma unroll
+    for (int j = 0; j < G::TJ; ++j)
+        sc_b[j] = sn_b[j];
+
+    constexpr int NM = G::TI * G::TJ;
+    int stage = 0, g = 0;
+    // the second half of the K tile whose first half went out last iteration
+    bool pend_next = false, pend_on = true;
+    int pend_kt = S - 1, pend_stage = S - 1;
+    for (int r = 0; r < my_tiles; ++r) {
+#pragma unroll
+        for (int i = 0; i < G::TI; ++i)
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                acc[i][j] = zero16();
+        for (int kt = 0; kt < nk; ++kt, ++g) {
+            // region 1: k-steps 0..NKS-2, each reading the next k-step's
+            // fragments under its matrix-core instructions
+#pragma unroll
+            for (int ks = 0; ks < NKS - 1; ++ks) {
+                read_frags((ks + 1) & 1, stage, ks + 1);
+                if (ks == 0)
+                    issue(pend_next, pend_kt, pend_stage, pend_on, 1);
+                mfmas(ks & 1);
+                constexpr int VM1 = (G::NA + G::NB) / 2;
+#pragma unroll
+                for (int x = 0; x < FRAG_READS; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+                }
+#pragma unroll
+                for (int x = 0; x < NM - FRAG_READS; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (ks == 0 && x < VM1)
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+                }
+            }
+            if constexpr (NKS == 1)
+                issue(pend_next, pend_kt, pend_stage, pend_on, 1);
+            // ready: K tile g+1 landed (K tiles g+2, g+3 may stay in flight);
+            // free: every wave's reads of K tile g are in registers
+            {
+                const int after = total - 2 - g;
+                wait_tiles_after<G::LOADS>(after < S - 2 ? after : S - 2);
+            }
+            wait_lgkm0();
+            barrier();
+            // region 2: the last k-step; read K tile g+1's first fragments and
+            // scales, then load K tile g+S into the stage just released
+            const int nstage = stage + 1 == S ? 0 : stage + 1;
+            constexpr int set_last = (NKS - 1) & 1;
+            constexpr int set_next = NKS == 1 ? 1 : 0;
+            read_frags(set_next, nstage, 0);
+            read_scales(nstage, kt + 1 < nk ? kt + 1 : 0);
+            {
+                const int kl = kt + S;
+                pend_next = kl >= nk;
+                pend_kt = pend_next ? kl - nk : kl;
+                pend_stage = stage;
+                pend_on = g + S < total;
+                issue(pend_next, pend_kt, pend_stage, pend_on, 0);
+            }
+            mfmas(set_last);
+            {
+                constexpr int NDS = FRAG_READS + (Op::MX ? G::TI + G::TJ : 0);
+                constexpr int DS_PER = (NDS + NM / 2 - 1) / (NM / 2);
+                constexpr int VM_PER = ((G::NA + G::NB) / 2 + G::NSA + G::NSB + NM / 2 - 1) / (NM / 2);
+#pragma unroll
+                for (int x = 0; x < NM / 2; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, DS_PER, 0);
+                }
+#pragma unroll
+                for (int x = 0; x < NM / 2; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, VM_PER, 0);
+                }
+            }
+            if constexpr (NKS == 1) {
+                // one k-step per K tile: the next K tile's fragments move into
+                // the set the next iteration consumes
+#pragma unroll
+                for (int i = 0; i < G::TI; ++i)
+                    fa[0][i] = fa[1][i];
+#pragma unroll
+                for (int j = 0; j < G::TJ; ++j)
+                    fb[0][j] = fb[1][j];
+            }
+            if constexpr (Op::MX) {
+#pragma unroll
+                for (int i = 0; i < G::TI; ++i)
+                    sc_a[i] = sn_a[i];
+#pragma unroll
+                for (int j = 0; j < G::TJ; ++j)
+                    sc_b[j] = sn_b[j];
+            }
+            stage = nstage;
+        }
+        int tm, tn;
+        grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
+        store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+        // the load side moves one tile ahead
+#pragma unroll
+        for (int t = 0; t < G::NA; ++t)
+            a_cur[t] = a_nxt[t];
+#pragma unroll
+        for (int t = 0; t < G::NB; ++t)
+            b_cur[t] = b_nxt[t];
+        sa_cur = sa_nxt;
+        sb_cur = sb_nxt;
+        bases(r + 2, a_nxt, b_nxt, sa_nxt, sb_nxt);
+        // the pending half belongs to the tile that is now current
+        pend_next = false;
+    }
+    wait_vmcnt<0>();   // no direct load still writing LDS when the waves end
+}
+
+// ---------------------------------------------------------------------------
+// Level 7: role-specialised waves ("B200 GEMM Optimization Ladder", section
+// E step 8: producer / matrix-core / writeback roles and their hand-offs).
+//
+// Eight waves, two per SIMD, in two groups of four.  Each wave owns a 128x64
+// slice of the 256x256 tile (128 accumulator registers, so two waves fit a
+// SIMD's register file).  A wave alternates two roles, and the groups are
+// one role apart, so on every SIMD one wave feeds the matrix core while the
+// other moves data:
+//   memory role:  read the whole K tile's fragments from LDS into registers,
+//                 issue this wave's share of the direct loads of K tile
+//                 g+S-1, write back the previous tile's result when a tile
+//                 ends, and wait for its own loads of K tile g+1;
+//   compute role: the K tile's matrix-core instructions, back to back, on
+//                 fragments already in registers (raised issue priority).
+// Every role boundary is a workgroup barrier.  The four hand-offs:
+//   load -> compute (ready): a K tile's loads are waited for by each issuing
+//       wave in its memory role one K tile ahead, before a barrier that
+//       precedes every read of that tile;
+//   compute -> load (free): a stage is reloaded only in the memory role after
+//       both groups have read it (two barriers later);
+//   compute -> writeback: the accumulators are stored in the memory role
+//       after the tile's last compute role;
+//   writeback -> compute: the accumulators are zeroed after the stores are
+//       issued, before the next compute role.
+// The ring: S = 4 stages of 32-wide bf16 (64-wide fp8) K tiles, 64-byte LDS
+// rows with the swz4 swizzle, as in gemm_ring.  Needs at least four K tiles.
+struct PP {
+    static constexpr int BM = 256, BN = 256, S = 4;
+    static constexpr int WM = 128, WN = 64;        // wave tile
+    static constexpr int TI = WM / 32, TJ = WN / 32;
+    static constexpr int ROWB = 64, RPL = 16;
+    static constexpr int NA = BM / RPL / 8, NB = BN / RPL / 8;   // loads per wave per K tile
+};
+
+template <class Op, bool PERSIST, int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pingpong(GemmArgs p, int group_m)
+{
+    constexpr int BM = PP::BM, BN = PP::BN, S = PP::S;
+    constexpr int TI = PP::TI, TJ = PP::TJ;
+    constexpr int EPC = 16 / Op::ELT;
+    constexpr int A_BYTES = BM * PP::ROWB, B_BYTES = BN * PP::ROWB;
+    constexpr int SA_BYTES = Op::MX ? BM * 4 : 0, SB_BYTES = Op::MX ? BN * 4 : 0;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+    constexpr int LOADS = PP::NA + PP::NB + (Op::MX ? 1 : 0);    // per wave per K tile
+    constexpr int KS = Op::MX ? 1 : 2;                           // k-steps per K tile
+    static_assert(S * STAGE_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((S - 2) * LOADS < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2, pos = wave & 3;                   // SIMD = pos
+    const int wm = pos >> 1, wn = (pos & 1) * 2 + grp;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int ntiles = tiles_m * tiles_n;
+    const int nk = (p.K + Op::BK - 1) / Op::BK;                  // >= S (host guarantees)
+    const int nwg = gridDim.x, wg = blockIdx.x;
+    const int first = xcd_major(wg, nwg);
+    const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
+    const int total = my_tiles * nk;
+
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        make_rsrc(p.A, (uint32_t)(((size_t)(p.M - 1) * p.lda + p.K) * Op::ELT));
+    const __amdgpu_buffer_rsrc_t rsrc_b =
+        make_rsrc(p.B, (uint32_t)(((size_t)(p.N - 1) * p.ldb + p.K) * Op::ELT));
+    const int nblk = (p.K + 31) / 32;
+    __amdgpu_buffer_rsrc_t rsrc_s = rsrc_a;       // this wave's scale operand (MX)
+    int s_rows = 0, s_ld = 0;
+    if constexpr (Op::MX) {
+        const int nblk4 = (nblk + 3) & ~3;
+        // waves 0-3 stage A's scale words, waves 4-7 B's
+        rsrc_s = grp == 0 ? make_rsrc(p.SA, (uint32_t)((size_t)(p.M - 1) * p.ld_sa + nblk4))
+                          : make_rsrc(p.SB, (uint32_t)((size_t)(p.N - 1) * p.ld_sb + nblk4));
+        s_rows = grp == 0 ? p.M : p.N;
+        s_ld = grp == 0 ? p.ld_sa : p.ld_sb;
+    }
+
+    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
+
+    // Direct-load geometry: this wave's loads t = 0..N-1 fill LDS rows
+    // (wave*N + t)*16 .. +15; lane l writes row +l/4 at physical chunk l%4 and
+    // fetches logical chunk (l%4) ^ swz4(l/4).
+    const int lrow = lane >> 2;
+    const int kc_lane = ((lane & 3) ^ swz4(lrow)) * EPC;
+    uint32_t a_cur[PP::NA], a_nxt[PP::NA], b_cur[PP::NB], b_nxt[PP::NB];
+    uint32_t s_cur = OOB_OFFSET, s_nxt = OOB_OFFSET;
+    auto bases = [&](int r, uint32_t (&ab)[PP::NA], uint32_t (&bb)[PP::NB], uint32_t &sb) {
+        int m0 = p.M, n0 = p.N;
+        if (r < my_tiles) {
+            int tm, tn;
+            grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
+            m0 = tm * BM;
+            n0 = tn * BN;
+        }
+#pragma unroll
+        for (int t = 0; t < PP::NA; ++t) {
+            const int row = m0 + (wave * PP::NA + t) * PP::RPL + lrow;
+            ab[t] = row < p.M ? (uint32_t)(row * p.lda + kc_lane) * Op::ELT : OOB_OFFSET;
+        }
+#pragma unroll
+        for (int t = 0; t < PP::NB; ++t) {
+            const int row = n0 + (wave * PP::NB + t) * PP::RPL + lrow;
+            bb[t] = row < p.N ? (uint32_t)(row * p.ldb + kc_lane) * Op::ELT : OOB_OFFSET;
+        }
+        if constexpr (Op::MX) {
+            const int row = (grp == 0 ? m0 : n0) + pos * 64 + lane;
+            sb = row < s_rows ? (uint32_t)(row * s_ld) : OOB_OFFSET;
+        }
+    };
+
+    // This wave's direct loads of K tile kt (current or next tile) into
+    // `stage`; `on` false turns every lane out of range (LDS still written).
+    auto issue = [&](bool next, int kt, int stage, bool on) {
+        const int k0 = kt * Op::BK;
+        const bool ok = on && k0 + kc_lane < p.K;
+        const int soff = k0 * Op::ELT;
+        char *base = smem + stage * STAGE_BYTES;
+#pragma unroll
+        for (int t = 0; t < PP::NA; ++t) {
+            const uint32_t voff = ok ? (next ? a_nxt[t] : a_cur[t]) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (lds_ptr_t)(base + (wave * PP::NA + t) * 1024), 16, voff, soff, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < PP::NB; ++t) {
+            const uint32_t voff = ok ? (next ? b_nxt[t] : b_cur[t]) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (lds_ptr_t)(base + A_BYTES + (wave * PP::NB + t) * 1024), 16, voff, soff,
+                0, 0);
+        }
+        if constexpr (Op::MX) {
+            // aligned scale word with blocks 2kt, 2kt+1 of rows pos*64 + lane
+            char *sbase = base + A_BYTES + B_BYTES + grp * SA_BYTES + pos * 256;
+            const uint32_t v = on ? (next ? s_nxt : s_cur) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_s, (lds_ptr_t)sbase, 4, v,
+                                                     (2 * kt) & ~3, 0, 0);
+        }
+    };
+
+    typedef typename std::conditional<Op::MX, intx8, bf16x8>::type Frag;
+    Frag fa[KS][TI], fb[KS][TJ];
+    int sc_a[TI], sc_b[TJ];
+    const int swz_lane = swz4(l32 & 15);
+
+    auto read_tile = [&](int stage, int kt) {
+        const char *As = smem + stage * STAGE_BYTES;
+        const char *Bs = As + A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (!Op::MX) {
+                const int chunk = ((2 * ks + h) ^ swz_lane) * 16;
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+                    fa[ks][i] = *(const bf16x8 *)(As + (wm * PP::WM + i * 32 + l32) * PP::ROWB + chunk);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    fb[ks][j] = *(const bf16x8 *)(Bs + (wn * PP::WN + j * 32 + l32) * PP::ROWB + chunk);
+            } else {
+                const int c_lo = (h ^ swz_lane) * 16, c_hi = ((2 + h) ^ swz_lane) * 16;
+#pragma unroll
+                for (int i = 0; i < TI; ++i) {
+                    const char *row = As + (wm * PP::WM + i * 32 + l32) * PP::ROWB;
+                    intx4 lo = *(const intx4 *)(row + c_lo), hi = *(const intx4 *)(row + c_hi);
+                    fa[ks][i] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) {
+                    const char *row = Bs + (wn * PP::WN + j * 32 + l32) * PP::ROWB;
+                    intx4 lo = *(const intx4 *)(row + c_lo), hi = *(const intx4 *)(row + c_hi);
+                    fb[ks][j] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            }
+        }
+        if constexpr (Op::MX) {
+            const uint32_t *SAs = (const uint32_t *)(Bs + B_BYTES);
+            const uint32_t *SBs = SAs + BM;
+            const bool past = 2 * kt + h >= nblk;
+            const int shift = 8 * (2 * (kt & 1) + h);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+                sc_a[i] = past ? 127 : (int)((SAs[wm * PP::WM + i * 32 + l32] >> shift) & 0xFF);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                sc_b[j] = past ? 127 : (int)((SBs[wn * PP::WN + j * 32 + l32] >> shift) & 0xFF);
+        }
+    };
+
+    floatx16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+            acc[i][j] = zero16();
+
+    auto writeback = [&](int r) {
+        int tm, tn;
+        grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
+        store_tile<EPI, PP, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                acc[i][j] = zero16();
+    };
+
+    // ---------------------------------------------------------- prologue
+    bases(0, a_cur, b_cur, s_cur);
+    bases(1, a_nxt, b_nxt, s_nxt);
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q)
+        issue(false, q, q, true);                   // nk >= S: all of tile 0
+    wait_vmcnt<(S - 2) * LOADS>();                  // this wave's share of K tile 0
+    barrier();
+    if (grp == 1)
+        barrier();                                  // group 1 starts one role later
+
+    int stage = 0, g = 0;
+    for (int r = 0; r < my_tiles; ++r) {
+        for (int kt = 0; kt < nk; ++kt, ++g) {
+            // ------------------------------------------------- memory role
+            read_tile(stage, kt);
+            {
+                const int kl = kt + S - 1;
+                const bool nxt = kl >= nk;
+                issue(nxt, nxt ? kl - nk : kl, stage == 0 ? S - 1 : stage - 1, g + S - 1 < total);
+            }
+            if (kt == 0 && r > 0)
+                writeback(r - 1);
+            wait_lgkm0();
+            {
+                // own loads of K tile g+1 landed (g+2 .. g+S-1 may be in flight)
+                const int after = total - 2 - g;
+                wait_tiles_after<LOADS>(after < S - 2 ? after : S - 2);
+            }
+            barrier();
+            // ------------------------------------------------ compute role
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j) {
+                        if constexpr (!Op::MX)
+                            acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
+                        else
+                            acc[i][j] = mfma_mxfp8<0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+                    }
+            __builtin_amdgcn_s_setprio(0);
+            barrier();
+            stage = stage + 1 == S ? 0 : stage + 1;
+        }
+#pragma unroll
+        for (int t = 0; t < PP::NA; ++t)
+            a_cur[t] = a_nxt[t];
+#pragma unroll
+        for (int t = 0; t < PP::NB; ++t)
+            b_cur[t] = b_nxt[t];
+        s_cur = s_nxt;
+        bases(r + 2, a_nxt, b_nxt, s_nxt);
+    }
+    if (my_tiles > 0)
+        writeback(my_tiles - 1);
+    if (grp == 0)
+        barrier();                                  // group 0 ends one role later
+    wait_vmcnt<0>();
+}
+
 int g_num_cus = 0;
+
+// The branch-free epilogue applies: bf16 C, beta == 0, whole tiles, C rows
+// 8-byte aligned.
+bool whole_bf16(const GemmArgs &p, int bm, int bn)
+{
+    return p.c_dtype == OUT_BF16 && p.beta == 0.0f && p.M % bm == 0 && p.N % bn == 0 &&
+           p.ldc % 4 == 0 && ((uintptr_t)p.C % 8) == 0;
+}
 
 int num_cus()
 {
@@ -409,8 +1128,48 @@ hipError_t launch(const GemmArgs &p, hipStream_t s)
     int grid = ntiles;
     if (PERSIST)
         grid = ntiles < num_cus() ? ntiles : num_cus();
-    hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST>), dim3(grid), dim3(256), 0, s, p,
-                       group_m);
+    if (whole_bf16(p, BM, BN))
+        hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, EPI_BF16_WHOLE>), dim3(grid),
+                           dim3(256), 0, s, p, group_m);
+    else
+        hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, EPI_ANY>), dim3(grid), dim3(256),
+                           0, s, p, group_m);
+    return hipGetLastError();
+}
+
+template <class Op, int BM, int BN, bool PERSIST>
+hipError_t launch_ring(const GemmArgs &p, hipStream_t s)
+{
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int ntiles = tiles_m * tiles_n;
+    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    int grid = ntiles;
+    if (PERSIST)
+        grid = ntiles < num_cus() ? ntiles : num_cus();
+    if (whole_bf16(p, BM, BN))
+        hipLaunchKernelGGL((gemm_ring<Op, BM, BN, 4, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
+                           s, p, group_m);
+    else
+        hipLaunchKernelGGL((gemm_ring<Op, BM, BN, 4, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p,
+                           group_m);
+    return hipGetLastError();
+}
+
+template <class Op, bool PERSIST>
+hipError_t launch_pingpong(const GemmArgs &p, hipStream_t s)
+{
+    const int tiles_m = (p.M + PP::BM - 1) / PP::BM, tiles_n = (p.N + PP::BN - 1) / PP::BN;
+    const int ntiles = tiles_m * tiles_n;
+    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    int grid = ntiles;
+    if (PERSIST)
+        grid = ntiles < num_cus() ? ntiles : num_cus();
+    if (whole_bf16(p, PP::BM, PP::BN))
+        hipLaunchKernelGGL((gemm_pingpong<Op, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(512), 0, s, p,
+                           group_m);
+    else
+        hipLaunchKernelGGL((gemm_pingpong<Op, PERSIST, EPI_ANY>), dim3(grid), dim3(512), 0, s, p,
+                           group_m);
     return hipGetLastError();
 }
 
@@ -423,14 +1182,24 @@ bool big_tiles(const GemmArgs &p)
 
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
-    // 256x256 tiles when they give every CU work, 128x128 otherwise
+    // 256x256 tiles when they give every CU work, 128x128 otherwise; the
+    // scheduled ring needs two K tiles
     const bool big = big_tiles(p);
+    const bool ring_ok = p.K > 3 * Bf16Ring::BK;
     switch (level) {
     case 4:
         return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
     case 5:
+        if (big && ring_ok)
+            return launch_ring<Bf16Ring, 256, 256, false>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
     case 6:
+        if (big && ring_ok)
+            return launch_ring<Bf16Ring, 256, 256, true>(p, s);
+        return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
+    case 7:
+        if (ring_ok)
+            return launch_pingpong<Bf16Ring, true>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
     default:
         return hipErrorInvalidValue;
@@ -440,8 +1209,15 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s)
 {
     switch (level) {
-    case 5: return launch<Mxfp8Op, 256, 256, 2, false>(p, s);
-    case 6: return launch<Mxfp8Op, 256, 256, 2, true>(p, s);
+    case 5:
+        return p.K > 3 * Mxfp8Ring::BK ? launch_ring<Mxfp8Ring, 256, 256, false>(p, s)
+                                 : launch<Mxfp8Op, 256, 256, 2, false>(p, s);
+    case 6:
+        return p.K > 3 * Mxfp8Ring::BK ? launch_ring<Mxfp8Ring, 256, 256, true>(p, s)
+                                 : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
+    case 7:
+        return p.K > 3 * Mxfp8Ring::BK ? launch_pingpong<Mxfp8Ring, true>(p, s)
+                                       : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -61,4 +61,14 @@ MCE_HD int swz8(int row)
     return (row & 7) ^ ((row >> 3) & 1);
 }
 
+// XOR swizzle for 64-byte LDS rows (4 chunks of 16 bytes).  Among rows
+// r..r+7 (r even-aligned to 8) the rows of one parity map a logical chunk to
+// 4 distinct slots, and among rows r, r+4, r+8, r+12 it maps to 4 distinct
+// slots, so 8-lane and 16-lane groups of a 16-byte read at one logical chunk
+// over consecutive rows hit distinct banks.
+MCE_HD int swz4(int row)
+{
+    return ((row >> 1) ^ (row >> 2)) & 3;
+}
+
 } // namespace mce

@@ -27,8 +27,8 @@ from gpu_util import DeviceProblem, expected_bits, run_problem
 
 pytestmark = pytest.mark.gpu
 
-BF16_LEVELS = [1, 2, 3, 4, 5, 6]
-MX_LEVELS = [3, 5, 6]
+BF16_LEVELS = [1, 2, 3, 4, 5, 6, 7]
+MX_LEVELS = [3, 5, 6, 7]
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 
 
