@@ -117,7 +117,7 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  * Levels 4-7 need both operands K-contiguous (A row-major, B column-major),
  * 16-byte aligned base pointers, lda and ldb multiples of 8 and K a multiple
  * of 8; otherwise they return MCE_EUNSUPPORTED.  gemm_mxfp8_level accepts
- * levels 3 and 5-6 (same meaning; its level 3 also takes any K).
+ * levels 3 and 5-7 (same meaning; its level 3 also takes any K).
  */
 int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, int a_col_major,

@@ -6,16 +6,18 @@
 //            (buffer_load_dwordx4 ... lds: no VGPR staging, bounds-checked by
 //            the buffer resource) into XOR-swizzled LDS rows; one stage, so
 //            each K tile is loaded, waited for and then consumed.
-//   level 5: a ring of STAGES LDS stages with ready/free hand-offs: the
-//            loads of K tile kt+STAGES-1 are in flight while tile kt is
-//            consumed (prologue fills STAGES-1 stages, steady state, drain).
+//   level 5: a ring of LDS stages with ready/free hand-offs: the loads of
+//            later K tiles are in flight while tile kt is consumed (prologue
+//            fills the ring, steady state, drain).  The tuned form for
+//            256x256 tiles is gemm_early below; gemm_fast covers the rest.
 //   level 6: a persistent grid of one workgroup per CU walks its tiles in an
 //            XCD-aware grouped order; the ring runs across tile boundaries,
 //            so the next tile's first loads overlap this tile's last K tile
 //            and its epilogue.
 //
 // One K tile is 128 bytes of K per operand row: 64 bf16 or 128 E4M3 values,
-// i.e. eight 16-byte chunks per LDS row in both formats.  For MX operands
+// i.e. eight 16-byte chunks per LDS row in both formats (level 7 uses
+// 64-byte rows).  For MX operands
 // the E8M0 scales of the tile's four 32-element blocks (one 32-bit word per
 // row) travel with the stage, loaded by the same direct-load path, and are
 // kept apart from the operand rows ("B200 TMEM Lifecycle Planner", section
@@ -437,29 +439,22 @@ void gemm_fast(GemmArgs p, int group_m)
 }
 
 // ---------------------------------------------------------------------------
-// Levels 5 and 6, scheduled: a four-stage ring of narrow K tiles (32 bf16 or
-// 64 E4M3 values = 64 bytes per LDS row), one barrier per K tile placed
-// before the K tile's last k-step:
-//   - the loads of K tile g+4 go into the stage released at iteration g's
-//     barrier, so each load has about three K tiles of time to land and a
-//     K tile's loads (32 KiB per workgroup) are spread thinly enough for the
-//     direct-load path;
-//   - fragments of the next k-step are read under the matrix-core
-//     instructions of the current one (two fragment register sets), and the
-//     next K tile's first fragments are read right after the barrier;
-//   - every load address is a branch-free select of precomputed per-tile
-//     offsets (row bounds folded in) with K in the scalar offset.
-// Instruction interleaving inside each barrier-free region is fixed with
-// scheduling-group barriers.  Needs at least four K tiles.
+// Pieces shared by the pipelined kernels below: scheduling-group masks for
+// fixing the interleave of matrix-core instructions with LDS reads and
+// direct loads inside a barrier-free region, the K-tile formats, and the
+// stage geometry.  Every load address is a branch-free select of per-tile
+// offsets computed once per tile (row bounds folded in), with K in the
+// scalar offset.
 constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 
-struct Bf16Ring {
+// 64-byte LDS rows (the role-specialised kernel)
+struct Bf16Ring {                     // 64-byte rows
     static constexpr bool MX = false;
     static constexpr int ELT = 2;
     static constexpr int BK = 32;     // K elements per K tile
     static constexpr int NKS = 2;     // 32x32x16 k-steps per K tile
 };
-struct Mxfp8Ring {
+struct Mxfp8Ring {                    // 64-byte rows
     static constexpr bool MX = true;
     static constexpr int ELT = 1;
     static constexpr int BK = 64;
@@ -468,16 +463,16 @@ struct Mxfp8Ring {
 
 template <class Op, int BM, int BN, int S>
 struct RingGeometry {
-    static constexpr int ROWB = Op::BK * Op::ELT;          // 64 bytes per LDS row
+    static constexpr int ROWB = Op::BK * Op::ELT;          // 64 or 128 bytes per LDS row
     static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
     static constexpr int RPL = 1024 / ROWB;                // rows per direct load
     static constexpr int EPC = 16 / Op::ELT;               // K elements per chunk
     static constexpr int WM = BM / 2, WN = BN / 2;
     static constexpr int TI = WM / 32, TJ = WN / 32;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-    // one aligned 4-byte scale word per row (blocks 4*(kt/2) .. +3: this K
-    // tile's two blocks and its neighbour's); a direct load of any size
-    // fills one 4-byte LDS slot per lane
+    // one aligned 4-byte scale word per row (the four blocks containing the K
+    // tile's blocks); a direct load of any size fills one 4-byte LDS slot per
+    // lane
     static constexpr int SA_BYTES = Op::MX ? BM * 4 : 0;
     static constexpr int SB_BYTES = Op::MX ? BN * 4 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
@@ -487,12 +482,16 @@ struct RingGeometry {
     static constexpr int NSA = Op::MX ? 1 : 0;             // 4-byte scale loads: 64 rows each
     static constexpr int NSB = Op::MX ? 1 : 0;
     static constexpr int LOADS = NA + NB + NSA + NSB;
-    static_assert(ROWB == 64 && CH == 4 && RPL == 16, "64-byte LDS rows");
+    static_assert((ROWB == 64 && CH == 4 && RPL == 16) || (ROWB == 128 && CH == 8 && RPL == 8),
+                  "64- or 128-byte LDS rows");
+    static_assert(NA % 2 == 0 && NB % 2 == 0, "loads split in halves; swizzle parity");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((S - 2) * LOADS < 64, "vmcnt range");
     static_assert(!Op::MX || (BM == 256 && BN == 256), "MX scale loads assume 256-row tiles");
 };
 
+// Waits until at most n K tiles' loads (n <= 3) of LOADS direct loads each
+// are still in flight.
 template <int LOADS>
 __device__ __forceinline__ void wait_tiles_after(int n)
 {
@@ -500,19 +499,63 @@ __device__ __forceinline__ void wait_tiles_after(int n)
         wait_vmcnt<0>();
     else if (n == 1)
         wait_vmcnt<LOADS>();
-    else
+    else if (n == 2)
         wait_vmcnt<2 * LOADS>();
+    else
+        wait_vmcnt<3 * LOADS>();
 }
 
-template <class Op, int BM, int BN, int S, bool PERSIST, int EPI>
+// ---------------------------------------------------------------------------
+// Levels 5 and 6, early release: a two-stage ring of K tiles with 128-byte
+// LDS rows (64 bf16 or 128 E4M3 values per row), so every direct load moves
+// whole 128-byte lines; on MI355X a direct load of 64-byte row segments
+// delivers about half the bytes per clock of one of 128-byte rows.  With
+// only two stages the next-but-one K tile can be loaded only once the stage
+// is released, so each wave reads the whole K tile's fragments into
+// registers during its first k-step and releases the stage early.  Two
+// barriers per K tile g (stage s = g % 2):
+//   phase A  k-step 0 on the matrix cores; fragments of k-steps 1.. read;
+//   barrier 1 (free):  every wave's reads of stage s are in registers;
+//   phase X  the next k-steps; the loads of K tile g+2 into stage s begin;
+//   barrier 2 (ready): each wave waited for its loads of K tile g+1;
+//   phase Y  the last matrix-core instructions of K tile g; K tile g+1's
+//            first fragments (and MX scales) read; the remaining loads.
+// The loads of a K tile spread over phases X and Y of one iteration and have
+// until barrier 2 of the next to land.  Needs at least two K tiles.
+// Per format: XM matrix-core instructions in phase X; LX and LY of a K
+// tile's direct loads issued in phases X and Y, the rest in the next phase
+// A; YA of the next K tile's first A fragments read in phase Y, the rest in
+// the next phase A (the instruction order needs A fragment i only from the
+// (TJ*i)-th instruction on).
+struct Bf16Ring64 {                   // 128-byte rows
+    static constexpr bool MX = false;
+    static constexpr int ELT = 2;
+    static constexpr int BK = 64;
+    static constexpr int NKS = 4;
+    static constexpr int XM = 32, LX = 11, LY = 5, YA = 4;
+};
+struct Mxfp8Ring128 {                 // 128-byte rows
+    static constexpr bool MX = true;
+    static constexpr int ELT = 1;
+    static constexpr int BK = 128;
+    static constexpr int NKS = 2;
+    static constexpr int XM = 7, LX = 6, LY = 6, YA = 1;
+};
+
+template <class Op, int BM, int BN, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_ring(GemmArgs p, int group_m)
+void gemm_early(GemmArgs p, int group_m)
 {
-    using G = RingGeometry<Op, BM, BN, S>;
+    using G = RingGeometry<Op, BM, BN, 2>;
     constexpr int NKS = Op::NKS;
+    constexpr int NM = G::TI * G::TJ;                      // matrix-core instructions per k-step
     constexpr int RPF = Op::MX ? 2 : 1;                    // LDS reads per fragment
     constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
-    static_assert(S == 4, "the wait helper covers up to two K tiles in flight after the next");
+    constexpr int XM = Op::XM, YM = (NKS - 1) * NM - XM;   // phases X and Y
+    constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA;
+    static_assert(G::CH == 8, "128-byte LDS rows");
+    static_assert(XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
+    static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -522,7 +565,7 @@ void gemm_ring(GemmArgs p, int group_m)
 
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int nk = (p.K + Op::BK - 1) / Op::BK;            // >= S (host guarantees)
+    const int nk = (p.K + Op::BK - 1) / Op::BK;            // >= 2 (host guarantees)
     const int nwg = gridDim.x, wg = blockIdx.x;
     const int first = xcd_major(wg, nwg);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
@@ -544,13 +587,13 @@ void gemm_ring(GemmArgs p, int group_m)
 
     auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
 
-    // Direct-load geometry: load t of this wave fills 1 KiB = 16 rows of
-    // 64 bytes; lane l writes row (wave*N + t)*16 + l/4 at physical chunk
-    // l%4.  The row's low four bits are l/4, so swz4(row) = swz4(l/4) and the
-    // lane fetches the same logical chunk in every load.
-    const int lrow = lane >> 2;
-    const int lchunk = (lane & 3) ^ swz4(lrow);
-    const int kc_lane = lchunk * G::EPC;
+    // Direct-load geometry: load t of this wave fills 1 KiB = 8 rows of 128
+    // bytes; lane l writes row (wave*N + t)*8 + l/8 at physical chunk l%8;
+    // swz8(row) = (l/8) ^ (t&1) (bit 3 of the row is the parity of
+    // wave*N + t, N even), so a lane fetches one of two logical chunks.
+    const int lrow = lane >> 3;
+    const int kc_even = ((lane & 7) ^ lrow) * G::EPC;
+    const int kc_odd = ((lane & 7) ^ lrow ^ 1) * G::EPC;
     uint32_t a_cur[G::NA], a_nxt[G::NA], b_cur[G::NB], b_nxt[G::NB];
     uint32_t sa_cur = OOB_OFFSET, sa_nxt = OOB_OFFSET, sb_cur = OOB_OFFSET, sb_nxt = OOB_OFFSET;
     auto bases = [&](int r, uint32_t (&ab)[G::NA], uint32_t (&bb)[G::NB], uint32_t &sab,
@@ -565,12 +608,14 @@ void gemm_ring(GemmArgs p, int group_m)
 #pragma unroll
         for (int t = 0; t < G::NA; ++t) {
             const int row = m0 + (wave * G::NA + t) * G::RPL + lrow;
-            ab[t] = row < p.M ? (uint32_t)(row * p.lda + kc_lane) * Op::ELT : OOB_OFFSET;
+            const int kc = (t & 1) ? kc_odd : kc_even;
+            ab[t] = row < p.M ? (uint32_t)(row * p.lda + kc) * Op::ELT : OOB_OFFSET;
         }
 #pragma unroll
         for (int t = 0; t < G::NB; ++t) {
             const int row = n0 + (wave * G::NB + t) * G::RPL + lrow;
-            bb[t] = row < p.N ? (uint32_t)(row * p.ldb + kc_lane) * Op::ELT : OOB_OFFSET;
+            const int kc = (t & 1) ? kc_odd : kc_even;
+            bb[t] = row < p.N ? (uint32_t)(row * p.ldb + kc) * Op::ELT : OOB_OFFSET;
         }
         if constexpr (Op::MX) {
             const int ra = m0 + wave * 64 + lane, rb = n0 + wave * 64 + lane;
@@ -579,129 +624,130 @@ void gemm_ring(GemmArgs p, int group_m)
         }
     };
 
-    // Direct loads of K tile kt of the current (next) tile into `stage`, in
-    // two halves (part 0: the first half of the A and B loads and the scale
-    // words; part 1: the rest) so that a K tile's loads spread over two
-    // k-steps; `on` false turns every lane out of range (nothing is fetched).
-    auto issue = [&](bool next, int kt, int stage, bool on, int part) {
+    // Direct loads number u in [LO, HI) of K tile kt of the current (next)
+    // tile into `stage`: u < NA the A rows, then the B rows, then (MX) the
+    // A and B scale words.  `on` false turns every lane out of range
+    // (nothing is fetched; zeros are still written to LDS).
+    auto issue = [&](auto lo_c, auto hi_c, bool next, int kt, int stage, bool on) {
+        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
         const int k0 = kt * Op::BK;
-        const bool ok = on && k0 + kc_lane < p.K;
+        const bool ok_even = on && k0 + kc_even < p.K, ok_odd = on && k0 + kc_odd < p.K;
         const int soff = k0 * Op::ELT;
         char *base = smem + stage * G::STAGE_BYTES;
 #pragma unroll
-        for (int t = part * G::NA / 2; t < (part + 1) * G::NA / 2; ++t) {
-            const uint32_t voff = ok ? (next ? a_nxt[t] : a_cur[t]) : OOB_OFFSET;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_a, (lds_ptr_t)(base + (wave * G::NA + t) * 1024), 16, voff, soff, 0, 0);
-        }
-#pragma unroll
-        for (int t = part * G::NB / 2; t < (part + 1) * G::NB / 2; ++t) {
-            const uint32_t voff = ok ? (next ? b_nxt[t] : b_cur[t]) : OOB_OFFSET;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_b, (lds_ptr_t)(base + G::A_BYTES + (wave * G::NB + t) * 1024), 16, voff, soff,
-                0, 0);
-        }
-        if (Op::MX && part == 0) {
-            // the aligned scale word holding blocks 2kt and 2kt+1 of each row
-            char *sbase = base + G::A_BYTES + G::B_BYTES;
-            const uint32_t va = on ? (next ? sa_nxt : sa_cur) : OOB_OFFSET;
-            const uint32_t vb = on ? (next ? sb_nxt : sb_cur) : OOB_OFFSET;
-            const int sw = (2 * kt) & ~3;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_sa, (lds_ptr_t)(sbase + wave * 256), 4,
-                                                     va, sw, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_sb, (lds_ptr_t)(sbase + G::SA_BYTES + wave * 256), 4, vb, sw, 0, 0);
+        for (int u = LO; u < HI; ++u) {
+            if (u < G::NA) {
+                const int t = u;
+                const bool ok = (t & 1) ? ok_odd : ok_even;
+                const uint32_t voff = ok ? (next ? a_nxt[t] : a_cur[t]) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_a, (lds_ptr_t)(base + (wave * G::NA + t) * 1024), 16, voff, soff, 0, 0);
+            } else if (u < G::NA + G::NB) {
+                const int t = u - G::NA;
+                const bool ok = (t & 1) ? ok_odd : ok_even;
+                const uint32_t voff = ok ? (next ? b_nxt[t] : b_cur[t]) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_b, (lds_ptr_t)(base + G::A_BYTES + (wave * G::NB + t) * 1024), 16, voff,
+                    soff, 0, 0);
+            } else if (u == G::NA + G::NB) {
+                // the K tile's aligned scale word of each row (4 blocks)
+                const uint32_t va = on ? (next ? sa_nxt : sa_cur) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_sa, (lds_ptr_t)(base + G::A_BYTES + G::B_BYTES + wave * 256), 4, va,
+                    kt * (Op::BK / 32), 0, 0);
+            } else {
+                const uint32_t vb = on ? (next ? sb_nxt : sb_cur) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc_sb,
+                    (lds_ptr_t)(base + G::A_BYTES + G::B_BYTES + G::SA_BYTES + wave * 256), 4, vb,
+                    kt * (Op::BK / 32), 0, 0);
+            }
         }
     };
 
     typedef typename std::conditional<Op::MX, intx8, bf16x8>::type Frag;
-    Frag fa[2][G::TI], fb[2][G::TJ];
-    int sc_a[G::TI], sc_b[G::TJ];      // MX scale bytes of the K tile being consumed
-    int sn_a[G::TI], sn_b[G::TJ];      // ... of the next K tile
-    const int swz_lane = swz4(l32 & 15);   // rows a lane reads differ by multiples of 16
+    Frag fa[NKS][G::TI], fb[NKS][G::TJ];   // one register set per k-step of a K tile
+    int sc_a[G::TI], sc_b[G::TJ];          // MX scale words of the K tile being consumed
+    int sn_a[G::TI], sn_b[G::TJ];          // ... of the next K tile
+    // rows a lane reads differ by multiples of 32: the swizzle is lane-constant
+    const int swz_lane = swz8(l32);
 
-    auto read_frags = [&](int set, int stage, int ks) {
-        const char *As = smem + stage * G::STAGE_BYTES;
-        const char *Bs = As + G::A_BYTES;
+    // fragment i (A) or j (B) of k-step ks from `stage`
+    auto frag = [&](const char *rowp, int ks) -> Frag {
         if constexpr (!Op::MX) {
-            const int chunk = ((2 * ks + h) ^ swz_lane) * 16;
-#pragma unroll
-            for (int i = 0; i < G::TI; ++i)
-                fa[set][i] = *(const bf16x8 *)(As + (wm * G::WM + i * 32 + l32) * G::ROWB + chunk);
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
-                fb[set][j] = *(const bf16x8 *)(Bs + (wn * G::WN + j * 32 + l32) * G::ROWB + chunk);
+            return *(const bf16x8 *)(rowp + ((2 * ks + h) ^ swz_lane) * 16);
         } else {
-            // lane (l32, h): k = 16h..16h+15 and 32+16h..32+16h+15 of the K tile
-            const int c_lo = (h ^ swz_lane) * 16;
-            const int c_hi = ((2 + h) ^ swz_lane) * 16;
-#pragma unroll
-            for (int i = 0; i < G::TI; ++i) {
-                const char *row = As + (wm * G::WM + i * 32 + l32) * G::ROWB;
-                intx4 lo = *(const intx4 *)(row + c_lo), hi = *(const intx4 *)(row + c_hi);
-                fa[set][i] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-                const char *row = Bs + (wn * G::WN + j * 32 + l32) * G::ROWB;
-                intx4 lo = *(const intx4 *)(row + c_lo), hi = *(const intx4 *)(row + c_hi);
-                fb[set][j] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
+            // lane (l32, h): k = 64ks + 16h .. +15 and 64ks + 32 + 16h .. +15
+            intx4 lo = *(const intx4 *)(rowp + ((4 * ks + h) ^ swz_lane) * 16);
+            intx4 hi = *(const intx4 *)(rowp + ((4 * ks + 2 + h) ^ swz_lane) * 16);
+            return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     };
+    auto read_a = [&](int ks, int stage, int i) {
+        fa[ks][i] = frag(smem + stage * G::STAGE_BYTES + (wm * G::WM + i * 32 + l32) * G::ROWB, ks);
+    };
+    auto read_b = [&](int ks, int stage, int j) {
+        fb[ks][j] = frag(smem + stage * G::STAGE_BYTES + G::A_BYTES +
+                             (wn * G::WN + j * 32 + l32) * G::ROWB, ks);
+    };
 
-    // MX: the scale byte of each lane's block (block 2kt + h of its row); a
-    // block at or past ceil(K/32) holds zero data and gets 127 (x1).
+    // MX: each lane's scale word of K tile kt (blocks 4kt .. 4kt+3 of its
+    // row), blocks at or past ceil(K/32) forced to 127 (x1: they hold zero
+    // data), shifted one byte down for the upper half-wave, which supplies
+    // the odd block of each instruction; op_sel then picks byte 2*ks.
     auto read_scales = [&](int stage, int kt) {
         if constexpr (Op::MX) {
             const uint32_t *SAs =
                 (const uint32_t *)(smem + stage * G::STAGE_BYTES + G::A_BYTES + G::B_BYTES);
             const uint32_t *SBs = SAs + BM;
-            const bool past = 2 * kt + h >= nblk;
-            const int shift = 8 * (2 * (kt & 1) + h);
-#pragma unroll
-            for (int i = 0; i < G::TI; ++i) {
-                const uint32_t w = SAs[wm * G::WM + i * 32 + l32];
-                sn_a[i] = past ? 127 : (int)((w >> shift) & 0xFF);
+            const int left = nblk - kt * 4;
+            uint32_t keep = 0xFFFFFFFFu, force = 0;
+            if (left < 4) {
+                keep = left <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * left));
+                force = 0x7F7F7F7Fu & ~keep;
             }
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-                const uint32_t w = SBs[wn * G::WN + j * 32 + l32];
-                sn_b[j] = past ? 127 : (int)((w >> shift) & 0xFF);
-            }
+            for (int i = 0; i < G::TI; ++i)
+                sn_a[i] = (int)(((SAs[wm * G::WM + i * 32 + l32] & keep) | force) >> (8 * h));
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                sn_b[j] = (int)(((SBs[wn * G::WN + j * 32 + l32] & keep) | force) >> (8 * h));
         }
     };
 
     floatx16 acc[G::TI][G::TJ];
-    auto mfmas = [&](int set) {
+    // matrix-core instructions q in [LO, HI) of the K tile, q = ks*NM + i*TJ + j
+    auto mfmas = [&](auto lo_c, auto hi_c) {
+        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
 #pragma unroll
-        for (int i = 0; i < G::TI; ++i)
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-                if constexpr (!Op::MX)
-                    acc[i][j] = mfma_bf16(fb[set][j], fa[set][i], acc[i][j]);
-                else
-                    acc[i][j] = mfma_mxfp8<0>(fb[set][j], fa[set][i], acc[i][j], sc_b[j], sc_a[i]);
-            }
+        for (int q = LO; q < HI; ++q) {
+            const int ks = q / NM, i = (q % NM) / G::TJ, j = q % G::TJ;
+            if constexpr (!Op::MX)
+                acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
+            else if (ks == 0)
+                acc[i][j] = mfma_mxfp8<0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+            else
+                acc[i][j] = mfma_mxfp8<2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+        }
     };
 
+    using I0 = std::integral_constant<int, 0>;
     // ---------------------------------------------------------- prologue
     bases(0, a_cur, b_cur, sa_cur, sb_cur);
     bases(1, a_nxt, b_nxt, sa_nxt, sb_nxt);
-    // K tiles 0..S-2 whole and the first half of K tile S-1 (nk >= S: all in
-    // tile 0); that tile's second half is the first iteration's pending half.
-    // A direct load always writes LDS (zeros when out of range), so no
-    // placeholder load may target a stage in use.
-#pragma unroll
-    for (int q = 0; q < S - 1; ++q) {
-        issue(false, q, q, true, 0);
-        issue(false, q, q, true, 1);
-    }
-    issue(false, S - 1, S - 1, true, 0);
-    constexpr int P0 = (G::NA + G::NB) / 2 + G::NSA + G::NSB;   // loads in a first half
-    wait_vmcnt<(S - 2) * G::LOADS + P0>();         // K tile 0 landed
+    // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
+    // issues (a direct load always writes LDS, so no placeholder load may
+    // target a stage in use)
+    issue(I0(), std::integral_constant<int, G::LOADS>(), false, 0, 0, true);
+    issue(I0(), std::integral_constant<int, LX + LY>(), false, 1, 1, true);
+    wait_vmcnt<LX + LY>();                         // K tile 0 landed
     barrier();
-    read_frags(0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < YA; ++i)
+        read_a(0, 0, i);
+#pragma unroll
+    for (int j = 0; j < G::TJ; ++j)
+        read_b(0, 0, j);
     read_scales(0, 0);
 #pragma unroll
     for (int i = 0; i < G::TI; ++i)
@@ -710,11 +756,10 @@ void gemm_ring(GemmArgs p, int group_m)
     for (int j = 0; j < G::TJ; ++j)
         sc_b[j] = sn_b[j];
 
-    constexpr int NM = G::TI * G::TJ;
-    int stage = 0, g = 0;
-    // the second half of the K tile whose first half went out last iteration
-    bool pend_next = false, pend_on = true;
-    int pend_kt = S - 1, pend_stage = S - 1;
+    int g = 0;
+    // the last LA loads of the K tile whose loads began last iteration
+    bool pn_next = false, pn_on = true;
+    int pn_kt = 1, pn_stage = 1;
     for (int r = 0; r < my_tiles; ++r) {
 #pragma unroll
         for (int i = 0; i < G::TI; ++i)
@@ -722,77 +767,86 @@ void gemm_ring(GemmArgs p, int group_m)
             for (int j = 0; j < G::TJ; ++j)
                 acc[i][j] = zero16();
         for (int kt = 0; kt < nk; ++kt, ++g) {
-            // region 1: k-steps 0..NKS-2, each reading the next k-step's
-            // fragments under its matrix-core instructions
+            const int stage = g & 1;
+            // phase A: k-step 0; the K tile's other fragments into registers;
+            // the last loads of K tile g+1
 #pragma unroll
-            for (int ks = 0; ks < NKS - 1; ++ks) {
-                read_frags((ks + 1) & 1, stage, ks + 1);
-                if (ks == 0)
-                    issue(pend_next, pend_kt, pend_stage, pend_on, 1);
-                mfmas(ks & 1);
-                constexpr int VM1 = (G::NA + G::NB) / 2;
+            for (int i = YA; i < G::TI; ++i)
+                read_a(0, stage, i);
 #pragma unroll
-                for (int x = 0; x < FRAG_READS; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-                }
-#pragma unroll
-                for (int x = 0; x < NM - FRAG_READS; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    if (ks == 0 && x < VM1)
-                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-                }
-            }
-            if constexpr (NKS == 1)
-                issue(pend_next, pend_kt, pend_stage, pend_on, 1);
-            // ready: K tile g+1 landed (K tiles g+2, g+3 may stay in flight);
-            // free: every wave's reads of K tile g are in registers
-            {
-                const int after = total - 2 - g;
-                wait_tiles_after<G::LOADS>(after < S - 2 ? after : S - 2);
-            }
-            wait_lgkm0();
-            barrier();
-            // region 2: the last k-step; read K tile g+1's first fragments and
-            // scales, then load K tile g+S into the stage just released
-            const int nstage = stage + 1 == S ? 0 : stage + 1;
-            constexpr int set_last = (NKS - 1) & 1;
-            constexpr int set_next = NKS == 1 ? 1 : 0;
-            read_frags(set_next, nstage, 0);
-            read_scales(nstage, kt + 1 < nk ? kt + 1 : 0);
-            {
-                const int kl = kt + S;
-                pend_next = kl >= nk;
-                pend_kt = pend_next ? kl - nk : kl;
-                pend_stage = stage;
-                pend_on = g + S < total;
-                issue(pend_next, pend_kt, pend_stage, pend_on, 0);
-            }
-            mfmas(set_last);
-            {
-                constexpr int NDS = FRAG_READS + (Op::MX ? G::TI + G::TJ : 0);
-                constexpr int DS_PER = (NDS + NM / 2 - 1) / (NM / 2);
-                constexpr int VM_PER = ((G::NA + G::NB) / 2 + G::NSA + G::NSB + NM / 2 - 1) / (NM / 2);
-#pragma unroll
-                for (int x = 0; x < NM / 2; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, DS_PER, 0);
-                }
-#pragma unroll
-                for (int x = 0; x < NM / 2; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, VM_PER, 0);
-                }
-            }
-            if constexpr (NKS == 1) {
-                // one k-step per K tile: the next K tile's fragments move into
-                // the set the next iteration consumes
+            for (int ks = 1; ks < NKS; ++ks) {
 #pragma unroll
                 for (int i = 0; i < G::TI; ++i)
-                    fa[0][i] = fa[1][i];
+                    read_a(ks, stage, i);
 #pragma unroll
                 for (int j = 0; j < G::TJ; ++j)
-                    fb[0][j] = fb[1][j];
+                    read_b(ks, stage, j);
+            }
+            issue(std::integral_constant<int, LX + LY>(), std::integral_constant<int, G::LOADS>(),
+                  pn_next, pn_kt, pn_stage, pn_on);
+            mfmas(I0(), std::integral_constant<int, NM>());
+            {
+                constexpr int R = (G::TI - YA) * RPF + FRAG_READS * (NKS - 1);
+                constexpr int PER = (R + NM - 1) / NM;
+                constexpr int VPER = LA > 0 ? (LA + NM - 1) / NM : 0;
+#pragma unroll
+                for (int x = 0; x < NM; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (x * PER < R)
+                        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
+                    if (VPER > 0 && x * VPER < LA)
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, VPER, 0);
+                }
+            }
+            wait_lgkm0();
+            barrier();                             // free: stage `stage` read by every wave
+            __builtin_amdgcn_sched_barrier(0);
+            // phase X: the loads of K tile g+2 into the released stage begin
+            const int kl = kt + 2;
+            const bool lnext = kl >= nk;
+            const int lkt = lnext ? kl - nk : kl;
+            const bool lon = g + 2 < total;
+            issue(I0(), std::integral_constant<int, LX>(), lnext, lkt, stage, lon);
+            mfmas(std::integral_constant<int, NM>(), std::integral_constant<int, NM + XM>());
+            {
+                constexpr int PER = (LX + XM - 1) / XM;
+#pragma unroll
+                for (int x = 0; x < XM; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (x * PER < LX)
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, PER, 0);
+                }
+            }
+            wait_vmcnt<LX>();                      // this wave's loads of K tile g+1 landed
+            barrier();                             // ready: K tile g+1 in the other stage
+            __builtin_amdgcn_sched_barrier(0);
+            // phase Y: the rest of K tile g; K tile g+1's first fragments
+#pragma unroll
+            for (int i = 0; i < YA; ++i)
+                read_a(0, stage ^ 1, i);
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                read_b(0, stage ^ 1, j);
+            read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0);
+            issue(std::integral_constant<int, LX>(), std::integral_constant<int, LX + LY>(), lnext,
+                  lkt, stage, lon);
+            pn_next = lnext;
+            pn_kt = lkt;
+            pn_stage = stage;
+            pn_on = lon;
+            mfmas(std::integral_constant<int, NM + XM>(), std::integral_constant<int, NKS * NM>());
+            {
+                constexpr int R = (YA + G::TJ) * RPF + (Op::MX ? G::TI + G::TJ : 0);
+                constexpr int PER = (R + YM - 1) / YM;
+                constexpr int VPER = LY > 0 ? (LY + YM - 1) / YM : 0;
+#pragma unroll
+                for (int x = 0; x < YM; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (x * PER < R)
+                        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
+                    if (VPER > 0 && x * VPER < LY)
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, VPER, 0);
+                }
             }
             if constexpr (Op::MX) {
 #pragma unroll
@@ -802,7 +856,6 @@ void gemm_ring(GemmArgs p, int group_m)
                 for (int j = 0; j < G::TJ; ++j)
                     sc_b[j] = sn_b[j];
             }
-            stage = nstage;
         }
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
@@ -817,8 +870,8 @@ void gemm_ring(GemmArgs p, int group_m)
         sa_cur = sa_nxt;
         sb_cur = sb_nxt;
         bases(r + 2, a_nxt, b_nxt, sa_nxt, sb_nxt);
-        // the pending half belongs to the tile that is now current
-        pend_next = false;
+        // the pending loads belong to the tile that is now current
+        pn_next = false;
     }
     wait_vmcnt<0>();   // no direct load still writing LDS when the waves end
 }
@@ -849,7 +902,7 @@ void gemm_ring(GemmArgs p, int group_m)
 //   writeback -> compute: the accumulators are zeroed after the stores are
 //       issued, before the next compute role.
 // The ring: S = 4 stages of 32-wide bf16 (64-wide fp8) K tiles, 64-byte LDS
-// rows with the swz4 swizzle, as in gemm_ring.  Needs at least four K tiles.
+// rows with the swz4 swizzle.  Needs at least four K tiles.
 struct PP {
     static constexpr int BM = 256, BN = 256, S = 4;
     static constexpr int WM = 128, WN = 64;        // wave tile
@@ -1138,7 +1191,7 @@ hipError_t launch(const GemmArgs &p, hipStream_t s)
 }
 
 template <class Op, int BM, int BN, bool PERSIST>
-hipError_t launch_ring(const GemmArgs &p, hipStream_t s)
+hipError_t launch_early(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
@@ -1147,10 +1200,10 @@ hipError_t launch_ring(const GemmArgs &p, hipStream_t s)
     if (PERSIST)
         grid = ntiles < num_cus() ? ntiles : num_cus();
     if (whole_bf16(p, BM, BN))
-        hipLaunchKernelGGL((gemm_ring<Op, BM, BN, 4, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
                            s, p, group_m);
     else
-        hipLaunchKernelGGL((gemm_ring<Op, BM, BN, 4, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p,
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p,
                            group_m);
     return hipGetLastError();
 }
@@ -1180,25 +1233,30 @@ bool big_tiles(const GemmArgs &p)
 
 } // namespace
 
+// Ring shapes measured fastest at 8192^3 on MI355X: bf16 in 32-wide K tiles
+// (64-byte rows) with four stages and split loads; MX-fp8 in 128-wide K tiles
+// (128-byte rows, two k-steps per barrier) with two stages.  bf16 with
+// 64-wide tiles and two stages, or without split loads, measured within 2%;
+// MX with 64-wide tiles and four stages measured 20% slower.
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
     // 256x256 tiles when they give every CU work, 128x128 otherwise; the
-    // scheduled ring needs two K tiles
+    // early-release ring needs two K tiles
     const bool big = big_tiles(p);
-    const bool ring_ok = p.K > 3 * Bf16Ring::BK;
+    const bool ring_ok = p.K > Bf16Ring64::BK;
     switch (level) {
     case 4:
         return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
     case 5:
         if (big && ring_ok)
-            return launch_ring<Bf16Ring, 256, 256, false>(p, s);
+            return launch_early<Bf16Ring64, 256, 256, false>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
     case 6:
         if (big && ring_ok)
-            return launch_ring<Bf16Ring, 256, 256, true>(p, s);
+            return launch_early<Bf16Ring64, 256, 256, true>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
     case 7:
-        if (ring_ok)
+        if (p.K > 3 * Bf16Ring::BK)
             return launch_pingpong<Bf16Ring, true>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
     default:
@@ -1208,13 +1266,14 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 
 hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s)
 {
+    const bool ring_ok = p.K > Mxfp8Ring128::BK;   // two K tiles
     switch (level) {
     case 5:
-        return p.K > 3 * Mxfp8Ring::BK ? launch_ring<Mxfp8Ring, 256, 256, false>(p, s)
-                                 : launch<Mxfp8Op, 256, 256, 2, false>(p, s);
+        return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, false>(p, s)
+                       : launch<Mxfp8Op, 256, 256, 2, false>(p, s);
     case 6:
-        return p.K > 3 * Mxfp8Ring::BK ? launch_ring<Mxfp8Ring, 256, 256, true>(p, s)
-                                 : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
+        return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, true>(p, s)
+                       : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
     case 7:
         return p.K > 3 * Mxfp8Ring::BK ? launch_pingpong<Mxfp8Ring, true>(p, s)
                                        : launch<Mxfp8Op, 256, 256, 2, true>(p, s);

@@ -334,3 +334,56 @@ def test_config_shape_integer_checksums(cfg):
     ii, jj = sample_indices(p.M, p.N, 500, cfg)
     cref, _ = oracle_entries(p, ii, jj)
     assert np.array_equal(vals[ii, jj], cref)
+
+
+# ------------------------------------------- pipelined paths at large shapes
+
+# Large enough for the 256x256 pipelined kernels (at least one tile per
+# compute unit), with ragged M and N edges, a partial last K tile and, in
+# the persistent grid, two or three tiles per workgroup.
+LARGE_RAGGED = {BF16: (4100, 8200, 1000), E4M3FN: (4100, 8200, 1040)}
+
+
+@pytest.mark.parametrize("level", [5, 6, 7, None])
+@pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
+def test_large_ragged_integer_exact(level, fmt):
+    """Exact-integer inputs at a ragged large shape: row and column sums of C
+    equal A(B 1) and (1^T A) B exactly, and sampled entries match the oracle
+    bitwise."""
+    M, N, K = LARGE_RAGGED[fmt]
+    kw = {"ld_sa": 36, "ld_sb": 36} if fmt == E4M3FN else {}
+    p = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_F32, seed=7100 + (level or 0),
+                        name="large_ragged_int", **kw)
+    r = run_level(p, level)
+    assert r is not None, "the pipelined levels accept this problem"
+    vals = r[0]
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if fmt == E4M3FN:
+        from helpers import torch_decode_scales
+        A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+        B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    assert np.array_equal(vals.sum(axis=1), A @ B.sum(axis=1))
+    assert np.array_equal(vals.sum(axis=0), A.sum(axis=0) @ B)
+    ii, jj = sample_indices(M, N, 1000, 71)
+    cref, _ = oracle_entries(p, ii, jj)
+    assert np.array_equal(vals[ii, jj], cref)
+
+
+@pytest.mark.parametrize("level", [6, 7, None])
+@pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
+def test_large_ragged_alpha_beta_sampled(level, fmt):
+    """Random operands, alpha/beta update of a bf16 C at the ragged large
+    shape; sampled entries within the oracle's bound."""
+    M, N, K = LARGE_RAGGED[fmt]
+    kw = {"ld_sa": 36, "ld_sb": 36} if fmt == E4M3FN else {"dist": "normal", "std": 0.5}
+    p = make_problem(M, N, K, fmt=fmt, c_dtype=OUT_BF16, alpha=0.5, beta=-1.5,
+                     seed=7200 + (level or 0), name="large_ragged_ab", **kw)
+    r = run_level(p, level)
+    assert r is not None
+    vals = r[0]
+    ii, jj = sample_indices(M, N, 2000, 72)
+    cref, tsum = oracle_entries(p, ii, jj)
+    ok, worst, bad = oracle.check(vals[ii, jj], cref, tsum, True)
+    announce(f"large ragged {fmt} level {level}: worst err/tol {worst:.3g}")
+    assert ok, f"{bad} sampled entries out of bound (worst {worst})"
