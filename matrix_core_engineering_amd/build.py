@@ -48,7 +48,9 @@ def build(verbose=False):
             f.write("\n".join(l for l in log.splitlines() if "remark" in l))
             f.write("\n")
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol (e.g. a kernel whose host-side launch
+    # stub the compiler did not emit) fails the build instead of the load
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

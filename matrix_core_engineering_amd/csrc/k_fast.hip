@@ -514,33 +514,47 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // is released, so each wave reads the whole K tile's fragments into
 // registers during its first k-step and releases the stage early.  Two
 // barriers per K tile g (stage s = g % 2):
-//   phase A  k-step 0 on the matrix cores; fragments of k-steps 1.. read;
+//   phase A  the first KA k-steps on the matrix cores; the fragments of
+//            k-steps 1.. read;
 //   barrier 1 (free):  every wave's reads of stage s are in registers;
 //   phase X  the next k-steps; the loads of K tile g+2 into stage s begin;
 //   barrier 2 (ready): each wave waited for its loads of K tile g+1;
 //   phase Y  the last matrix-core instructions of K tile g; K tile g+1's
 //            first fragments (and MX scales) read; the remaining loads.
 // The loads of a K tile spread over phases X and Y of one iteration and have
-// until barrier 2 of the next to land.  Needs at least two K tiles.
-// Per format: XM matrix-core instructions in phase X; LX and LY of a K
-// tile's direct loads issued in phases X and Y, the rest in the next phase
-// A; YA of the next K tile's first A fragments read in phase Y, the rest in
-// the next phase A (the instruction order needs A fragment i only from the
-// (TJ*i)-th instruction on).
+// until barrier 2 of the next to land.  Needs at least two K tiles and K a
+// multiple of the K tile.
+// Per format: KA k-steps in phase A (the K tile's fragment reads spread
+// over them: four waves read LDS at about 108 B/clk per CU); XM matrix-core
+// instructions in phase X; LX and LY of a K tile's direct loads issued in
+// phases X and Y, the rest in the next phase A; YA of the next K tile's
+// first A fragments read in phase Y, the rest in the next phase A (the
+// instruction order needs A fragment i only from the (TJ*i)-th instruction
+// on).
 struct Bf16Ring64 {                   // 128-byte rows
     static constexpr bool MX = false;
     static constexpr int ELT = 2;
     static constexpr int BK = 64;
     static constexpr int NKS = 4;
-    static constexpr int XM = 32, LX = 11, LY = 5, YA = 4;
+    static constexpr int KA = 1, XM = 32, LX = 16, LY = 0, YA = 2;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
     static constexpr bool MX = true;
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
     static constexpr int NKS = 2;
-    static constexpr int XM = 7, LX = 6, LY = 6, YA = 1;
+    static constexpr int KA = 1, XM = 10, LX = 8, LY = 4, YA = 2;
 };
+
+// Whether a direct load follows the x-th of n matrix-core instructions when
+// l <= n loads are spread evenly over them (load j after instruction
+// floor(j*n/l)): four waves issuing a 1 KiB direct load per instruction
+// would outrun the address unit (about one such load per 21 clocks per CU)
+// and stall on a full queue with matrix-core work behind it.
+__host__ __device__ constexpr bool loads_after(int x, int n, int l)
+{
+    return l > 0 && ((x + 1) * l + n - 1) / n > (x * l + n - 1) / n;
+}
 
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -551,11 +565,13 @@ void gemm_early(GemmArgs p, int group_m)
     constexpr int NM = G::TI * G::TJ;                      // matrix-core instructions per k-step
     constexpr int RPF = Op::MX ? 2 : 1;                    // LDS reads per fragment
     constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
-    constexpr int XM = Op::XM, YM = (NKS - 1) * NM - XM;   // phases X and Y
+    constexpr int KA = Op::KA, AM = KA * NM;                // phase A
+    constexpr int XM = Op::XM, YM = (NKS - KA) * NM - XM;  // phases X and Y
     constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA;
     static_assert(G::CH == 8, "128-byte LDS rows");
     static_assert(XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
     static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
+    static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -571,96 +587,100 @@ void gemm_early(GemmArgs p, int group_m)
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
     const int total = my_tiles * nk;
 
-    const __amdgpu_buffer_rsrc_t rsrc_a =
-        make_rsrc(p.A, (uint32_t)(((size_t)(p.M - 1) * p.lda + p.K) * Op::ELT));
-    const __amdgpu_buffer_rsrc_t rsrc_b =
-        make_rsrc(p.B, (uint32_t)(((size_t)(p.N - 1) * p.ldb + p.K) * Op::ELT));
-    const int nblk = (p.K + 31) / 32;
-    __amdgpu_buffer_rsrc_t rsrc_sa = rsrc_a, rsrc_sb = rsrc_b;
-    if constexpr (Op::MX) {
-        // scale rows are 4-byte aligned: the last row's final word may pass
-        // ceil(K/32) but stays inside its aligned word
-        const int nblk4 = (nblk + 3) & ~3;
-        rsrc_sa = make_rsrc(p.SA, (uint32_t)((size_t)(p.M - 1) * p.ld_sa + nblk4));
-        rsrc_sb = make_rsrc(p.SB, (uint32_t)((size_t)(p.N - 1) * p.ld_sb + nblk4));
-    }
+    const int nblk = (p.K + 31) / 32;                      // MX scale blocks per row
 
     auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
 
-    // Direct-load geometry: load t of this wave fills 1 KiB = 8 rows of 128
-    // bytes; lane l writes row (wave*N + t)*8 + l/8 at physical chunk l%8;
-    // swz8(row) = (l/8) ^ (t&1) (bit 3 of the row is the parity of
-    // wave*N + t, N even), so a lane fetches one of two logical chunks.
+    // Direct-load addressing.  Each tile gets its own buffer resources (A
+    // and B rows of the tile, MX scale rows) whose record count ends at the
+    // tile's last valid row, so rows past M or N read as zeros; a lane's
+    // offset inside the tile (row and chunk) is fixed for the whole kernel,
+    // and K moves in the scalar offset.  No address arithmetic per load.
+    // Load t of this wave fills 1 KiB = 8 rows of 128 bytes: lane l writes
+    // row (wave*N + t)*8 + l/8 at physical chunk l%8; swz8(row) = (l/8) ^
+    // (t&1) (bit 3 of the row is the parity of wave*N + t, N even).
     const int lrow = lane >> 3;
     const int kc_even = ((lane & 7) ^ lrow) * G::EPC;
     const int kc_odd = ((lane & 7) ^ lrow ^ 1) * G::EPC;
-    uint32_t a_cur[G::NA], a_nxt[G::NA], b_cur[G::NB], b_nxt[G::NB];
-    uint32_t sa_cur = OOB_OFFSET, sa_nxt = OOB_OFFSET, sb_cur = OOB_OFFSET, sb_nxt = OOB_OFFSET;
-    auto bases = [&](int r, uint32_t (&ab)[G::NA], uint32_t (&bb)[G::NB], uint32_t &sab,
-                     uint32_t &sbb) {
-        int m0 = p.M, n0 = p.N;                            // past the end: all rows invalid
+    uint32_t va[G::NA], vb[G::NB];
+#pragma unroll
+    for (int t = 0; t < G::NA; ++t)
+        va[t] = (uint32_t)(((wave * G::NA + t) * G::RPL + lrow) * p.lda + ((t & 1) ? kc_odd : kc_even)) *
+                Op::ELT;
+#pragma unroll
+    for (int t = 0; t < G::NB; ++t)
+        vb[t] = (uint32_t)(((wave * G::NB + t) * G::RPL + lrow) * p.ldb + ((t & 1) ? kc_odd : kc_even)) *
+                Op::ELT;
+    const uint32_t vsa = (uint32_t)((wave * 64 + lane) * p.ld_sa);
+    const uint32_t vsb = (uint32_t)((wave * 64 + lane) * p.ld_sb);
+
+    // Base and record count of the r-th tile's resources (A rows, B rows,
+    // MX scale rows); past the last tile every record count is zero (loads
+    // fetch nothing and write zeros).
+    struct TileSpan {
+        const char *a, *b, *sa, *sb;
+        uint32_t na, nb, nsa, nsb;
+    };
+    auto tile_span = [&](int r) {
+        TileSpan t{(const char *)p.A, (const char *)p.B, (const char *)p.SA, (const char *)p.SB,
+                   0, 0, 0, 0};
         if (r < my_tiles) {
             int tm, tn;
             grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
-            m0 = tm * BM;
-            n0 = tn * BN;
+            const int m0 = tm * BM, n0 = tn * BN;
+            const int ra = p.M - m0 < BM ? p.M - m0 : BM, rb = p.N - n0 < BN ? p.N - n0 : BN;
+            t.a += (size_t)m0 * p.lda * Op::ELT;
+            t.b += (size_t)n0 * p.ldb * Op::ELT;
+            t.na = (uint32_t)(((size_t)(ra - 1) * p.lda + p.K) * Op::ELT);
+            t.nb = (uint32_t)(((size_t)(rb - 1) * p.ldb + p.K) * Op::ELT);
+            if constexpr (Op::MX) {
+                // scale rows are 4-byte aligned: the last row's final word
+                // may pass ceil(K/32) but stays inside its aligned word
+                const int nblk4 = (nblk + 3) & ~3;
+                t.sa += (size_t)m0 * p.ld_sa;
+                t.sb += (size_t)n0 * p.ld_sb;
+                t.nsa = (uint32_t)((ra - 1) * p.ld_sa + nblk4);
+                t.nsb = (uint32_t)((rb - 1) * p.ld_sb + nblk4);
+            }
         }
-#pragma unroll
-        for (int t = 0; t < G::NA; ++t) {
-            const int row = m0 + (wave * G::NA + t) * G::RPL + lrow;
-            const int kc = (t & 1) ? kc_odd : kc_even;
-            ab[t] = row < p.M ? (uint32_t)(row * p.lda + kc) * Op::ELT : OOB_OFFSET;
-        }
-#pragma unroll
-        for (int t = 0; t < G::NB; ++t) {
-            const int row = n0 + (wave * G::NB + t) * G::RPL + lrow;
-            const int kc = (t & 1) ? kc_odd : kc_even;
-            bb[t] = row < p.N ? (uint32_t)(row * p.ldb + kc) * Op::ELT : OOB_OFFSET;
-        }
-        if constexpr (Op::MX) {
-            const int ra = m0 + wave * 64 + lane, rb = n0 + wave * 64 + lane;
-            sab = ra < p.M ? (uint32_t)(ra * p.ld_sa) : OOB_OFFSET;
-            sbb = rb < p.N ? (uint32_t)(rb * p.ld_sb) : OOB_OFFSET;
-        }
+        return t;
     };
+    TileSpan cur = tile_span(0), nxt = tile_span(1);
 
     // Direct loads number u in [LO, HI) of K tile kt of the current (next)
     // tile into `stage`: u < NA the A rows, then the B rows, then (MX) the
-    // A and B scale words.  `on` false turns every lane out of range
-    // (nothing is fetched; zeros are still written to LDS).
-    auto issue = [&](auto lo_c, auto hi_c, bool next, int kt, int stage, bool on) {
-        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
-        const int k0 = kt * Op::BK;
-        const bool ok_even = on && k0 + kc_even < p.K, ok_odd = on && k0 + kc_odd < p.K;
-        const int soff = k0 * Op::ELT;
+    // A and B scale words.  Past the workgroup's last tile, `next` selects
+    // the zero-record resources.
+    // (the offsets go through locals: an element of a template-sized array
+    // captured by the lambda, passed straight to the builtin, makes the host
+    // pass drop the kernel's launch stub)
+    auto issue = [&](int lo, int hi, bool next, int kt, int stage) {
+        const int soff = kt * Op::BK * Op::ELT;
         char *base = smem + stage * G::STAGE_BYTES;
+        const TileSpan &t = next ? nxt : cur;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.a, t.na), rb = make_rsrc(t.b, t.nb);
+        char *sbase = base + G::A_BYTES + G::B_BYTES;
 #pragma unroll
-        for (int u = LO; u < HI; ++u) {
+        for (int u = lo; u < hi; ++u) {
             if (u < G::NA) {
-                const int t = u;
-                const bool ok = (t & 1) ? ok_odd : ok_even;
-                const uint32_t voff = ok ? (next ? a_nxt[t] : a_cur[t]) : OOB_OFFSET;
+                const uint32_t voff = va[u];
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_a, (lds_ptr_t)(base + (wave * G::NA + t) * 1024), 16, voff, soff, 0, 0);
+                    ra, (lds_ptr_t)(base + (wave * G::NA + u) * 1024), 16, voff, soff, 0, 0);
             } else if (u < G::NA + G::NB) {
-                const int t = u - G::NA;
-                const bool ok = (t & 1) ? ok_odd : ok_even;
-                const uint32_t voff = ok ? (next ? b_nxt[t] : b_cur[t]) : OOB_OFFSET;
+                const int v = u - G::NA;
+                const uint32_t voff = vb[v];
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_b, (lds_ptr_t)(base + G::A_BYTES + (wave * G::NB + t) * 1024), 16, voff,
-                    soff, 0, 0);
+                    rb, (lds_ptr_t)(base + G::A_BYTES + (wave * G::NB + v) * 1024), 16, voff, soff,
+                    0, 0);
             } else if (u == G::NA + G::NB) {
                 // the K tile's aligned scale word of each row (4 blocks)
-                const uint32_t va = on ? (next ? sa_nxt : sa_cur) : OOB_OFFSET;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_sa, (lds_ptr_t)(base + G::A_BYTES + G::B_BYTES + wave * 256), 4, va,
-                    kt * (Op::BK / 32), 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(t.sa, t.nsa),
+                                                         (lds_ptr_t)(sbase + wave * 256), 4, vsa,
+                                                         kt * (Op::BK / 32), 0, 0);
             } else {
-                const uint32_t vb = on ? (next ? sb_nxt : sb_cur) : OOB_OFFSET;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc_sb,
-                    (lds_ptr_t)(base + G::A_BYTES + G::B_BYTES + G::SA_BYTES + wave * 256), 4, vb,
-                    kt * (Op::BK / 32), 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(t.sb, t.nsb),
+                                                         (lds_ptr_t)(sbase + G::SA_BYTES + wave * 256),
+                                                         4, vsb, kt * (Op::BK / 32), 0, 0);
             }
         }
     };
@@ -717,10 +737,9 @@ void gemm_early(GemmArgs p, int group_m)
 
     floatx16 acc[G::TI][G::TJ];
     // matrix-core instructions q in [LO, HI) of the K tile, q = ks*NM + i*TJ + j
-    auto mfmas = [&](auto lo_c, auto hi_c) {
-        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+    auto mfmas = [&](int lo, int hi) {
 #pragma unroll
-        for (int q = LO; q < HI; ++q) {
+        for (int q = lo; q < hi; ++q) {
             const int ks = q / NM, i = (q % NM) / G::TJ, j = q % G::TJ;
             if constexpr (!Op::MX)
                 acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
@@ -731,15 +750,12 @@ void gemm_early(GemmArgs p, int group_m)
         }
     };
 
-    using I0 = std::integral_constant<int, 0>;
     // ---------------------------------------------------------- prologue
-    bases(0, a_cur, b_cur, sa_cur, sb_cur);
-    bases(1, a_nxt, b_nxt, sa_nxt, sb_nxt);
     // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
     // issues (a direct load always writes LDS, so no placeholder load may
     // target a stage in use)
-    issue(I0(), std::integral_constant<int, G::LOADS>(), false, 0, 0, true);
-    issue(I0(), std::integral_constant<int, LX + LY>(), false, 1, 1, true);
+    issue(0, G::LOADS, false, 0, 0);
+    issue(0, LX + LY, false, 1, 1);
     wait_vmcnt<LX + LY>();                         // K tile 0 landed
     barrier();
 #pragma unroll
@@ -758,7 +774,7 @@ void gemm_early(GemmArgs p, int group_m)
 
     int g = 0;
     // the last LA loads of the K tile whose loads began last iteration
-    bool pn_next = false, pn_on = true;
+    bool pn_next = false;
     int pn_kt = 1, pn_stage = 1;
     for (int r = 0; r < my_tiles; ++r) {
 #pragma unroll
@@ -768,8 +784,8 @@ void gemm_early(GemmArgs p, int group_m)
                 acc[i][j] = zero16();
         for (int kt = 0; kt < nk; ++kt, ++g) {
             const int stage = g & 1;
-            // phase A: k-step 0; the K tile's other fragments into registers;
-            // the last loads of K tile g+1
+            // phase A: the first KA k-steps; the K tile's other fragments into
+            // registers; the last loads of K tile g+1
 #pragma unroll
             for (int i = YA; i < G::TI; ++i)
                 read_a(0, stage, i);
@@ -782,41 +798,40 @@ void gemm_early(GemmArgs p, int group_m)
                 for (int j = 0; j < G::TJ; ++j)
                     read_b(ks, stage, j);
             }
-            issue(std::integral_constant<int, LX + LY>(), std::integral_constant<int, G::LOADS>(),
-                  pn_next, pn_kt, pn_stage, pn_on);
-            mfmas(I0(), std::integral_constant<int, NM>());
+            issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
+            mfmas(0, AM);
             {
                 constexpr int R = (G::TI - YA) * RPF + FRAG_READS * (NKS - 1);
-                constexpr int PER = (R + NM - 1) / NM;
-                constexpr int VPER = LA > 0 ? (LA + NM - 1) / NM : 0;
+                constexpr int PER = (R + AM - 1) / AM;
 #pragma unroll
-                for (int x = 0; x < NM; ++x) {
+                for (int x = 0; x < AM; ++x) {
                     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
                     if (x * PER < R)
                         __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
-                    if (VPER > 0 && x * VPER < LA)
-                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, VPER, 0);
+                    if (loads_after(x, AM, LA))
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
                 }
             }
+            // the waits and barriers are fences for the scheduler too: no
+            // matrix-core instruction may drift across them
+            __builtin_amdgcn_sched_barrier(0);
             wait_lgkm0();
             barrier();                             // free: stage `stage` read by every wave
             __builtin_amdgcn_sched_barrier(0);
             // phase X: the loads of K tile g+2 into the released stage begin
+            // (past the last K tile `lnext` holds: the zero-record resources)
             const int kl = kt + 2;
             const bool lnext = kl >= nk;
             const int lkt = lnext ? kl - nk : kl;
-            const bool lon = g + 2 < total;
-            issue(I0(), std::integral_constant<int, LX>(), lnext, lkt, stage, lon);
-            mfmas(std::integral_constant<int, NM>(), std::integral_constant<int, NM + XM>());
-            {
-                constexpr int PER = (LX + XM - 1) / XM;
+            issue(0, LX, lnext, lkt, stage);
+            mfmas(AM, AM + XM);
 #pragma unroll
-                for (int x = 0; x < XM; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    if (x * PER < LX)
-                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, PER, 0);
-                }
+            for (int x = 0; x < XM; ++x) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (loads_after(x, XM, LX))
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<LX>();                      // this wave's loads of K tile g+1 landed
             barrier();                             // ready: K tile g+1 in the other stage
             __builtin_amdgcn_sched_barrier(0);
@@ -828,24 +843,21 @@ void gemm_early(GemmArgs p, int group_m)
             for (int j = 0; j < G::TJ; ++j)
                 read_b(0, stage ^ 1, j);
             read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0);
-            issue(std::integral_constant<int, LX>(), std::integral_constant<int, LX + LY>(), lnext,
-                  lkt, stage, lon);
+            issue(LX, LX + LY, lnext, lkt, stage);
             pn_next = lnext;
             pn_kt = lkt;
             pn_stage = stage;
-            pn_on = lon;
-            mfmas(std::integral_constant<int, NM + XM>(), std::integral_constant<int, NKS * NM>());
+            mfmas(AM + XM, NKS * NM);
             {
                 constexpr int R = (YA + G::TJ) * RPF + (Op::MX ? G::TI + G::TJ : 0);
                 constexpr int PER = (R + YM - 1) / YM;
-                constexpr int VPER = LY > 0 ? (LY + YM - 1) / YM : 0;
 #pragma unroll
                 for (int x = 0; x < YM; ++x) {
                     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
                     if (x * PER < R)
                         __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
-                    if (VPER > 0 && x * VPER < LY)
-                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, VPER, 0);
+                    if (loads_after(x, YM, LY))
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
                 }
             }
             if constexpr (Op::MX) {
@@ -861,15 +873,8 @@ void gemm_early(GemmArgs p, int group_m)
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
         store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         // the load side moves one tile ahead
-#pragma unroll
-        for (int t = 0; t < G::NA; ++t)
-            a_cur[t] = a_nxt[t];
-#pragma unroll
-        for (int t = 0; t < G::NB; ++t)
-            b_cur[t] = b_nxt[t];
-        sa_cur = sa_nxt;
-        sb_cur = sb_nxt;
-        bases(r + 2, a_nxt, b_nxt, sa_nxt, sb_nxt);
+        cur = nxt;
+        nxt = tile_span(r + 2);
         // the pending loads belong to the tile that is now current
         pn_next = false;
     }
@@ -1241,9 +1246,9 @@ bool big_tiles(const GemmArgs &p)
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
     // 256x256 tiles when they give every CU work, 128x128 otherwise; the
-    // early-release ring needs two K tiles
+    // early-release ring needs two or more whole K tiles
     const bool big = big_tiles(p);
-    const bool ring_ok = p.K > Bf16Ring64::BK;
+    const bool ring_ok = p.K > Bf16Ring64::BK && p.K % Bf16Ring64::BK == 0;
     switch (level) {
     case 4:
         return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
@@ -1266,7 +1271,7 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 
 hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s)
 {
-    const bool ring_ok = p.K > Mxfp8Ring128::BK;   // two K tiles
+    const bool ring_ok = p.K > Mxfp8Ring128::BK && p.K % Mxfp8Ring128::BK == 0;   // whole K tiles
     switch (level) {
     case 5:
         return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, false>(p, s)
