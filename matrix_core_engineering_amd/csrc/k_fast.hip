@@ -120,10 +120,11 @@ struct Geometry {
 // tile); edge tiles mask per element.
 // Epilogue variants, chosen on the host per call: EPI_BF16_WHOLE when C is
 // bf16, beta == 0, M and N are whole tiles and C rows are 8-byte aligned
-// (one branch-free path); EPI_ANY otherwise.  Keeping the choice out of the
+// (one branch-free path); EPI_BF16_LDS (gemm_early) the same with 16-byte
+// aligned rows, staged through LDS for whole-line stores; EPI_ANY otherwise.  Keeping the choice out of the
 // kernel's run-time branches lets the compiler move accumulators to stores
 // one block at a time.
-enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1 };
+enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1, EPI_BF16_LDS = 2 };
 
 template <int EPI, class G, int BM, int BN>
 __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
@@ -211,6 +212,54 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G:
                 __builtin_amdgcn_sched_barrier(0);
             }
     }
+}
+
+// Whole bf16 tiles through LDS: each wave converts two 32x32 blocks at a
+// time (32 rows x 64 columns = 32 rows of 128 bytes) into its own LDS
+// buffer, then reads them back so that eight consecutive lanes hold one
+// row's 128 bytes, and stores 16 bytes per lane: every store instruction
+// writes eight whole 128-byte lines of C instead of 32 rows x 16 bytes.
+// The buffer's row pitch is 144 bytes, so the 64 lanes' 8-byte writes of a
+// block fill every bank exactly twice.  Stores count in vmcnt like loads;
+// the next ready wait drains them.
+constexpr int EPI_PITCH = 144;                           // bytes per staged row
+constexpr int EPI_WAVE_BYTES = 32 * EPI_PITCH;           // per wave
+
+template <class G, int BM, int BN>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
+                                               int m_tile, int n_tile, int wm, int wn, int lane,
+                                               char *buf)
+{
+    static_assert(G::TJ % 2 == 0, "blocks staged in pairs");
+    const int h = lane >> 5, l32 = lane & 31;
+    const int rrow = lane >> 3, rchunk = lane & 7;       // read-back position
+#pragma unroll
+    for (int i = 0; i < G::TI; ++i)
+#pragma unroll
+        for (int jp = 0; jp < G::TJ / 2; ++jp) {
+            // lane (l32, h) holds row l32, columns 8q + 4h .. +3 of each block
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx16 &a = acc[i][2 * jp + jj];
+                    *(u16x4 *)(buf + l32 * EPI_PITCH + jj * 64 + q * 16 + h * 8) =
+                        u16x4{f32_to_bf16_rne(p.alpha * a[4 * q]), f32_to_bf16_rne(p.alpha * a[4 * q + 1]),
+                              f32_to_bf16_rne(p.alpha * a[4 * q + 2]), f32_to_bf16_rne(p.alpha * a[4 * q + 3])};
+                }
+            wait_lgkm0();
+            uint16_t *c0 = (uint16_t *)p.C + (size_t)(m_tile + wm * G::WM + i * 32) * p.ldc + n_tile +
+                           wn * G::WN + jp * 64 + rchunk * 8;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = s * 8 + rrow;
+                const intx4 v = *(const intx4 *)(buf + row * EPI_PITCH + rchunk * 16);
+                *(intx4 *)(c0 + (size_t)row * p.ldc) = v;
+            }
+            // the next pair's writes may not overtake these reads
+            wait_lgkm0();
+            __builtin_amdgcn_sched_barrier(0);
+        }
 }
 
 template <class Op, int BM, int BN, int STAGES, bool PERSIST, int EPI>
@@ -572,7 +621,7 @@ void gemm_early(GemmArgs p, int group_m)
     static_assert(XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
     static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
     static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
-    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + (EPI == EPI_BF16_LDS ? 4 * EPI_WAVE_BYTES : 0)];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -871,7 +920,11 @@ void gemm_early(GemmArgs p, int group_m)
         }
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
-        store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+        if constexpr (EPI == EPI_BF16_LDS)
+            store_tile_lds<G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, lane,
+                                      smem + G::LDS_BYTES + wave * EPI_WAVE_BYTES);
+        else
+            store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         // the load side moves one tile ahead
         cur = nxt;
         nxt = tile_span(r + 2);
@@ -1204,7 +1257,10 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
     int grid = ntiles;
     if (PERSIST)
         grid = ntiles < num_cus() ? ntiles : num_cus();
-    if (whole_bf16(p, BM, BN))
+    if (whole_bf16(p, BM, BN) && p.ldc % 8 == 0 && (uintptr_t)p.C % 16 == 0)
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
+                           s, p, group_m);
+    else if (whole_bf16(p, BM, BN))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
                            s, p, group_m);
     else

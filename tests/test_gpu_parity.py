@@ -391,3 +391,29 @@ def test_large_ragged_alpha_beta_sampled(level, fmt, kind):
     ok, worst, bad = oracle.check(vals[ii, jj], cref, tsum, True)
     announce(f"large ragged {fmt} level {level}: worst err/tol {worst:.3g}")
     assert ok, f"{bad} sampled entries out of bound (worst {worst})"
+
+
+@pytest.mark.parametrize("level", [5, 6, None])
+@pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
+def test_whole_tiles_bf16_output_bitwise(level, fmt):
+    """Whole 256x256 tiles, K a multiple of every K tile, bf16 output with
+    beta = 0 (the path whose results are staged through LDS before the
+    store): exact-integer inputs make every fp32 sum exact, so the bf16
+    result is the correctly rounded exact product, checked for the whole
+    matrix against a float64 product (exact for these integers)."""
+    M, N, K = 4096, 4096, 1024
+    p = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_BF16, seed=7300 + (level or 0),
+                        name="whole_tiles_bf16_out")
+    r = run_level(p, level)
+    assert r is not None
+    raw = r[1]
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if fmt == E4M3FN:
+        from helpers import torch_decode_scales
+        A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+        B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    from helpers import f64_to_bf16_bits
+    expect = f64_to_bf16_bits(A @ B)
+    bad = np.argwhere(raw != expect)
+    assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
