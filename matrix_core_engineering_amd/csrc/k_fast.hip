@@ -215,7 +215,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G:
 }
 
 // Whole bf16 tiles through LDS: each wave converts two 32x32 blocks at a
-// time (32 rows x 64 columns = 32 rows of 128 bytes) into its own LDS
+// time (32 rows x 64 columns = 32 rows of 128 bytes; RR = 16: half of the
+// rows per round, for kernels with less LDS to spare) into its own LDS
 // buffer, then reads them back so that eight consecutive lanes hold one
 // row's 128 bytes, and stores 16 bytes per lane: every store instruction
 // writes eight whole 128-byte lines of C instead of 32 rows x 16 bytes.
@@ -223,40 +224,46 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G:
 // block fill every bank exactly twice.  Stores count in vmcnt like loads;
 // the next ready wait drains them.
 constexpr int EPI_PITCH = 144;                           // bytes per staged row
-constexpr int EPI_WAVE_BYTES = 32 * EPI_PITCH;           // per wave
+template <int RR> constexpr int epi_wave_bytes() { return RR * EPI_PITCH; }
 
-template <class G, int BM, int BN>
+template <class G, int BM, int BN, int RR>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
                                                int m_tile, int n_tile, int wm, int wn, int lane,
                                                char *buf)
 {
     static_assert(G::TJ % 2 == 0, "blocks staged in pairs");
+    static_assert(RR == 16 || RR == 32, "rows per round");
     const int h = lane >> 5, l32 = lane & 31;
     const int rrow = lane >> 3, rchunk = lane & 7;       // read-back position
 #pragma unroll
     for (int i = 0; i < G::TI; ++i)
 #pragma unroll
-        for (int jp = 0; jp < G::TJ / 2; ++jp) {
+        for (int jp = 0; jp < G::TJ / 2; ++jp)
+#pragma unroll
+            for (int half = 0; half < 32 / RR; ++half) {
             // lane (l32, h) holds row l32, columns 8q + 4h .. +3 of each block
+            if (RR == 32 || (l32 >> 4) == half) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const floatx16 &a = acc[i][2 * jp + jj];
-                    *(u16x4 *)(buf + l32 * EPI_PITCH + jj * 64 + q * 16 + h * 8) =
-                        u16x4{f32_to_bf16_rne(p.alpha * a[4 * q]), f32_to_bf16_rne(p.alpha * a[4 * q + 1]),
-                              f32_to_bf16_rne(p.alpha * a[4 * q + 2]), f32_to_bf16_rne(p.alpha * a[4 * q + 3])};
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const floatx16 &a = acc[i][2 * jp + jj];
+                        *(u16x4 *)(buf + (l32 % RR) * EPI_PITCH + jj * 64 + q * 16 + h * 8) =
+                            u16x4{f32_to_bf16_rne(p.alpha * a[4 * q]), f32_to_bf16_rne(p.alpha * a[4 * q + 1]),
+                                  f32_to_bf16_rne(p.alpha * a[4 * q + 2]),
+                                  f32_to_bf16_rne(p.alpha * a[4 * q + 3])};
+                    }
+            }
             wait_lgkm0();
-            uint16_t *c0 = (uint16_t *)p.C + (size_t)(m_tile + wm * G::WM + i * 32) * p.ldc + n_tile +
-                           wn * G::WN + jp * 64 + rchunk * 8;
+            uint16_t *c0 = (uint16_t *)p.C + (size_t)(m_tile + wm * G::WM + i * 32 + half * RR) * p.ldc +
+                           n_tile + wn * G::WN + jp * 64 + rchunk * 8;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < RR / 8; ++s) {
                 const int row = s * 8 + rrow;
                 const intx4 v = *(const intx4 *)(buf + row * EPI_PITCH + rchunk * 16);
                 *(intx4 *)(c0 + (size_t)row * p.ldc) = v;
             }
-            // the next pair's writes may not overtake these reads
+            // the next round's writes may not overtake these reads
             wait_lgkm0();
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -498,13 +505,13 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 
 // 64-byte LDS rows (the role-specialised kernel)
 struct Bf16Ring {                     // 64-byte rows
-    static constexpr bool MX = false;
+    static constexpr bool MX = false, SG = false;
     static constexpr int ELT = 2;
     static constexpr int BK = 32;     // K elements per K tile
     static constexpr int NKS = 2;     // 32x32x16 k-steps per K tile
 };
 struct Mxfp8Ring {                    // 64-byte rows
-    static constexpr bool MX = true;
+    static constexpr bool MX = true, SG = false;
     static constexpr int ELT = 1;
     static constexpr int BK = 64;
     static constexpr int NKS = 1;     // one 32x32x64 k-step per K tile
@@ -522,14 +529,14 @@ struct RingGeometry {
     // one aligned 4-byte scale word per row (the four blocks containing the K
     // tile's blocks); a direct load of any size fills one 4-byte LDS slot per
     // lane
-    static constexpr int SA_BYTES = Op::MX ? BM * 4 : 0;
-    static constexpr int SB_BYTES = Op::MX ? BN * 4 : 0;
+    static constexpr int SA_BYTES = Op::MX && !Op::SG ? BM * 4 : 0;
+    static constexpr int SB_BYTES = Op::MX && !Op::SG ? BN * 4 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
     static constexpr int LDS_BYTES = S * STAGE_BYTES;
     static constexpr int NA = BM / RPL / 4;                // direct loads per wave per K tile
     static constexpr int NB = BN / RPL / 4;
-    static constexpr int NSA = Op::MX ? 1 : 0;             // 4-byte scale loads: 64 rows each
-    static constexpr int NSB = Op::MX ? 1 : 0;
+    static constexpr int NSA = Op::MX && !Op::SG ? 1 : 0;  // 4-byte scale loads: 64 rows each
+    static constexpr int NSB = Op::MX && !Op::SG ? 1 : 0;
     static constexpr int LOADS = NA + NB + NSA + NSB;
     static_assert((ROWB == 64 && CH == 4 && RPL == 16) || (ROWB == 128 && CH == 8 && RPL == 8),
                   "64- or 128-byte LDS rows");
@@ -581,18 +588,27 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // instruction order needs A fragment i only from the (TJ*i)-th instruction
 // on).
 struct Bf16Ring64 {                   // 128-byte rows
-    static constexpr bool MX = false;
+    static constexpr bool MX = false, SG = false;
     static constexpr int ELT = 2;
     static constexpr int BK = 64;
     static constexpr int NKS = 4;
     static constexpr int KA = 1, XM = 32, LX = 16, LY = 0, YA = 2;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
-    static constexpr bool MX = true;
+    static constexpr bool MX = true, SG = false;
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
     static constexpr int NKS = 2;
-    static constexpr int KA = 1, XM = 10, LX = 8, LY = 4, YA = 2;
+    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2;
+};
+// MX with K a multiple of 512 (whole groups of 16 scale blocks): the scale
+// words of four K tiles travel together, 16 bytes per row, in a separate
+// double-buffered area (see gemm_early).  A 4-byte load per row and K tile
+// touches as many cache lines as a 16-byte one, and 64 rows' worth per
+// instruction doubled the K tile's line requests.
+struct Mxfp8Ring128G : Mxfp8Ring128 {
+    static constexpr bool SG = true;
+    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2;
 };
 
 // Whether a direct load follows the x-th of n matrix-core instructions when
@@ -621,7 +637,14 @@ void gemm_early(GemmArgs p, int group_m)
     static_assert(XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
     static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
     static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
-    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + (EPI == EPI_BF16_LDS ? 4 * EPI_WAVE_BYTES : 0)];
+    // LDS: the two stages, then (scale groups) two buffers of 16 bytes per
+    // A and B row and a 1 KiB sink for the loads of iterations that load no
+    // group, then (staged epilogue) one buffer per wave
+    constexpr int SG_BYTES = Op::SG ? 2 * (BM + BN) * 16 + 1024 : 0;
+    constexpr int EPI_RR = Op::SG ? 16 : 32;
+    constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? 4 * epi_wave_bytes<EPI_RR>() : 0;
+    static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + SG_BYTES + EPI_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -700,9 +723,10 @@ void gemm_early(GemmArgs p, int group_m)
     // tile into `stage`: u < NA the A rows, then the B rows, then (MX) the
     // A and B scale words.  Past the workgroup's last tile, `next` selects
     // the zero-record resources.
-    // (the offsets go through locals: an element of a template-sized array
-    // captured by the lambda, passed straight to the builtin, makes the host
-    // pass drop the kernel's launch stub)
+    // (resources and offsets go through named locals: a resource-building
+    // call or an element of a template-sized array captured by the lambda,
+    // passed straight to the builtin, makes the host pass drop the kernel's
+    // launch stub without a diagnostic)
     auto issue = [&](int lo, int hi, bool next, int kt, int stage) {
         const int soff = kt * Op::BK * Op::ELT;
         char *base = smem + stage * G::STAGE_BYTES;
@@ -723,13 +747,15 @@ void gemm_early(GemmArgs p, int group_m)
                     0, 0);
             } else if (u == G::NA + G::NB) {
                 // the K tile's aligned scale word of each row (4 blocks)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(t.sa, t.nsa),
-                                                         (lds_ptr_t)(sbase + wave * 256), 4, vsa,
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sa, t.nsa);
+                const uint32_t voff = vsa;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sbase + wave * 256), 4, voff,
                                                          kt * (Op::BK / 32), 0, 0);
             } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(t.sb, t.nsb),
-                                                         (lds_ptr_t)(sbase + G::SA_BYTES + wave * 256),
-                                                         4, vsb, kt * (Op::BK / 32), 0, 0);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sb, t.nsb);
+                const uint32_t voff = vsb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sbase + G::SA_BYTES + wave * 256),
+                                                         4, voff, kt * (Op::BK / 32), 0, 0);
             }
         }
     };
@@ -763,9 +789,22 @@ void gemm_early(GemmArgs p, int group_m)
     // MX: each lane's scale word of K tile kt (blocks 4kt .. 4kt+3 of its
     // row), blocks at or past ceil(K/32) forced to 127 (x1: they hold zero
     // data), shifted one byte down for the upper half-wave, which supplies
-    // the odd block of each instruction; op_sel then picks byte 2*ks.
-    auto read_scales = [&](int stage, int kt) {
-        if constexpr (Op::MX) {
+    // the odd block of each instruction; op_sel then picks byte 2*ks.  With
+    // scale groups the word is word (gk % 4) of the row's 16 bytes in group
+    // buffer (gk / 4) % 2, gk counting K tiles over the workgroup's tiles,
+    // and every block is valid (K is a multiple of 512).
+    auto read_scales = [&](int stage, int kt, int gk) {
+        if constexpr (Op::MX && Op::SG) {
+            const uint32_t *SAs =
+                (const uint32_t *)(smem + G::LDS_BYTES + ((gk >> 2) & 1) * (BM + BN) * 16) + (gk & 3);
+            const uint32_t *SBs = SAs + BM * 4;
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i)
+                sn_a[i] = (int)(SAs[(wm * G::WM + i * 32 + l32) * 4] >> (8 * h));
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                sn_b[j] = (int)(SBs[(wn * G::WN + j * 32 + l32) * 4] >> (8 * h));
+        } else if constexpr (Op::MX) {
             const uint32_t *SAs =
                 (const uint32_t *)(smem + stage * G::STAGE_BYTES + G::A_BYTES + G::B_BYTES);
             const uint32_t *SBs = SAs + BM;
@@ -781,6 +820,28 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
             for (int j = 0; j < G::TJ; ++j)
                 sn_b[j] = (int)(((SBs[wn * G::WN + j * 32 + l32] & keep) | force) >> (8 * h));
+        }
+    };
+
+    // Scale groups: the 16 bytes (four K tiles) of each A and B row of the
+    // group starting at K tile kt of the current (next) tile, into group
+    // buffer buf; one load per wave and operand, lane l = row wave*64 + l.
+    // With `real` false the loads have no records (nothing is fetched) and
+    // write their zeros into the sink: issuing them every iteration keeps
+    // the loop free of branches, which would let the compiler sink the
+    // matrix-core instructions past the barriers.
+    auto issue_group = [&](bool next, int kt, int buf, bool real) {
+        if constexpr (Op::SG) {
+            const TileSpan &t = next ? nxt : cur;
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.sa, real ? t.nsa : 0u);
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.sb, real ? t.nsb : 0u);
+            char *gb = smem + G::LDS_BYTES + buf * (BM + BN) * 16;
+            char *sink = smem + G::LDS_BYTES + 2 * (BM + BN) * 16;   // shared by every wave
+            char *da = real ? gb + wave * 1024 : sink, *db = real ? gb + BM * 16 + wave * 1024 : sink;
+            const int soff = kt * (Op::BK / 32);
+            const uint32_t voa = vsa, vob = vsb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)da, 16, voa, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)db, 16, vob, soff, 0, 0);
         }
     };
 
@@ -803,9 +864,10 @@ void gemm_early(GemmArgs p, int group_m)
     // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
     // issues (a direct load always writes LDS, so no placeholder load may
     // target a stage in use)
+    issue_group(false, 0, 0, true);                // scale group 0 (four K tiles)
     issue(0, G::LOADS, false, 0, 0);
     issue(0, LX + LY, false, 1, 1);
-    wait_vmcnt<LX + LY>();                         // K tile 0 landed
+    wait_vmcnt<LX + LY>();                         // K tile 0 (and scale group 0) landed
     barrier();
 #pragma unroll
     for (int i = 0; i < YA; ++i)
@@ -813,7 +875,7 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
     for (int j = 0; j < G::TJ; ++j)
         read_b(0, 0, j);
-    read_scales(0, 0);
+    read_scales(0, 0, 0);
 #pragma unroll
     for (int i = 0; i < G::TI; ++i)
         sc_a[i] = sn_a[i];
@@ -891,7 +953,7 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
             for (int j = 0; j < G::TJ; ++j)
                 read_b(0, stage ^ 1, j);
-            read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0);
+            read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1);
             issue(LX, LX + LY, lnext, lkt, stage);
             pn_next = lnext;
             pn_kt = lkt;
@@ -909,6 +971,15 @@ void gemm_early(GemmArgs p, int group_m)
                         __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
                 }
             }
+            if constexpr (Op::SG) {
+                // at a group's first K tile: the next group's scale words into
+                // the other group buffer, whose last reads (two groups back)
+                // ended before this iteration's barrier 1; they land long
+                // before their first reader, phase Y of iteration g+3 (other
+                // iterations issue the same loads into the sink)
+                const bool gnext = kt + 4 >= nk;
+                issue_group(gnext, gnext ? 0 : kt + 4, ((g >> 2) + 1) & 1, (g & 3) == 0);
+            }
             if constexpr (Op::MX) {
 #pragma unroll
                 for (int i = 0; i < G::TI; ++i)
@@ -921,8 +992,9 @@ void gemm_early(GemmArgs p, int group_m)
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
         if constexpr (EPI == EPI_BF16_LDS)
-            store_tile_lds<G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, lane,
-                                      smem + G::LDS_BYTES + wave * EPI_WAVE_BYTES);
+            store_tile_lds<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane,
+                                              smem + G::LDS_BYTES + SG_BYTES +
+                                                  wave * epi_wave_bytes<EPI_RR>());
         else
             store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         // the load side moves one tile ahead
@@ -1328,11 +1400,18 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s)
 {
     const bool ring_ok = p.K > Mxfp8Ring128::BK && p.K % Mxfp8Ring128::BK == 0;   // whole K tiles
+    // whole groups of 16 scale blocks, 16-byte aligned scale rows
+    const bool groups = p.K % 512 == 0 && p.ld_sa % 16 == 0 && p.ld_sb % 16 == 0 &&
+                        (uintptr_t)p.SA % 16 == 0 && (uintptr_t)p.SB % 16 == 0;
     switch (level) {
     case 5:
+        if (ring_ok && groups)
+            return launch_early<Mxfp8Ring128G, 256, 256, false>(p, s);
         return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, false>(p, s)
                        : launch<Mxfp8Op, 256, 256, 2, false>(p, s);
     case 6:
+        if (ring_ok && groups)
+            return launch_early<Mxfp8Ring128G, 256, 256, true>(p, s);
         return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, true>(p, s)
                        : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
     case 7:

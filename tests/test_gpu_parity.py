@@ -342,19 +342,23 @@ def test_config_shape_integer_checksums(cfg):
 # compute unit), with ragged M and N edges and, in the persistent grid, two
 # or three tiles per workgroup; K either a multiple of every K tile (the
 # early-release kernel) or with a partial last K tile (the other kernels).
+# "kgroups": K a multiple of 512 with scale rows padded to 16 bytes (MX
+# scale words of four K tiles travel together), three groups per tile.
 LARGE_RAGGED = {BF16: (4100, 8200, 1000), E4M3FN: (4100, 8200, 1040)}
-LARGE_RAGGED_K = {"ktail": LARGE_RAGGED, "kwhole": {BF16: (4100, 8200, 1024), E4M3FN: (4100, 8200, 1024)}}
+LARGE_RAGGED_K = {"ktail": LARGE_RAGGED, "kwhole": {BF16: (4100, 8200, 1024), E4M3FN: (4100, 8200, 1024)},
+                  "kgroups": {BF16: (4100, 8200, 1536), E4M3FN: (4100, 8200, 1536)}}
+SCALE_LD = {"ktail": 36, "kwhole": 36, "kgroups": 48}
 
 
 @pytest.mark.parametrize("level", [5, 6, 7, None])
 @pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
-@pytest.mark.parametrize("kind", ["ktail", "kwhole"])
+@pytest.mark.parametrize("kind", ["ktail", "kwhole", "kgroups"])
 def test_large_ragged_integer_exact(level, fmt, kind):
     """Exact-integer inputs at a ragged large shape: row and column sums of C
     equal A(B 1) and (1^T A) B exactly, and sampled entries match the oracle
     bitwise."""
     M, N, K = LARGE_RAGGED_K[kind][fmt]
-    kw = {"ld_sa": 36, "ld_sb": 36} if fmt == E4M3FN else {}
+    kw = {"ld_sa": SCALE_LD[kind], "ld_sb": SCALE_LD[kind]} if fmt == E4M3FN else {}
     p = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_F32, seed=7100 + (level or 0),
                         name="large_ragged_int", **kw)
     r = run_level(p, level)
@@ -375,12 +379,13 @@ def test_large_ragged_integer_exact(level, fmt, kind):
 
 @pytest.mark.parametrize("level", [6, 7, None])
 @pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
-@pytest.mark.parametrize("kind", ["ktail", "kwhole"])
+@pytest.mark.parametrize("kind", ["ktail", "kwhole", "kgroups"])
 def test_large_ragged_alpha_beta_sampled(level, fmt, kind):
     """Random operands, alpha/beta update of a bf16 C at the ragged large
     shape; sampled entries within the oracle's bound."""
     M, N, K = LARGE_RAGGED_K[kind][fmt]
-    kw = {"ld_sa": 36, "ld_sb": 36} if fmt == E4M3FN else {"dist": "normal", "std": 0.5}
+    kw = ({"ld_sa": SCALE_LD[kind], "ld_sb": SCALE_LD[kind]} if fmt == E4M3FN
+          else {"dist": "normal", "std": 0.5})
     p = make_problem(M, N, K, fmt=fmt, c_dtype=OUT_BF16, alpha=0.5, beta=-1.5,
                      seed=7200 + (level or 0), name="large_ragged_ab", **kw)
     r = run_level(p, level)
