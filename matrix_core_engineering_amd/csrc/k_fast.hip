@@ -1326,6 +1326,10 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
     const int group_m = tiles_m < 8 ? tiles_m : 8;
+    // with no more tiles than CUs a persistent grid is the one-tile grid:
+    // run the simpler kernel
+    if (PERSIST && ntiles <= num_cus())
+        return launch_early<Op, BM, BN, false>(p, s);
     int grid = ntiles;
     if (PERSIST)
         grid = ntiles < num_cus() ? ntiles : num_cus();
