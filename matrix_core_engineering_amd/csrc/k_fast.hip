@@ -611,16 +611,6 @@ struct Mxfp8Ring128G : Mxfp8Ring128 {
     static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2;
 };
 
-// Whether a direct load follows the x-th of n matrix-core instructions when
-// l <= n loads are spread evenly over them (load j after instruction
-// floor(j*n/l)): four waves issuing a 1 KiB direct load per instruction
-// would outrun the address unit (about one such load per 21 clocks per CU)
-// and stall on a full queue with matrix-core work behind it.
-__host__ __device__ constexpr bool loads_after(int x, int n, int l)
-{
-    return l > 0 && ((x + 1) * l + n - 1) / n > (x * l + n - 1) / n;
-}
-
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_early(GemmArgs p, int group_m)

@@ -71,4 +71,14 @@ MCE_HD int swz4(int row)
     return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
+// Whether a direct load follows the x-th of n matrix-core instructions when
+// l <= n loads are spread evenly over them (load j after instruction
+// floor(j*n/l)): four waves issuing a 1 KiB direct load per instruction
+// would outrun the address unit (about one such load per 21 clocks per CU)
+// and stall on a full queue with matrix-core work behind it.
+MCE_HD constexpr bool loads_after(int x, int n, int l)
+{
+    return l > 0 && ((x + 1) * l + n - 1) / n > (x * l + n - 1) / n;
+}
+
 } // namespace mce
