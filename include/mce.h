@@ -114,10 +114,14 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  *   level 6  + persistent grid with a tile-order scheduler (step 7)
  *   level 7  + role-specialised waves (step 8)
  *
- * Levels 4-7 need both operands K-contiguous (A row-major, B column-major),
- * 16-byte aligned base pointers, lda and ldb multiples of 8 and K a multiple
- * of 8; otherwise they return MCE_EUNSUPPORTED.  gemm_mxfp8_level accepts
- * levels 3 and 5-7 (same meaning; its level 3 also takes any K).
+ * bf16 levels 4 and 7 need both operands K-contiguous (A row-major, B
+ * column-major), 16-byte aligned base pointers, lda and ldb multiples of 8
+ * and K a multiple of 8; otherwise they return MCE_EUNSUPPORTED.  bf16
+ * levels 5 and 6 take every problem: those that levels 4 and 7 cannot take
+ * run a kernel that stages the operands through registers (any layout,
+ * alignment and K).  gemm_mxfp8_level accepts levels 3 and 5-7, 5-7 with the
+ * K-contiguity and alignment rules above and scale rows padded to 4 bytes
+ * (same meaning; its level 3 also takes any K).
  */
 int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, int a_col_major,

@@ -97,11 +97,8 @@ constexpr int kBestMxLevel = 6;
 
 int pick_level(const Call &c)
 {
-    if (c.fmt == FMT_BF16) {
-        if (kBestBf16Level >= 4 && fast_eligible(c))
-            return kBestBf16Level;
-        return 3;
-    }
+    if (c.fmt == FMT_BF16)   // levels 5-6 take any bf16 problem
+        return kBestBf16Level;
     if (kBestMxLevel >= 5 && fast_eligible(c) && mx_scales_eligible(c))
         return kBestMxLevel;
     return 3;
@@ -114,8 +111,8 @@ bool level_accepts(const Call &c, int level)
         switch (level) {
         case 1: return c.M <= 128 && c.N <= 128 && c.K <= 64;
         case 2: return c.M <= 128 && c.N <= 128;
-        case 3: return true;
-        case 4: case 5: case 6: case 7: return fast_eligible(c);
+        case 3: case 5: case 6: return true;
+        case 4: case 7: return fast_eligible(c);
         default: return false;
         }
     }
@@ -243,8 +240,9 @@ int run(const Call &in)
     } else {
         int level = in.level != 0 ? in.level : pick_level(c);
         if (c.fmt == FMT_BF16)
-            err = level <= 3 ? mce::launch_simple_bf16(level, p, c.stream)
-                             : mce::launch_fast_bf16(level, p, c.stream);
+            err = level <= 3                              ? mce::launch_simple_bf16(level, p, c.stream)
+                  : fast_eligible(c) || level == 4 || level == 7 ? mce::launch_fast_bf16(level, p, c.stream)
+                                                         : mce::launch_general_bf16(level, p, c.stream);
         else
             err = level <= 3 ? mce::launch_simple_mxfp8(p, c.stream)
                              : mce::launch_fast_mxfp8(level, p, c.stream);

@@ -39,6 +39,7 @@
 // ("B200 TMA Pipeline Designer", section E steps 4-7: per-stage ready/free
 // protocol, initial phases, prologue / steady state / drain.)
 #include "common.hpp"
+#include "epilogue.hpp"
 #include "launch.hpp"
 #include "sched.hpp"
 
@@ -48,7 +49,6 @@ namespace mce {
 namespace {
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
 // [15:14], expcnt[6:4] = 7, lgkmcnt[11:8] = 15: no wait on those).
@@ -112,107 +112,6 @@ struct Geometry {
     static_assert(NA % 2 == 0 && NB % 2 == 0, "swizzle parity argument needs even load counts");
     static_assert(!Op::MX || (NSA == 1 && NSB == 1), "MX scale staging assumes 256-row tiles");
 };
-
-// Epilogue of one workgroup tile: out = alpha*acc + beta*C0, written straight
-// from the accumulators (C^T layout: lane l owns row l % 32 and four groups
-// of four consecutive columns per 32x32 block).  Interior tiles with
-// vector-aligned C take the branch-free vector path (one uniform test per
-// tile); edge tiles mask per element.
-// Epilogue variants, chosen on the host per call: EPI_BF16_WHOLE when C is
-// bf16, beta == 0, M and N are whole tiles and C rows are 8-byte aligned
-// (one branch-free path); EPI_BF16_LDS (gemm_early) the same with 16-byte
-// aligned rows, staged through LDS for whole-line stores; EPI_ANY otherwise.  Keeping the choice out of the
-// kernel's run-time branches lets the compiler move accumulators to stores
-// one block at a time.
-enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1, EPI_BF16_LDS = 2 };
-
-template <int EPI, class G, int BM, int BN>
-__device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
-                                           int m_tile, int n_tile, int wm, int wn, int h, int l32)
-{
-    const int mbase = m_tile + wm * G::WM + l32;
-    const int nbase = n_tile + wn * G::WN + 4 * h;
-    const bool vec_c = (p.ldc % 4) == 0 &&
-                       ((uintptr_t)p.C % (p.c_dtype == OUT_F32 ? 16 : 8)) == 0;
-    const bool full = vec_c && m_tile + BM <= p.M && n_tile + BN <= p.N;
-    if (EPI == EPI_BF16_WHOLE || (full && p.c_dtype == OUT_BF16 && p.beta == 0.0f)) {
-        // the common case: one row pointer per 32-row block, columns as
-        // immediate offsets, no C read
-#pragma unroll
-        for (int i = 0; i < G::TI; ++i) {
-            uint16_t *row = (uint16_t *)p.C + (size_t)(mbase + i * 32) * p.ldc + nbase;
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const floatx16 &a = acc[i][j];
-                    *(u16x4 *)(row + j * 32 + q * 8) =
-                        u16x4{f32_to_bf16_rne(p.alpha * a[4 * q]), f32_to_bf16_rne(p.alpha * a[4 * q + 1]),
-                              f32_to_bf16_rne(p.alpha * a[4 * q + 2]), f32_to_bf16_rne(p.alpha * a[4 * q + 3])};
-                }
-                // one 32x32 block at a time: keeps the scheduler from pulling
-                // every accumulator into VGPRs at once
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    } else if (EPI == EPI_BF16_WHOLE) {
-        // unreachable: the host only picks this variant for whole bf16 tiles
-    } else if (full && p.c_dtype == OUT_F32) {
-#pragma unroll
-        for (int i = 0; i < G::TI; ++i) {
-            float *row = (float *)p.C + (size_t)(mbase + i * 32) * p.ldc + nbase;
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const floatx16 &a = acc[i][j];
-                    floatx4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                    v *= p.alpha;
-                    floatx4 *dst = (floatx4 *)(row + j * 32 + q * 8);
-                    if (p.beta != 0.0f)
-                        v += p.beta * *dst;
-                    *dst = v;
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    } else if (full) {
-        // bf16 output with beta != 0
-#pragma unroll
-        for (int i = 0; i < G::TI; ++i) {
-            uint16_t *row = (uint16_t *)p.C + (size_t)(mbase + i * 32) * p.ldc + nbase;
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const floatx16 &a = acc[i][j];
-                    u16x4 *dst = (u16x4 *)(row + j * 32 + q * 8);
-                    const u16x4 c0 = *dst;
-                    u16x4 o;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c0[e]), p.alpha * a[4 * q + e]));
-                    *dst = o;
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < G::TI; ++i)
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = mbase + i * 32;
-                    const int n = nbase + j * 32 + (r >> 2) * 8 + (r & 3);
-                    if (m < p.M && n < p.N)
-                        store_c(p, m, n, acc[i][j][r]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-    }
-}
 
 // Whole bf16 tiles through LDS: each wave converts two 32x32 blocks at a
 // time (32 rows x 64 columns = 32 rows of 128 bytes; RR = 16: half of the

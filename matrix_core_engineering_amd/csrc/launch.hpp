@@ -19,5 +19,8 @@ hipError_t launch_scale_c(const GemmArgs &p, hipStream_t s);
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s);
 // Levels 5-6 (MX fp8).
 hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s);
+// Levels 5-6 (bf16) for operands the direct-load kernels cannot take: any
+// layout, alignment and K, through registers.
+hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);
 
 } // namespace mce

@@ -71,6 +71,16 @@ MCE_HD int swz4(int row)
     return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
+// XOR swizzle for the 64-byte LDS rows of the register-staged kernel, whose
+// MN-major operands are written transposed: rows 8c + e (c = 0..15) of one
+// K column map to four different chunks (row bit 3 enters), while the
+// 16-lane fragment reads over consecutive rows at one logical chunk still
+// hit 16 different 16-byte bank slots.
+MCE_HD int swz4g(int row)
+{
+    return ((row >> 3) ^ (row >> 1)) & 3;
+}
+
 // Whether a direct load follows the x-th of n matrix-core instructions when
 // l <= n loads are spread evenly over them (load j after instruction
 // floor(j*n/l)): four waves issuing a 1 KiB direct load per instruction

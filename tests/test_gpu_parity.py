@@ -44,7 +44,7 @@ def level_should_accept(level, p):
         return M <= 128 and N <= 128 and p.K <= 64
     if level == 2:
         return M <= 128 and N <= 128
-    if level == 3:
+    if level in (3, 5, 6):
         return True
     a_kc = (p.b_col_major if p.c_col_major else not p.a_col_major)
     b_kc = (not p.a_col_major if p.c_col_major else p.b_col_major)

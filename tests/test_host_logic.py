@@ -26,6 +26,7 @@ void h_grouped_tile(int id, int tm_, int tn_, int g, int *tm, int *tn)
 int h_persistent_tile_id(int wg, int nwg, int r) { return mce::persistent_tile_id(wg, nwg, r); }
 int h_swz8(int r) { return mce::swz8(r); }
 int h_swz4(int r) { return mce::swz4(r); }
+int h_swz4g(int r) { return mce::swz4g(r); }
 int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 0; }
 }
 '''
@@ -117,10 +118,32 @@ def test_swz4_fragment_reads_conflict_free(lib, base):
             assert counts.max() == 1, (chunk, p, s)
 
 
+@pytest.mark.parametrize("base", [0, 32, 64, 96])
+def test_swz4g_fragment_reads_conflict_free(lib, base):
+    """Register-staged kernel, 64-byte rows: same 16-lane read pattern."""
+    for chunk in range(4):
+        for p in range(2):
+            rows = list(range(base + 16 * p, base + 16 * p + 16))
+            counts = np.bincount(slots(rows, chunk, lib.h_swz4g, 64), minlength=16)
+            assert counts.max() == 1, (chunk, p)
+
+
 def test_swizzles_are_permutations_per_row(lib):
     for r in range(512):
         assert sorted(c ^ lib.h_swz8(r) for c in range(8)) == list(range(8))
         assert sorted(c ^ lib.h_swz4(r) for c in range(4)) == list(range(4))
+        assert sorted(c ^ lib.h_swz4g(r) for c in range(4)) == list(range(4))
+
+
+@pytest.mark.parametrize("e", range(8))
+@pytest.mark.parametrize("kchunk", range(4))
+def test_swz4g_spreads_transposed_write_rows(lib, e, kchunk):
+    """MN-major operands are written transposed: the 16 lanes that share a
+    K pair write rows 8c + e, c = 0..15, at one logical chunk; swz4g puts
+    them in four different physical chunks (swz4 in only two)."""
+    phys = {kchunk ^ lib.h_swz4g(8 * c + e) for c in range(16)}
+    assert len(phys) == 4
+    assert len({kchunk ^ lib.h_swz4(8 * c + e) for c in range(16)}) == 2
 
 
 def test_epilogue_staging_pitch_spreads_banks():
