@@ -126,3 +126,105 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G:
 }
 
 } // namespace mce
+
+namespace mce {
+
+// Epilogue staged through LDS for any C (fp32 or bf16, any beta, leading
+// dimension or edge): each wave converts 32 rows of its tile at a time
+// (alpha * acc, fp32) into its own buffer, reads them back so that
+// consecutive lanes hold consecutive 16-byte pieces of a row, and then reads
+// C (beta != 0), combines and stores by those pieces.  A store instruction
+// then covers 256 contiguous bytes of each of four rows (fp32) instead of
+// 32 bytes of each of 32 rows.  The buffer pitch is 272 bytes: 16 lanes'
+// 16-byte writes of consecutive rows hit 16 different bank slots.  The
+// caller's LDS must be free (no other wave may still read it) and is free
+// again when every wave has returned.
+constexpr int EPI_F32_PITCH = 272;
+constexpr int EPI_F32_WAVE_BYTES = 32 * EPI_F32_PITCH;
+
+// out = v + beta * C0 for one element whose alpha * acc is v
+__device__ __forceinline__ void store_c_scaled(const GemmArgs &p, int row, int col, float v)
+{
+    const size_t idx = (size_t)row * p.ldc + col;
+    if (p.c_dtype == OUT_F32) {
+        float *c = (float *)p.C;
+        if (p.beta != 0.0f)
+            v = __builtin_fmaf(p.beta, c[idx], v);
+        c[idx] = v;
+    } else {
+        uint16_t *c = (uint16_t *)p.C;
+        if (p.beta != 0.0f)
+            v = __builtin_fmaf(p.beta, bf16_to_f32(c[idx]), v);
+        c[idx] = f32_to_bf16_rne(v);
+    }
+}
+
+template <class G>
+__device__ __forceinline__ void store_tile_staged(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
+                                                  int m_tile, int n_tile, int wm, int wn, int lane,
+                                                  char *buf)
+{
+    static_assert(G::WN == 64, "rows of 64 fp32 = 256 bytes");
+    const int h = lane >> 5, l32 = lane & 31;
+    const int rrow = lane >> 4, rpiece = lane & 15;      // read-back position
+    const int n0 = n_tile + wn * G::WN + rpiece * 4;
+#pragma unroll
+    for (int i = 0; i < G::TI; ++i) {
+        // lane (l32, h) holds row l32, columns 32j + 8q + 4h .. +3
+#pragma unroll
+        for (int j = 0; j < G::TJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const floatx16 &a = acc[i][j];
+                floatx4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                v *= p.alpha;
+                *(floatx4 *)(buf + l32 * EPI_F32_PITCH + (j * 32 + q * 8 + h * 4) * 4) = v;
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): this wave's writes landed
+        const int m0 = m_tile + wm * G::WM + i * 32;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int row = s * 4 + rrow;
+            const int m = m0 + row;
+            floatx4 v = *(const floatx4 *)(buf + row * EPI_F32_PITCH + rpiece * 16);
+            if (m < p.M && n0 + 4 <= p.N) {
+                if (p.c_dtype == OUT_F32) {
+                    float *dst = (float *)p.C + (size_t)m * p.ldc + n0;
+                    if (p.beta != 0.0f) {
+                        floatx4 c0;
+                        __builtin_memcpy(&c0, dst, 16);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = __builtin_fmaf(p.beta, c0[e], v[e]);
+                    }
+                    __builtin_memcpy(dst, &v, 16);
+                } else {
+                    uint16_t *dst = (uint16_t *)p.C + (size_t)m * p.ldc + n0;
+                    u16x4 o;
+                    if (p.beta != 0.0f) {
+                        u16x4 c0;
+                        __builtin_memcpy(&c0, dst, 8);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            o[e] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c0[e]), v[e]));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            o[e] = f32_to_bf16_rne(v[e]);
+                    }
+                    __builtin_memcpy(dst, &o, 8);
+                }
+            } else if (m < p.M) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n0 + e < p.N)
+                        store_c_scaled(p, m, n0 + e, v[e]);
+            }
+        }
+        // the next round's writes may not overtake these reads
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+} // namespace mce

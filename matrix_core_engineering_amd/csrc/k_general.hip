@@ -35,6 +35,8 @@ constexpr int GBM = 128, GBN = 128, GBK = 32;
 constexpr int GROWB = GBK * 2;                 // 64-byte LDS rows: 4 chunks of 8 K
 constexpr int GOP_BYTES = GBM * GROWB;         // one operand tile, 8 KiB
 constexpr int GSTAGE = 2 * GOP_BYTES;          // A + B
+// the ring's two stages, reused by the four waves' epilogue buffers
+constexpr int GSMEM = 2 * GSTAGE > 4 * EPI_F32_WAVE_BYTES ? 2 * GSTAGE : 4 * EPI_F32_WAVE_BYTES;
 
 // Wave tile 64 x 64 of a 2 x 2 wave grid (the epilogue's view).
 struct GenGeom {
@@ -97,9 +99,9 @@ struct Stager {
 };
 
 template <bool A_KC, bool B_KC, bool PERSIST>
-__global__ __launch_bounds__(256) void gemm_general(GemmArgs p, int group_m)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gemm_general(GemmArgs p, int group_m)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * GSTAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[GSMEM];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,7 +167,11 @@ __global__ __launch_bounds__(256) void gemm_general(GemmArgs p, int group_m)
             }
             __syncthreads();   // stage kt+1 written by every wave; stage kt read by every wave
         }
-        store_tile<EPI_ANY, GenGeom, GBM, GBN>(p, acc, m0, n0, wm, wn, h, l32);
+        // the last barrier released both stages: the epilogue stages C
+        // through them, 256 contiguous bytes of a row per 16 lanes
+        store_tile_staged<GenGeom>(p, acc, m0, n0, wm, wn, lane, smem + wave * EPI_F32_WAVE_BYTES);
+        if (PERSIST)
+            __syncthreads();   // every wave's buffer read before the next prologue writes
     }
 }
 
@@ -177,8 +183,8 @@ hipError_t launch_g(const GemmArgs &p, hipStream_t s)
     const int group_m = tiles_m < 8 ? tiles_m : 8;
     int grid = ntiles;
     if (PERSIST) {
-        // three workgroups fit a CU (32 KiB of LDS, at most 168 registers per
-        // lane): the persistent grid keeps all of them busy
+        // three workgroups fit a CU (34 KiB of LDS, the kernel is held to 168
+        // registers per lane): the persistent grid keeps all of them busy
         int dev = 0, ncu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
@@ -208,7 +214,18 @@ hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
     switch (level) {
     case 5: return launch_g_layout<false>(p, s);
-    case 6: return launch_g_layout<true>(p, s);
+    case 6: {
+        // while the tiles fit the three workgroups per CU at once, the
+        // persistent grid is the one-tile grid (whose kernel needs fewer
+        // registers and so keeps three workgroups per CU)
+        const long ntiles = (long)((p.M + GBM - 1) / GBM) * ((p.N + GBN - 1) / GBN);
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            ntiles <= 3L * ncu)
+            return launch_g_layout<false>(p, s);
+        return launch_g_layout<true>(p, s);
+    }
     default: return hipErrorInvalidValue;
     }
 }
