@@ -38,7 +38,8 @@ METRIC = "GEMM TFLOP/s and % of dense MFMA peak (bf16, MX-fp8) at 8192³ on 1 MI
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_8192.txt")
 KERNEL_SOURCES = ["matrix_core_engineering_amd/csrc/k_fast.hip",
                   "matrix_core_engineering_amd/csrc/common.hpp",
-                  "matrix_core_engineering_amd/csrc/sched.hpp"]
+                  "matrix_core_engineering_amd/csrc/sched.hpp",
+                  "matrix_core_engineering_amd/csrc/epilogue.hpp"]
 
 
 def kernel_source_hash():
