@@ -131,14 +131,16 @@ namespace mce {
 
 // Epilogue staged through LDS for any C (fp32 or bf16, any beta, leading
 // dimension or edge): each wave converts 32 rows of its tile at a time
-// (alpha * acc, fp32) into its own buffer, reads them back so that
-// consecutive lanes hold consecutive 16-byte pieces of a row, and then reads
-// C (beta != 0), combines and stores by those pieces.  A store instruction
-// then covers 256 contiguous bytes of each of four rows (fp32) instead of
-// 32 bytes of each of 32 rows.  The buffer pitch is 272 bytes: 16 lanes'
-// 16-byte writes of consecutive rows hit 16 different bank slots.  The
-// caller's LDS must be free (no other wave may still read it) and is free
-// again when every wave has returned.
+// (alpha * acc, fp32) into its own buffer, reads them back so that each
+// lane holds a 16-byte piece of a row, and then reads C (beta != 0),
+// combines and stores by those pieces.  A store instruction then covers 256
+// contiguous bytes of each of four rows (fp32) instead of 32 bytes of each
+// of 32 rows.  LDS cycles (measured on gfx950): a 16-byte write serves 8
+// lanes, and the 272-byte pitch puts 8 consecutive rows in 8 different
+// 16-byte slots of a 128-byte window; a 16-byte read serves the 16 lanes of
+// quad group parity((lane >> 2) & 7) of a 32-lane half, so each such group
+// reads one whole row.  The caller's LDS must be free (no other wave may
+// still read it) and is free again when every wave has returned.
 constexpr int EPI_F32_PITCH = 272;
 constexpr int EPI_F32_WAVE_BYTES = 32 * EPI_F32_PITCH;
 
@@ -166,7 +168,10 @@ __device__ __forceinline__ void store_tile_staged(const GemmArgs &p, floatx16 (&
 {
     static_assert(G::WN == 64, "rows of 64 fp32 = 256 bytes");
     const int h = lane >> 5, l32 = lane & 31;
-    const int rrow = lane >> 4, rpiece = lane & 15;      // read-back position
+    // read-back position: the 16 lanes of one read cycle share a row
+    const int qh = (lane >> 2) & 7;
+    const int rrow = 2 * (lane >> 5) + (__builtin_popcount(qh) & 1);
+    const int rpiece = 4 * (qh >> 1) + (lane & 3);
     const int n0 = n_tile + wn * G::WN + rpiece * 4;
 #pragma unroll
     for (int i = 0; i < G::TI; ++i) {

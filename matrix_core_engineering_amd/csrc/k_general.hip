@@ -3,23 +3,24 @@
 // take: either operand MN-major (A column-major or B row-major), rows that
 // are not 16-byte aligned, or K not a whole number of 16-byte chunks.
 //
-// The operands travel through registers: each lane loads two 16-byte
-// chunks of a 128 x 32 operand tile per K tile (gfx950 global loads accept
-// any alignment, so a 2-byte-aligned row costs no extra instructions; only
-// chunks that cross the M, N or K edge fall back to masked element loads),
-// then writes them to LDS in the K-major, XOR-swizzled 64-byte rows that
-// the matrix-core fragment reads expect.  A K-contiguous chunk is eight
+// The operands travel through registers: each lane loads 16-byte chunks of
+// a 128-row operand tile per K tile (gfx950 global loads accept any
+// alignment, so a 2-byte-aligned row costs no extra instructions), then
+// writes them to LDS in the K-major, XOR-swizzled rows that the
+// matrix-core fragment reads expect.  A K-contiguous chunk is eight
 // consecutive K of one row (one 16-byte LDS write); for an MN-major operand
-// a lane loads the same eight rows at two adjacent K and writes them
-// transposed as eight 4-byte (k, k+1) pairs ("B200 TMA Pipeline Designer",
-// section B: the layout the reader expects is produced by the writer).
+// a lane loads the same eight rows at adjacent K and writes them transposed
+// as 4-byte (k, k+1) pairs ("B200 TMA Pipeline Designer", section B: the
+// layout the reader expects is produced by the writer).
 //
-// Ring: two LDS stages; the loads of K tile kt+1 are in registers while
-// tile kt is consumed, written to the other stage after the matrix-core
-// work, and one barrier per K tile hands both stages over.  (A second
-// register set, loading two K tiles ahead, measured slower: the registers
-// cost a workgroup per CU.)  Level 6 walks
-// the tiles of a persistent grid in the XCD-aware grouped order.
+// Ring: two LDS stages of 64-byte rows (K tile 32).  K tile kt+1 is loaded
+// into registers before K tile kt's matrix-core work and written to the
+// other stage after it; one barrier per K tile hands both stages over.  (A
+// second register set, loading two K tiles ahead, measured no faster and
+// pushes the persistent kernel into spills.)  The LDS (34 KiB: the
+// epilogue's four wave buffers reuse the ring) and the 168-register cap let
+// three workgroups share a CU.  Level 6 walks the tiles of a persistent grid
+// in the XCD-aware grouped order.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -28,38 +29,92 @@
 namespace mce {
 namespace {
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int GBM = 128, GBN = 128, GBK = 32;
-constexpr int GROWB = GBK * 2;                 // 64-byte LDS rows: 4 chunks of 8 K
-constexpr int GOP_BYTES = GBM * GROWB;         // one operand tile, 8 KiB
-constexpr int GSTAGE = 2 * GOP_BYTES;          // A + B
-// the ring's two stages, reused by the four waves' epilogue buffers
-constexpr int GSMEM = 2 * GSTAGE > 4 * EPI_F32_WAVE_BYTES ? 2 * GSTAGE : 4 * EPI_F32_WAVE_BYTES;
+constexpr int GBM = 128, GBN = 128;
+
+template <int BK>
+struct GenTile {
+    static_assert(BK == 32, "K tile: 64-byte rows, a K pair per lane for MN-major operands");
+    static constexpr int ROWB = BK * 2;                  // bytes per LDS row
+    static constexpr int CPR = BK / 8;                   // 16-byte chunks per row
+    static constexpr int CH = BK / 16;                   // chunks per lane and operand
+    static constexpr int OP_BYTES = GBM * ROWB;          // one operand tile
+    static constexpr int STAGE_BYTES = 2 * OP_BYTES;     // A + B
+    static constexpr int RING = 2 * STAGE_BYTES;
+    static constexpr int SMEM = RING > 4 * EPI_F32_WAVE_BYTES ? RING : 4 * EPI_F32_WAVE_BYTES;
+    static __device__ __forceinline__ int swz(int row) { return swz4q(row); }
+};
 
 // Wave tile 64 x 64 of a 2 x 2 wave grid (the epilogue's view).
 struct GenGeom {
     static constexpr int WM = 64, WN = 64, TI = 2, TJ = 2;
 };
 
-// One 128-row x 32-K operand tile through two 16-byte chunks per lane.
+// One 128-row x BK operand tile through CH 16-byte chunks per lane.
 // KC: element (r, k) at base[r * ld + k] (K-contiguous); otherwise at
 // base[k * ld + r] (MN-major).  rows: the operand's extent (M or N).
-template <bool KC>
+// KC chunk j of lane tid: row idx / CPR, K (idx % CPR) * 8 with
+// idx = j * 256 + tid.  MN chunk j: rows 8 mn_c(tid) .. +7 at K
+// mn_k(tid) + j: eight consecutive lanes read 128 contiguous bytes of one K
+// row, and the 32 lanes that write LDS in one cycle (measured: 32 lanes per
+// cycle for 4-byte writes) cover four K pairs, so the transposed writes
+// meet at most two to a bank.
+template <bool KC, int BK>
 struct Stager {
-    u16x8 v[2];
+    using T = GenTile<BK>;
+    typedef u16x8 Regs[T::CH];             // one K tile's chunks of this lane
+    const uint16_t *ptr[KC ? T::CH : 1];   // this tile's chunk addresses at K = 0
+    int roff;                              // MN-major: first LDS row of this lane's chunks
 
-    __device__ __forceinline__ void load(const uint16_t *base, int ld, int rows, int K, int r0,
-                                         int k0, int tid)
+    static __device__ __forceinline__ int mn_c(int tid) { return (tid & 7) | ((tid >> 7) << 3); }
+    static __device__ __forceinline__ int mn_k(int tid) { return 2 * ((tid >> 3) & 15); }
+
+    // Per tile.  Rows past the edge are never read: a KC row there is
+    // clamped to the last row (its products only reach C rows or columns
+    // that are never stored), and an MN-major chunk that would cross the
+    // edge starts at rows - 8 instead and fills those eight LDS rows (with
+    // the values another lane may also write there); LDS rows past the edge
+    // then keep stale values, which also reach only C entries that are
+    // never stored.  The MN-major clamp needs eight valid rows in the tile.
+    __device__ __forceinline__ void prep(const uint16_t *base, int ld, int rows, int r0, int tid)
+    {
+        if (KC) {
+#pragma unroll
+            for (int j = 0; j < T::CH; ++j) {
+                const int idx = j * 256 + tid;
+                ptr[KC ? j : 0] = base + (size_t)min(r0 + idx / T::CPR, rows - 1) * ld + (idx % T::CPR) * 8;
+            }
+            roff = 0;
+        } else {
+            // clamp only while the tile holds eight valid rows, so that the
+            // chunk's LDS rows stay inside the tile
+            const int r = rows - r0 >= 8 ? min(r0 + mn_c(tid) * 8, rows - 8) : r0 + mn_c(tid) * 8;
+            ptr[0] = base + (size_t)mn_k(tid) * ld + r;
+            roff = r - r0;
+        }
+    }
+
+    // a whole K tile: no masks
+    __device__ __forceinline__ void load_fast(Regs &v, int ld, int k0) const
     {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < T::CH; ++j) {
+            const uint16_t *src = KC ? ptr[KC ? j : 0] + k0 : ptr[0] + (size_t)(k0 + j) * ld;
+            __builtin_memcpy(&v[j], src, 16);
+        }
+    }
+
+    // any K tile (after prep): chunks that cross the M, N or K edge are
+    // loaded per element, into the LDS rows the store expects
+    __device__ __forceinline__ void load(Regs &v, const uint16_t *base, int ld, int rows, int K,
+                                         int r0, int k0, int tid) const
+    {
+#pragma unroll
+        for (int j = 0; j < T::CH; ++j) {
             const int idx = j * 256 + tid;
-            // KC: chunk = 8 K of one row; MN: chunk j = 8 rows at K 2*(tid/16)
-            // + j (the 16 lanes of a K read 256 contiguous bytes)
-            const int r = KC ? r0 + idx / 4 : r0 + (tid % 16) * 8;
-            const int k = KC ? k0 + (idx % 4) * 8 : k0 + 2 * (tid / 16) + j;
+            const int r = KC ? r0 + idx / T::CPR : r0 + roff;
+            const int k = KC ? k0 + (idx % T::CPR) * 8 : k0 + mn_k(tid) + j;
             const bool whole = KC ? (r < rows && k + 8 <= K) : (k < K && r + 8 <= rows);
             if (whole) {
                 const uint16_t *src = KC ? base + (size_t)r * ld + k : base + (size_t)k * ld + r;
@@ -77,50 +132,85 @@ struct Stager {
         }
     }
 
-    __device__ __forceinline__ void store(char *lds, int tid) const
+    __device__ __forceinline__ void store(const Regs &v, char *lds, int tid) const
     {
         if (KC) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < T::CH; ++j) {
                 const int idx = j * 256 + tid;
-                const int row = idx / 4, c = idx % 4;
-                *(u16x8 *)(lds + row * GROWB + ((c ^ swz4g(row)) * 16)) = v[j];
+                const int row = idx / T::CPR, c = idx % T::CPR;
+                *(u16x8 *)(lds + row * T::ROWB + ((c ^ T::swz(row)) * 16)) = v[j];
             }
         } else {
-            const int kk = 2 * (tid / 16), c = tid % 16;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = c * 8 + e;
-                const uint32_t pair = (uint32_t)v[0][e] | ((uint32_t)v[1][e] << 16);
-                *(uint32_t *)(lds + row * GROWB + (((kk >> 3) ^ swz4g(row)) * 16) + (kk & 7) * 2) = pair;
+            for (int jp = 0; jp < T::CH / 2; ++jp) {
+                const int kk = mn_k(tid) + 2 * jp;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int row = roff + e;
+                    const uint32_t pair = (uint32_t)v[2 * jp][e] | ((uint32_t)v[2 * jp + 1][e] << 16);
+                    *(uint32_t *)(lds + row * T::ROWB + (((kk >> 3) ^ T::swz(row)) * 16) + (kk & 7) * 2) =
+                        pair;
+                }
             }
         }
     }
 };
 
-template <bool A_KC, bool B_KC, bool PERSIST>
+template <bool A_KC, bool B_KC, bool PERSIST, int BK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void gemm_general(GemmArgs p, int group_m)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[GSMEM];
+    using T = GenTile<BK>;
+    __shared__ __attribute__((aligned(1024))) char smem[T::SMEM];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
-    // rows a lane reads differ by multiples of 32: the swizzle is lane-constant
-    const int swz_lane = swz4g(l32);
+    // each fragment row's swizzle (rows wm*64 + i*32 + l32, wn*64 + j*32 + l32)
+    int swz_a[2], swz_b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        swz_a[i] = T::swz(wm * 64 + i * 32 + l32);
+        swz_b[i] = T::swz(wn * 64 + i * 32 + l32);
+    }
 
     const int tiles_m = (p.M + GBM - 1) / GBM, tiles_n = (p.N + GBN - 1) / GBN;
     const int ntiles = tiles_m * tiles_n;
-    const int nk = (p.K + GBK - 1) / GBK;
+    const int nk = (p.K + BK - 1) / BK;
+    const int nf = p.K / BK;   // K tiles wholly inside K
     const int nwg = gridDim.x, wg = blockIdx.x;
     const int first = xcd_major(wg, nwg);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
     const uint16_t *A = (const uint16_t *)p.A, *B = (const uint16_t *)p.B;
 
-    Stager<A_KC> sa;
-    Stager<B_KC> sb;
+    Stager<A_KC, BK> sa;
+    Stager<B_KC, BK> sb;
+    typename Stager<A_KC, BK>::Regs va;
+    typename Stager<B_KC, BK>::Regs vb;
     floatx16 acc[2][2];
+
+    auto compute = [&](int stage) {
+        const char *As = smem + stage * T::STAGE_BYTES, *Bs = As + T::OP_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fa[i] = *(const bf16x8 *)(As + (wm * 64 + i * 32 + l32) * T::ROWB +
+                                          ((2 * ks + h) ^ swz_a[i]) * 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                fb[j] = *(const bf16x8 *)(Bs + (wn * 64 + j * 32 + l32) * T::ROWB +
+                                          ((2 * ks + h) ^ swz_b[j]) * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
+        }
+    };
+
     for (int r = 0; r < my_tiles; ++r) {
         int tm, tn;
         grouped_tile(PERSIST ? persistent_tile_id(wg, nwg, r) : first, tiles_m, tiles_n, group_m, tm,
@@ -131,51 +221,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = zero16();
-        // prologue: K tile 0 into stage 0
-        sa.load(A, p.lda, p.M, p.K, m0, 0, tid);
-        sb.load(B, p.ldb, p.N, p.K, n0, 0, tid);
-        sa.store(smem, tid);
-        sb.store(smem + GOP_BYTES, tid);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
+        sa.prep(A, p.lda, p.M, m0, tid);
+        sb.prep(B, p.ldb, p.N, n0, tid);
+        // The masked loads run only for the K tile with a tail (or for an
+        // MN-major operand whose tile holds fewer than eight valid rows),
+        // behind a uniform branch; every other K tile takes the steady loops
+        // below, whose whole-chunk loads have no branch between them, so each
+        // wait before an LDS write counts exactly the loads it must.
+        const bool a_in = A_KC || p.M - m0 >= 8, b_in = B_KC || p.N - n0 >= 8;
+        const bool steady = a_in && b_in;
+        auto load = [&](int kt) {
+            const int k0 = kt * BK;
+            if (k0 + BK <= p.K && a_in)
+                sa.load_fast(va, p.lda, k0);
+            else
+                sa.load(va, A, p.lda, p.M, p.K, m0, k0, tid);
+            if (k0 + BK <= p.K && b_in)
+                sb.load_fast(vb, p.ldb, k0);
+            else
+                sb.load(vb, B, p.ldb, p.N, p.K, n0, k0, tid);
+        };
+        auto load_fast = [&](int kt) {
+            sa.load_fast(va, p.lda, kt * BK);
+            sb.load_fast(vb, p.ldb, kt * BK);
+        };
+        auto store = [&](int stage) {
+            sa.store(va, smem + stage * T::STAGE_BYTES, tid);
+            sb.store(vb, smem + stage * T::STAGE_BYTES + T::OP_BYTES, tid);
+        };
+
+        // K tile kt+1 travels in registers under K tile kt's work and is
+        // written to the other stage, which the last barrier released
+        int kt = 0;
+        if (steady && nf >= 2) {
+            load_fast(0);
+            store(0);
+            __syncthreads();
+            for (; kt + 1 < nf; ++kt) {
+                load_fast(kt + 1);
+                compute(kt & 1);
+                store((kt + 1) & 1);
+                __syncthreads();
+            }
+        } else {
+            load(0);
+            store(0);
+            __syncthreads();
+        }
+        for (; kt < nk; ++kt) {
             const bool more = kt + 1 < nk;
-            if (more) {   // K tile kt+1 travels in registers under this tile's work
-                sa.load(A, p.lda, p.M, p.K, m0, (kt + 1) * GBK, tid);
-                sb.load(B, p.ldb, p.N, p.K, n0, (kt + 1) * GBK, tid);
-            }
-            const char *As = smem + (kt & 1) * GSTAGE, *Bs = As + GOP_BYTES;
-#pragma unroll
-            for (int ks = 0; ks < GBK / 16; ++ks) {
-                const int chunk = ((2 * ks + h) ^ swz_lane) * 16;
-                bf16x8 fa[2], fb[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    fa[i] = *(const bf16x8 *)(As + (wm * 64 + i * 32 + l32) * GROWB + chunk);
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    fb[j] = *(const bf16x8 *)(Bs + (wn * 64 + j * 32 + l32) * GROWB + chunk);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = mfma_bf16(fb[j], fa[i], acc[i][j]);
-            }
-            if (more) {   // the other stage was released by the last barrier
-                char *nxt = smem + ((kt + 1) & 1) * GSTAGE;
-                sa.store(nxt, tid);
-                sb.store(nxt + GOP_BYTES, tid);
-            }
+            if (more)
+                load(kt + 1);
+            compute(kt & 1);
+            if (more)
+                store((kt + 1) & 1);
             __syncthreads();   // stage kt+1 written by every wave; stage kt read by every wave
         }
-        // the last barrier released both stages: the epilogue stages C
-        // through them, 256 contiguous bytes of a row per 16 lanes
+        // the last barrier released the ring: the epilogue stages C through
+        // it, 256 contiguous bytes of a row per 16 lanes
         store_tile_staged<GenGeom>(p, acc, m0, n0, wm, wn, lane, smem + wave * EPI_F32_WAVE_BYTES);
         if (PERSIST)
             __syncthreads();   // every wave's buffer read before the next prologue writes
     }
 }
 
-template <bool A_KC, bool B_KC, bool PERSIST>
+template <bool A_KC, bool B_KC, bool PERSIST, int BK>
 hipError_t launch_g(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + GBM - 1) / GBM, tiles_n = (p.N + GBN - 1) / GBN;
@@ -191,21 +301,21 @@ hipError_t launch_g(const GemmArgs &p, hipStream_t s)
             ncu > 0 && ntiles > 3 * ncu)
             grid = 3 * ncu;
     }
-    hipLaunchKernelGGL((gemm_general<A_KC, B_KC, PERSIST>), dim3(grid), dim3(256), 0, s, p, group_m);
+    hipLaunchKernelGGL((gemm_general<A_KC, B_KC, PERSIST, BK>), dim3(grid), dim3(256), 0, s, p, group_m);
     return hipGetLastError();
 }
 
-template <bool PERSIST>
+template <bool PERSIST, int BK>
 hipError_t launch_g_layout(const GemmArgs &p, hipStream_t s)
 {
     const bool akc = !p.a_cm, bkc = p.b_cm;
     if (akc && bkc)
-        return launch_g<true, true, PERSIST>(p, s);
+        return launch_g<true, true, PERSIST, BK>(p, s);
     if (akc)
-        return launch_g<true, false, PERSIST>(p, s);
+        return launch_g<true, false, PERSIST, BK>(p, s);
     if (bkc)
-        return launch_g<false, true, PERSIST>(p, s);
-    return launch_g<false, false, PERSIST>(p, s);
+        return launch_g<false, true, PERSIST, BK>(p, s);
+    return launch_g<false, false, PERSIST, BK>(p, s);
 }
 
 } // namespace
@@ -213,18 +323,18 @@ hipError_t launch_g_layout(const GemmArgs &p, hipStream_t s)
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
     switch (level) {
-    case 5: return launch_g_layout<false>(p, s);
+    case 5: return launch_g_layout<false, 32>(p, s);
     case 6: {
         // while the tiles fit the three workgroups per CU at once, the
         // persistent grid is the one-tile grid (whose kernel needs fewer
-        // registers and so keeps three workgroups per CU)
+        // registers)
         const long ntiles = (long)((p.M + GBM - 1) / GBM) * ((p.N + GBN - 1) / GBN);
         int dev = 0, ncu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
             ntiles <= 3L * ncu)
-            return launch_g_layout<false>(p, s);
-        return launch_g_layout<true>(p, s);
+            return launch_g_layout<false, 32>(p, s);
+        return launch_g_layout<true, 32>(p, s);
     }
     default: return hipErrorInvalidValue;
     }

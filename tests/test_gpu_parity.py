@@ -377,6 +377,31 @@ def test_large_ragged_integer_exact(level, fmt, kind):
     assert np.array_equal(vals[ii, jj], cref)
 
 
+@pytest.mark.parametrize("level", [5, 6])
+@pytest.mark.parametrize("layout", [(False, False), (True, True), (True, False)],
+                         ids=["a_row_b_row", "a_col_b_col", "a_col_b_row"])
+@pytest.mark.parametrize("K", [1000, 1027])
+def test_large_ragged_general_layouts_integer_exact(level, layout, K):
+    """bf16 layouts the direct-load kernels do not take (an MN-major operand,
+    or K rows that are not 16-byte aligned), at a ragged shape with more
+    tiles than the one-tile grid holds: level 6 runs the persistent grid.
+    Row and column sums are exact, sampled entries bitwise."""
+    M, N = 4100, 8200
+    a_cm, b_cm = layout
+    p = integer_problem(M, N, K, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_F32,
+                        seed=7300 + level + K, name="large_general_int")
+    r = run_level(p, level)
+    assert r is not None
+    vals = r[0]
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    assert np.array_equal(vals.sum(axis=1), A @ B.sum(axis=1))
+    assert np.array_equal(vals.sum(axis=0), A.sum(axis=0) @ B)
+    ii, jj = sample_indices(M, N, 1000, 73)
+    cref, _ = oracle_entries(p, ii, jj)
+    assert np.array_equal(vals[ii, jj], cref)
+
+
 @pytest.mark.parametrize("level", [6, 7, None])
 @pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
 @pytest.mark.parametrize("kind", ["ktail", "kwhole", "kgroups"])
