@@ -1,7 +1,9 @@
 """Seeded synthetic GEMM inputs, shared by the tests, the smoke check and the
 benchmark.  This module holds no GEMM arithmetic: it only draws numbers and
-stores them in the byte formats the library reads (bf16 bits, E4M3FN codes,
-E8M0 scale bytes, fp32 or bf16 C0), in storage order.
+stores them in the byte formats the library reads (bf16 bits, MX element
+codes, E8M0 scale bytes, fp32 or bf16 C0), in storage order.  The 6- and
+4-bit MX element codes are packed along K: element e of a row at bit offset
+6e (4e) of the row's little-endian bit string.
 
 Every draw uses its own ``torch.Generator`` seeded with ``seed*1000 + t``
 (t: A=0, B=1, C0=2, SA=3, SB=4) and fills the operand in its *storage* order,
@@ -26,6 +28,12 @@ import torch
 
 BF16 = 0
 E4M3FN = 1
+E5M2 = 2
+E2M3 = 3
+E3M2 = 4
+E2M1 = 5
+MX_FORMATS = (E4M3FN, E5M2, E2M3, E3M2, E2M1)
+FORMAT_BITS = {BF16: 16, E4M3FN: 8, E5M2: 8, E2M3: 6, E3M2: 6, E2M1: 4}
 OUT_F32 = 0
 OUT_BF16 = 1
 MX_BLOCK = 32
@@ -37,8 +45,8 @@ class Problem:
     M: int
     N: int
     K: int
-    fmt: int                 # BF16 or E4M3FN
-    A: np.ndarray            # uint16 (bf16 bits) or uint8 (E4M3FN codes)
+    fmt: int                 # BF16 or one of MX_FORMATS (both operands)
+    A: np.ndarray            # uint16 (bf16 bits) or uint8 (MX codes, packed for 6/4 bits)
     lda: int
     a_col_major: bool
     B: np.ndarray
@@ -92,6 +100,48 @@ def to_e4m3fn_codes(x):
     return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+# Codes of the small integers 0..4 in the 6- and 4-bit formats (OCP MX v1.0
+# element tables), and each format's sign bit and code count.
+_INT_CODES = {E2M3: [0x00, 0x08, 0x10, 0x14, 0x18], E3M2: [0x00, 0x0C, 0x10, 0x12, 0x14],
+              E2M1: [0x0, 0x2, 0x4, 0x5, 0x6]}
+_SIGN = {E2M3: 0x20, E3M2: 0x20, E2M1: 0x8}
+_NCODES = {E2M3: 64, E3M2: 64, E2M1: 16}
+
+
+def pack_codes(codes, bits):
+    """(outer, inner) uint8 codes -> (outer, inner * bits / 8) packed bytes,
+    element e of a row at bit offset bits * e (little-endian)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return codes
+    outer, inner = codes.shape
+    if (inner * bits) % 8:
+        raise ValueError("a packed row must fill whole bytes")
+    out = np.zeros((outer, inner * bits // 8), dtype=np.uint8)
+    for e in range(inner):
+        bit = e * bits
+        byte, off = bit // 8, bit % 8
+        v = codes[:, e].astype(np.uint16) << off
+        out[:, byte] |= (v & 0xFF).astype(np.uint8)
+        if off + bits > 8:
+            out[:, byte + 1] |= (v >> 8).astype(np.uint8)
+    return out
+
+
+def _small_codes(fmt, dist, shape, g, lo, hi):
+    """6- or 4-bit codes: 'codes' draws every code with equal probability;
+    'int' draws integers lo..hi (|v| <= 4) and takes their codes."""
+    if dist == "codes":
+        return torch.randint(0, _NCODES[fmt], shape, generator=g).numpy().astype(np.uint8)
+    if dist == "int":
+        if not (-4 <= lo <= hi <= 4):
+            raise ValueError("integer draws of the small formats span -4..4")
+        v = torch.randint(int(lo), int(hi) + 1, shape, generator=g).numpy()
+        table = np.array(_INT_CODES[fmt], dtype=np.uint8)
+        return np.where(v < 0, table[np.abs(v)] | _SIGN[fmt], table[np.abs(v)]).astype(np.uint8)
+    raise ValueError(f"the 6- and 4-bit formats draw 'codes' or 'int', not {dist}")
+
+
 def _draw(dist, shape, g, lo=-1.0, hi=1.0, std=1.0):
     if dist == "uniform":
         return torch.rand(shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
@@ -104,12 +154,25 @@ def _draw(dist, shape, g, lo=-1.0, hi=1.0, std=1.0):
 
 def _operand(rows, cols, col_major, ld, fmt, dist, g, **kw):
     outer, inner = _storage_shape(rows, cols, col_major, ld)
+    logical_inner = rows if col_major else cols
+    if fmt in (E2M3, E3M2, E2M1):
+        codes = _small_codes(fmt, dist, (outer, inner), g, kw.get("lo", -1.0), kw.get("hi", 1.0))
+        # padding beyond the logical extent holds the largest code, so a
+        # kernel that reads it shows up in the result
+        codes[:, logical_inner:] = _NCODES[fmt] // 2 - 1
+        return pack_codes(codes, FORMAT_BITS[fmt])
+    if fmt == E5M2 and dist == "codes":
+        codes = torch.randint(0, 256, (outer, inner), generator=g).numpy().astype(np.uint8)
+        codes[(codes & 0x7C) == 0x7C] = 0x3C      # no infinities or NaN: 1.0
+        codes[:, logical_inner:] = 0x7F
+        return codes
     x = _draw(dist, (outer, inner), g, **kw)
     # padding columns beyond the logical extent hold NaN in bf16 and the NaN
     # code in fp8, so a kernel that reads them shows up in the result
-    logical_inner = rows if col_major else cols
     if inner > logical_inner:
         x[:, logical_inner:] = float("nan")
+    if fmt == E5M2:
+        return x.to(torch.float8_e5m2).view(torch.uint8).numpy()
     return to_bf16_bits(x) if fmt == BF16 else to_e4m3fn_codes(x)
 
 
@@ -136,7 +199,7 @@ def make_problem(M, N, K, *, fmt=BF16, a_col_major=False, b_col_major=True,
         c = _draw(c_dist, (outer, ldc), _gen(seed, 2), lo=-1.0, hi=1.0)
         C0 = c.numpy().astype(np.float32) if c_dtype == OUT_F32 else to_bf16_bits(c)
     SA = SB = None
-    if fmt == E4M3FN:
+    if fmt in MX_FORMATS:
         kb = (K + MX_BLOCK - 1) // MX_BLOCK
         ld_sa = max(kb, 1) if ld_sa is None else ld_sa
         ld_sb = max(kb, 1) if ld_sb is None else ld_sb

@@ -5,7 +5,8 @@ import this package.  It loads ``liboracle.so`` (built by gcc from
 ``oracle.c`` alone) and shares nothing with the HIP library.
 
 What it computes is the plain definition C <- alpha*op(A)*op(B) + beta*C0 with
-exact fp64 decoding of bf16 / E4M3FN / E8M0 inputs and fp64 sums over k in
+exact fp64 decoding of bf16 / MX (E4M3FN, E5M2, E2M3, E3M2, E2M1 elements,
+E8M0 scales; OCP MX v1.0) inputs and fp64 sums over k in
 order (the baseline contract of "B200 GEMM Optimization Ladder", section E
 step 1; block-scaled operands as in "B200 TMEM Lifecycle Planner", section A1
 case 2).  ``check`` applies the acceptance bound to a GPU result.
@@ -19,6 +20,11 @@ from .build import LIB_PATH, build_oracle
 
 BF16 = 0
 E4M3FN = 1
+E5M2 = 2
+E2M3 = 3
+E3M2 = 4
+E2M1 = 5
+FORMAT_BITS = {BF16: 16, E4M3FN: 8, E5M2: 8, E2M3: 6, E3M2: 6, E2M1: 4}
 OUT_F32 = 0
 OUT_BF16 = 1
 
@@ -45,6 +51,10 @@ def _load():
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
+    for name in ("e5m2", "e2m3", "e3m2", "e2m1"):
+        f = getattr(lib, f"oracle_{name}_to_f64")
+        f.argtypes = [ctypes.c_uint8]
+        f.restype = ctypes.c_double
     lib.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_e8m0_to_f64.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
@@ -63,6 +73,22 @@ def bf16_to_f64(code):
 
 def e4m3fn_to_f64(code):
     return _load().oracle_e4m3fn_to_f64(int(code))
+
+
+def e5m2_to_f64(code):
+    return _load().oracle_e5m2_to_f64(int(code))
+
+
+def e2m3_to_f64(code):
+    return _load().oracle_e2m3_to_f64(int(code))
+
+
+def e3m2_to_f64(code):
+    return _load().oracle_e3m2_to_f64(int(code))
+
+
+def e2m1_to_f64(code):
+    return _load().oracle_e2m1_to_f64(int(code))
 
 
 def e8m0_to_f64(code):

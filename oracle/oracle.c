@@ -19,9 +19,10 @@
  *    steps 2-4 (each level must be element-wise correct against that
  *    reference, including the K tail and the boundary tiles).
  *  - "B200 TMEM Lifecycle Planner", section A1 case 2 (block-scaled MMA: each
- *    operand carries its own scale factors beside the data).  The block size
- *    (32 consecutive K elements, one E8M0 scale each) and the element format
- *    (FP8 E4M3) follow the OCP Microscaling (MX) v1.0 formats.
+ *    operand carries its own scale factors beside the data).  The pages name
+ *    no element format; the block size (32 consecutive K elements, one E8M0
+ *    scale each) and the element formats (FP8 E4M3 and E5M2, FP6 E2M3 and
+ *    E3M2, FP4 E2M1) follow the OCP Microscaling (MX) v1.0 formats.
  *  - The math definition itself is the ordinary BLAS one: C0 is not read when
  *    beta == 0, and A, B are not read when alpha == 0 or K == 0.
  *
@@ -29,7 +30,23 @@
  *  - bf16:   the top 16 bits of an IEEE binary32; widen by shifting left 16.
  *  - E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; no infinities;
  *            exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN.
+ *  - E5M2:   sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent field
+ *            31 is infinity (mantissa 0) or NaN; field 0 is subnormal
+ *            (m/4 * 2^-14).
+ *  - E2M3:   6 bits: sign, 2 exponent bits (bias 1), 3 mantissa bits; no
+ *            infinities or NaN; field 0 is subnormal (m/8).
+ *  - E3M2:   6 bits: sign, 3 exponent bits (bias 3), 2 mantissa bits; no
+ *            infinities or NaN; field 0 is subnormal (m/4 * 2^-2).
+ *  - E2M1:   4 bits: sign, 2 exponent bits (bias 1), 1 mantissa bit; no
+ *            infinities or NaN; field 0 is subnormal (m/2).
  *  - E8M0:   an unsigned biased exponent, value 2^(b-127); 0xFF is NaN.
+ *
+ * Storage of the MX element formats: 8-bit formats one byte per element;
+ * the 6- and 4-bit formats packed along K, element e of a row at bit offset
+ * 6e (4e) of the row's little-endian bit string (so two E2M1 per byte, the
+ * lower K in the low nibble, and four E2M3 / E3M2 per three bytes), with
+ * leading dimensions in elements.  Packed operands are K-contiguous only
+ * (A row-major, B column-major).
  *
  * Leading dimensions are in elements.  a(i,k) lives at A[i*lda + k] when A is
  * row-major and at A[k*lda + i] when it is column-major; b(k,j) lives at
@@ -42,7 +59,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_BF16 = 0, ORACLE_E4M3FN = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_E4M3FN = 1, ORACLE_E5M2 = 2, ORACLE_E2M3 = 3, ORACLE_E3M2 = 4,
+       ORACLE_E2M1 = 5 };
 enum { ORACLE_OUT_F32 = 0, ORACLE_OUT_BF16 = 1 };
 
 double oracle_bf16_to_f64(uint16_t bits)
@@ -68,6 +86,74 @@ double oracle_e4m3fn_to_f64(uint8_t code)
     return sign ? -mag : mag;
 }
 
+/* A sign-exponent-mantissa code with no infinities or NaN (the MX 6- and
+   4-bit formats): field 0 is subnormal, m / 2^mbits * 2^(1 - bias). */
+static double small_float(unsigned code, int ebits, int mbits, int bias)
+{
+    int sign = (code >> (ebits + mbits)) & 1;
+    int e = (code >> mbits) & ((1 << ebits) - 1);
+    int m = code & ((1 << mbits) - 1);
+    double frac = (double)m / (double)(1 << mbits);
+    double mag = e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, e - bias);
+    return sign ? -mag : mag;
+}
+
+double oracle_e5m2_to_f64(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 2) & 0x1F;
+    int m = code & 0x3;
+    double mag;
+    if (e == 0x1F)
+        mag = m == 0 ? INFINITY : NAN;
+    else if (e == 0)
+        mag = ldexp((double)m / 4.0, -14);
+    else
+        mag = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return sign ? -mag : mag;
+}
+
+double oracle_e2m3_to_f64(uint8_t code) { return small_float(code & 0x3F, 2, 3, 1); }
+double oracle_e3m2_to_f64(uint8_t code) { return small_float(code & 0x3F, 3, 2, 3); }
+double oracle_e2m1_to_f64(uint8_t code) { return small_float(code & 0xF, 2, 1, 1); }
+
+/* Bits per element of each operand format. */
+static int format_bits(int fmt)
+{
+    switch (fmt) {
+    case ORACLE_BF16: return 16;
+    case ORACLE_E4M3FN:
+    case ORACLE_E5M2: return 8;
+    case ORACLE_E2M3:
+    case ORACLE_E3M2: return 6;
+    case ORACLE_E2M1: return 4;
+    default: return 0;
+    }
+}
+
+/* The code of element idx of an MX operand stored as described above. */
+static unsigned mx_code(int fmt, const void *X, int64_t idx)
+{
+    const uint8_t *b = (const uint8_t *)X;
+    int bits = format_bits(fmt);
+    if (bits == 8)
+        return b[idx];
+    int64_t bit = idx * bits;
+    unsigned w = b[bit / 8] | ((bit % 8 + bits > 8) ? (unsigned)b[bit / 8 + 1] << 8 : 0u);
+    return (w >> (bit % 8)) & ((1u << bits) - 1);
+}
+
+static double mx_value(int fmt, unsigned code)
+{
+    switch (fmt) {
+    case ORACLE_E4M3FN: return oracle_e4m3fn_to_f64((uint8_t)code);
+    case ORACLE_E5M2: return oracle_e5m2_to_f64((uint8_t)code);
+    case ORACLE_E2M3: return oracle_e2m3_to_f64((uint8_t)code);
+    case ORACLE_E3M2: return oracle_e3m2_to_f64((uint8_t)code);
+    default: return oracle_e2m1_to_f64((uint8_t)code);
+    }
+}
+
 double oracle_e8m0_to_f64(uint8_t code)
 {
     if (code == 0xFF)
@@ -89,8 +175,7 @@ static double load_a(int fmt, const void *A, int64_t lda, int col_major,
     int64_t idx = col_major ? k * lda + i : i * lda + k;
     if (fmt == ORACLE_BF16)
         return oracle_bf16_to_f64(((const uint16_t *)A)[idx]);
-    return oracle_e4m3fn_to_f64(((const uint8_t *)A)[idx]) *
-           oracle_e8m0_to_f64(SA[i * ld_sa + k / 32]);
+    return mx_value(fmt, mx_code(fmt, A, idx)) * oracle_e8m0_to_f64(SA[i * ld_sa + k / 32]);
 }
 
 /* b(k,j) of the logical K x N operand, decoded (scale applied for MX). */
@@ -100,8 +185,7 @@ static double load_b(int fmt, const void *B, int64_t ldb, int col_major,
     int64_t idx = col_major ? j * ldb + k : k * ldb + j;
     if (fmt == ORACLE_BF16)
         return oracle_bf16_to_f64(((const uint16_t *)B)[idx]);
-    return oracle_e4m3fn_to_f64(((const uint8_t *)B)[idx]) *
-           oracle_e8m0_to_f64(SB[j * ld_sb + k / 32]);
+    return mx_value(fmt, mx_code(fmt, B, idx)) * oracle_e8m0_to_f64(SB[j * ld_sb + k / 32]);
 }
 
 static double load_c0(const void *C0, int64_t ldc, int col_major, int c_dtype,
@@ -158,14 +242,21 @@ static int check(const problem *p)
 {
     if (p->M < 0 || p->N < 0 || p->K < 0)
         return 1;
-    if (p->a_fmt != p->b_fmt || (p->a_fmt != ORACLE_BF16 && p->a_fmt != ORACLE_E4M3FN))
+    if (format_bits(p->a_fmt) == 0 || format_bits(p->b_fmt) == 0)
+        return 1;
+    if ((p->a_fmt == ORACLE_BF16) != (p->b_fmt == ORACLE_BF16))
+        return 1;
+    /* packed formats: K-contiguous rows of whole bytes */
+    if (format_bits(p->a_fmt) < 8 && (p->a_col_major || (p->lda * format_bits(p->a_fmt)) % 8))
+        return 1;
+    if (format_bits(p->b_fmt) < 8 && (!p->b_col_major || (p->ldb * format_bits(p->b_fmt)) % 8))
         return 1;
     if (p->c_dtype != ORACLE_OUT_F32 && p->c_dtype != ORACLE_OUT_BF16)
         return 1;
     int reads_ab = p->alpha != 0.0 && p->K > 0 && p->M > 0 && p->N > 0;
     if (reads_ab && (!p->A || !p->B))
         return 1;
-    if (reads_ab && p->a_fmt == ORACLE_E4M3FN && (!p->SA || !p->SB))
+    if (reads_ab && p->a_fmt != ORACLE_BF16 && (!p->SA || !p->SB))
         return 1;
     if (p->beta != 0.0 && p->M > 0 && p->N > 0 && !p->C0)
         return 1;

@@ -4,7 +4,8 @@ import numpy as np
 import torch
 
 import oracle
-from matrix_core_engineering_amd.inputs import BF16, OUT_BF16, MX_BLOCK
+from matrix_core_engineering_amd.inputs import (BF16, E4M3FN, E5M2, FORMAT_BITS, MX_BLOCK, OUT_BF16,
+                                                _INT_CODES, _SIGN)
 
 
 def bf16_bits_to_f64(bits):
@@ -24,7 +25,46 @@ def torch_decode_elements(codes, fmt):
     t = torch.from_numpy(np.ascontiguousarray(codes))
     if fmt == BF16:
         return t.view(torch.bfloat16).to(torch.float64).numpy()
+    if fmt == E5M2:
+        return t.view(torch.float8_e5m2).to(torch.float64).numpy()
+    if fmt != E4M3FN:
+        raise ValueError("torch has no decoder for the packed formats; use int_decode_elements")
     return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def unpack_codes(store, bits, inner):
+    """(outer, bytes) packed storage -> (outer, inner) codes; element e of a
+    row at bit offset bits * e, little-endian (written here independently of
+    the generator's packer)."""
+    store = np.ascontiguousarray(store, dtype=np.uint8)
+    if bits == 8:
+        return store[:, :inner]
+    bitsrow = np.unpackbits(store, axis=1, bitorder="little")
+    out = np.zeros((store.shape[0], inner), dtype=np.uint8)
+    for b in range(bits):
+        out |= (bitsrow[:, b:inner * bits:bits] << b).astype(np.uint8)
+    return out
+
+
+def int_decode_elements(store, fmt, inner):
+    """Values of an 'int' draw in a packed format (codes of -4..4 only)."""
+    codes = unpack_codes(store, FORMAT_BITS[fmt], inner)
+    table = {}
+    for v, c in enumerate(_INT_CODES[fmt]):
+        table[c] = float(v)
+        table[c | _SIGN[fmt]] = -float(v)
+    vals = np.vectorize(lambda c: table.get(int(c), np.nan))(codes)
+    if np.isnan(vals).any():
+        raise ValueError("a code outside the integer table")
+    return vals.astype(np.float64)
+
+
+def decode_elements(p, store, rows, cols, col_major, inner):
+    """Logical rows x cols values of an operand of problem p: torch for bf16
+    and fp8, the integer code table for the packed formats."""
+    if FORMAT_BITS[p.fmt] >= 8:
+        return logical(torch_decode_elements(store, p.fmt), rows, cols, col_major)
+    return logical(int_decode_elements(store, p.fmt, inner), rows, cols, col_major)
 
 
 def torch_decode_scales(codes):
