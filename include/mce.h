@@ -15,7 +15,8 @@
  * fp8 entry points follow "B200 TMEM Lifecycle Planner", section A1 case 2
  * (block-scaled MMA: data and scale factors staged separately, scale layout
  * distinct from the accumulator layout), with the OCP MX formats: E4M3FN
- * elements and one E8M0 scale per 32 consecutive K elements.
+ * (gemm_mxfp8) or any MX element format (gemm_mx) and one E8M0 scale per 32
+ * consecutive K elements.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -69,6 +70,16 @@ typedef enum {
 } mce_status;
 
 enum { MCE_OUT_F32 = 0, MCE_OUT_BF16 = 1 };
+
+/* MX element formats (OCP MX v1.0), numbered as the block-scaled matrix-core
+   instruction's format operand. */
+enum {
+    MCE_MX_E4M3 = 0,   /* FP8 E4M3FN, one byte per element */
+    MCE_MX_E5M2 = 1,   /* FP8 E5M2, one byte per element */
+    MCE_MX_E2M3 = 2,   /* FP6 E2M3, packed: four elements per three bytes */
+    MCE_MX_E3M2 = 3,   /* FP6 E3M2, packed likewise */
+    MCE_MX_E2M1 = 4    /* FP4 E2M1, packed: two elements per byte */
+};
 
 /*
  * bf16 GEMM.  A: bf16 bits (uint16), B: bf16 bits, fp32 accumulate.
@@ -137,6 +148,37 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K,
                      void *C, int64_t ldc, int c_col_major, int c_dtype,
                      float alpha, float beta, void *stream);
 
+/*
+ * MX block-scaled GEMM for any MX element format (both operands the same):
+ * gemm_mxfp8 is gemm_mx(MCE_MX_E4M3, ...).  Scales, layouts and semantics as
+ * for gemm_mxfp8.  The 6- and 4-bit formats are packed along K: element k of
+ * a row is the 6 (4) bits at bit offset 6k (4k) of the row's little-endian
+ * bit string, so two E2M1 share a byte (lower k in the low nibble) and four
+ * E2M3 / E3M2 share three bytes; lda and ldb stay in elements and, like K,
+ * must be multiples of 2 (E2M1) or 4 (E2M3, E3M2), else MCE_EINVAL.  An
+ * unknown elem_format is MCE_EINVAL.  ("B200 TMEM Lifecycle Planner",
+ * section A1 case 2: block-scaled MMA; the pages name no element format.)
+ *
+ * Levels: 3 for every format; 5-7 for E4M3 and E5M2 under the rules of
+ * gemm_mxfp8_level; the 6- and 4-bit formats run level 3 (other levels
+ * return MCE_EUNSUPPORTED).
+ */
+int gemm_mx(int elem_format, int64_t M, int64_t N, int64_t K,
+            const void *A, int64_t lda, int a_col_major,
+            const void *SA, int64_t ld_sa,
+            const void *B, int64_t ldb, int b_col_major,
+            const void *SB, int64_t ld_sb,
+            void *C, int64_t ldc, int c_col_major, int c_dtype,
+            float alpha, float beta, void *stream);
+
+int gemm_mx_level(int level, int elem_format, int64_t M, int64_t N, int64_t K,
+                  const void *A, int64_t lda, int a_col_major,
+                  const void *SA, int64_t ld_sa,
+                  const void *B, int64_t ldb, int b_col_major,
+                  const void *SB, int64_t ld_sb,
+                  void *C, int64_t ldc, int c_col_major, int c_dtype,
+                  float alpha, float beta, void *stream);
+
 /* Level gemm_bf16 / gemm_mxfp8 would run for this problem (0 if none). */
 int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda, int a_col_major,
@@ -144,6 +186,10 @@ int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K,
 int gemm_mxfp8_pick_level(int64_t M, int64_t N, int64_t K,
                           const void *A, int64_t lda, int a_col_major,
                           const void *B, int64_t ldb, int b_col_major);
+/* Level gemm_mx would run for this format and problem (0 if none). */
+int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, int a_col_major,
+                       const void *B, int64_t ldb, int b_col_major);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char *gemm_status_string(int status);

@@ -11,17 +11,21 @@ import ctypes
 import os
 
 __all__ = ["gemm_bf16", "gemm_mxfp8", "gemm_bf16_level", "gemm_mxfp8_level",
-           "gemm_bf16_pick_level", "gemm_mxfp8_pick_level",
+           "gemm_bf16_pick_level", "gemm_mxfp8_pick_level", "gemm_mx",
+           "gemm_mx_level", "gemm_mx_pick_level", "MCE_MX_E4M3", "MCE_MX_E5M2",
+           "MCE_MX_E2M3", "MCE_MX_E3M2", "MCE_MX_E2M1",
            "gemm_status_string", "MceError", "lib_path", "load",
            "EXPORTED_SYMBOLS", "MCE_OK", "MCE_EINVAL", "MCE_EUNSUPPORTED",
            "MCE_ELAUNCH", "MCE_OUT_F32", "MCE_OUT_BF16"]
 
 MCE_OK, MCE_EINVAL, MCE_EUNSUPPORTED, MCE_ELAUNCH = 0, 1, 2, 3
 MCE_OUT_F32, MCE_OUT_BF16 = 0, 1
+MCE_MX_E4M3, MCE_MX_E5M2, MCE_MX_E2M3, MCE_MX_E3M2, MCE_MX_E2M1 = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("gemm_bf16", "gemm_mxfp8", "gemm_bf16_level",
                     "gemm_mxfp8_level", "gemm_bf16_pick_level",
-                    "gemm_mxfp8_pick_level", "gemm_status_string")
+                    "gemm_mxfp8_pick_level", "gemm_mx", "gemm_mx_level",
+                    "gemm_mx_pick_level", "gemm_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -61,6 +65,9 @@ def load():
     pick = mnk + [vp, i64, i32, vp, i64, i32]
     lib.gemm_bf16_pick_level.argtypes = pick
     lib.gemm_mxfp8_pick_level.argtypes = pick
+    lib.gemm_mx.argtypes = [i32] + mx_args
+    lib.gemm_mx_level.argtypes = [i32, i32] + mx_args
+    lib.gemm_mx_pick_level.argtypes = [i32] + pick
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = i32
     lib.gemm_status_string.argtypes = [i32]
@@ -137,6 +144,32 @@ def gemm_bf16_pick_level(M, N, K, A, lda, a_col_major, B, ldb, b_col_major):
 def gemm_mxfp8_pick_level(M, N, K, A, lda, a_col_major, B, ldb, b_col_major):
     return load().gemm_mxfp8_pick_level(M, N, K, _ptr(A), lda, int(a_col_major),
                                         _ptr(B), ldb, int(b_col_major))
+
+
+def gemm_mx(elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb, b_col_major,
+            SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta, stream=None,
+            raise_on_error=True):
+    st = load().gemm_mx(int(elem_format), M, N, K, _ptr(A), lda, int(a_col_major), _ptr(SA),
+                        ld_sa, _ptr(B), ldb, int(b_col_major), _ptr(SB), ld_sb, _ptr(C), ldc,
+                        int(c_col_major), int(c_dtype), float(alpha), float(beta),
+                        _stream(stream))
+    return _check(st, f"gemm_mx({elem_format})", raise_on_error)
+
+
+def gemm_mx_level(level, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                  b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
+                  stream=None, raise_on_error=True):
+    st = load().gemm_mx_level(int(level), int(elem_format), M, N, K, _ptr(A), lda,
+                              int(a_col_major), _ptr(SA), ld_sa, _ptr(B), ldb,
+                              int(b_col_major), _ptr(SB), ld_sb, _ptr(C), ldc,
+                              int(c_col_major), int(c_dtype), float(alpha), float(beta),
+                              _stream(stream))
+    return _check(st, f"gemm_mx_level({level}, {elem_format})", raise_on_error)
+
+
+def gemm_mx_pick_level(elem_format, M, N, K, A, lda, a_col_major, B, ldb, b_col_major):
+    return load().gemm_mx_pick_level(int(elem_format), M, N, K, _ptr(A), lda,
+                                     int(a_col_major), _ptr(B), ldb, int(b_col_major))
 
 
 def gemm_status_string(status):

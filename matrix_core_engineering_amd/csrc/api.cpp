@@ -14,7 +14,7 @@ namespace {
 
 using mce::GemmArgs;
 
-enum Fmt { FMT_BF16 = 0, FMT_MXFP8 = 1 };
+enum Fmt { FMT_BF16 = 0, FMT_MX = 1 };
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;   // 32-bit buffer offsets
 constexpr int kMaxDevices = 64;
@@ -56,6 +56,7 @@ bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
 struct Call {
     int level;   // 0 = pick
     Fmt fmt;
+    int mx_fmt;  // MX: element format (MCE_MX_*)
     int64_t M, N, K;
     const void *A;
     int64_t lda;
@@ -75,10 +76,24 @@ struct Call {
     hipStream_t stream;
 };
 
+// Bits per element of the call's operands.
+int elem_bits(const Call &c) { return c.fmt == FMT_BF16 ? 16 : mce::mx_bits(c.mx_fmt); }
+
+// Bytes spanned by rows x cols elements of `bits` with leading dimension ld.
+int64_t span_bytes_bits(int64_t outer, int64_t inner, int64_t ld, int bits)
+{
+    if (outer == 0 || inner == 0)
+        return 0;
+    return (((outer - 1) * ld + inner) * bits + 7) / 8;
+}
+
 // Levels 4-7 read operands with 16-byte direct loads: both operands
-// K-contiguous, 16-byte aligned rows, K a whole number of 16-byte chunks.
+// K-contiguous, 16-byte aligned rows, K a whole number of 16-byte chunks;
+// for MX only the 8-bit element formats have those kernels.
 bool fast_eligible(const Call &c)
 {
+    if (c.fmt == FMT_MX && elem_bits(c) != 8)
+        return false;
     int64_t elt = c.fmt == FMT_BF16 ? 2 : 1;
     int64_t per_chunk = 16 / elt;
     return c.a_cm == 0 && c.b_cm == 1 && (c.lda % per_chunk) == 0 && (c.ldb % per_chunk) == 0 &&
@@ -118,7 +133,7 @@ bool level_accepts(const Call &c, int level)
     }
     switch (level) {
     case 3: return true;
-    case 5: case 6: case 7: return fast_eligible(c) && mx_scales_eligible(c);
+    case 5: case 6: case 7: return fast_eligible(c) && mx_scales_eligible(c);   // 8-bit formats
     default: return false;
     }
 }
@@ -131,9 +146,15 @@ int validate(const Call &c)
         return MCE_EINVAL;
     if (c.c_dtype != MCE_OUT_F32 && c.c_dtype != MCE_OUT_BF16)
         return MCE_EINVAL;
-    if (c.fmt == FMT_MXFP8 && !(c.a_cm == 0 && c.b_cm == 1))
+    if (c.fmt == FMT_MX && (c.mx_fmt < MCE_MX_E4M3 || c.mx_fmt > MCE_MX_E2M1))
+        return MCE_EINVAL;
+    if (c.fmt == FMT_MX && !(c.a_cm == 0 && c.b_cm == 1))
         return MCE_EUNSUPPORTED;
-    const int64_t elt = c.fmt == FMT_BF16 ? 2 : 1;
+    const int bits = elem_bits(c);
+    // packed 6- and 4-bit rows: every row and the K extent fill whole bytes
+    const int64_t per_byte_group = bits == 6 ? 4 : bits == 4 ? 2 : 1;
+    if (c.K % per_byte_group || c.lda % per_byte_group || c.ldb % per_byte_group)
+        return MCE_EINVAL;
     const int64_t celt = c.c_dtype == MCE_OUT_F32 ? 4 : 2;
     // leading dimensions: at least the contiguous extent, and at least 1
     auto ld_ok = [](int64_t ld, int64_t extent) { return ld >= 1 && ld >= extent; };
@@ -141,7 +162,7 @@ int validate(const Call &c)
         !ld_ok(c.ldc, c.c_cm ? c.M : c.N))
         return MCE_EINVAL;
     const int64_t nblk = (c.K + 31) / 32;
-    if (c.fmt == FMT_MXFP8 && (!ld_ok(c.ld_sa, nblk) || !ld_ok(c.ld_sb, nblk)))
+    if (c.fmt == FMT_MX && (!ld_ok(c.ld_sa, nblk) || !ld_ok(c.ld_sb, nblk)))
         return MCE_EINVAL;
     if (c.M == 0 || c.N == 0)
         return MCE_OK;
@@ -155,13 +176,13 @@ int validate(const Call &c)
         return MCE_OK;
     if (!c.A || !c.B)
         return MCE_EINVAL;
-    const int64_t na = c.a_cm ? span_bytes(c.K, c.M, c.lda, elt) : span_bytes(c.M, c.K, c.lda, elt);
-    const int64_t nb = c.b_cm ? span_bytes(c.N, c.K, c.ldb, elt) : span_bytes(c.K, c.N, c.ldb, elt);
+    const int64_t na = c.a_cm ? span_bytes_bits(c.K, c.M, c.lda, bits) : span_bytes_bits(c.M, c.K, c.lda, bits);
+    const int64_t nb = c.b_cm ? span_bytes_bits(c.N, c.K, c.ldb, bits) : span_bytes_bits(c.K, c.N, c.ldb, bits);
     if (na >= kMaxBytes || nb >= kMaxBytes)
         return MCE_EINVAL;
     if (overlaps(c.C, nc, c.A, na) || overlaps(c.C, nc, c.B, nb))
         return MCE_EINVAL;
-    if (c.fmt == FMT_MXFP8) {
+    if (c.fmt == FMT_MX) {
         if (!c.SA || !c.SB)
             return MCE_EINVAL;
         const int64_t nsa = span_bytes(c.M, nblk, c.ld_sa, 1);
@@ -218,6 +239,7 @@ GemmArgs kernel_args(const Call &c)
     p.c_dtype = c.c_dtype;
     p.alpha = c.alpha;
     p.beta = c.beta;
+    p.mx_fmt = c.mx_fmt;
     return p;
 }
 
@@ -244,15 +266,14 @@ int run(const Call &in)
                   : fast_eligible(c) || level == 4 || level == 7 ? mce::launch_fast_bf16(level, p, c.stream)
                                                          : mce::launch_general_bf16(level, p, c.stream);
         else
-            err = level <= 3 ? mce::launch_simple_mxfp8(p, c.stream)
-                             : mce::launch_fast_mxfp8(level, p, c.stream);
+            err = level <= 3 ? mce::launch_simple_mx(p, c.stream) : mce::launch_fast_mx(level, p, c.stream);
         if (err == hipErrorInvalidValue && level >= 4)
             return MCE_EUNSUPPORTED;
     }
     return err == hipSuccess ? MCE_OK : MCE_ELAUNCH;
 }
 
-Call make_call(int level, Fmt fmt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+Call make_call(int level, Fmt fmt, int mx_fmt, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                int a_cm, const void *SA, int64_t ld_sa, const void *B, int64_t ldb, int b_cm,
                const void *SB, int64_t ld_sb, void *C, int64_t ldc, int c_cm, int c_dtype,
                float alpha, float beta, void *stream)
@@ -260,6 +281,7 @@ Call make_call(int level, Fmt fmt, int64_t M, int64_t N, int64_t K, const void *
     Call c;
     c.level = level;
     c.fmt = fmt;
+    c.mx_fmt = mx_fmt;
     c.M = M;
     c.N = N;
     c.K = K;
@@ -291,7 +313,7 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a
               const void *B, int64_t ldb, int b_col_major, void *C, int64_t ldc, int c_col_major,
               int c_dtype, float alpha, float beta, void *stream)
 {
-    return run(make_call(0, FMT_BF16, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
+    return run(make_call(0, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
                          b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta,
                          stream));
 }
@@ -301,7 +323,7 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int 
                const void *SB, int64_t ld_sb, void *C, int64_t ldc, int c_col_major, int c_dtype,
                float alpha, float beta, void *stream)
 {
-    return run(make_call(0, FMT_MXFP8, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+    return run(make_call(0, FMT_MX, MCE_MX_E4M3, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
                          b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
                          stream));
 }
@@ -313,7 +335,7 @@ int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K, const void *A, i
 {
     if (level < 1 || level > 7)
         return MCE_EUNSUPPORTED;
-    return run(make_call(level, FMT_BF16, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
+    return run(make_call(level, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
                          b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta,
                          stream));
 }
@@ -325,7 +347,7 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K, const void *A, 
 {
     if (level < 1 || level > 7)
         return MCE_EUNSUPPORTED;
-    return run(make_call(level, FMT_MXFP8, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+    return run(make_call(level, FMT_MX, MCE_MX_E4M3, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
                          b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
                          stream));
 }
@@ -333,7 +355,7 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K, const void *A, 
 int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                          int a_col_major, const void *B, int64_t ldb, int b_col_major)
 {
-    Call c = make_call(0, FMT_BF16, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb, b_col_major,
+    Call c = make_call(0, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb, b_col_major,
                        nullptr, 0, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
     if (M < 0 || N < 0 || K < 0)
         return 0;
@@ -343,9 +365,41 @@ int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_t
 int gemm_mxfp8_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                           int a_col_major, const void *B, int64_t ldb, int b_col_major)
 {
-    Call c = make_call(0, FMT_MXFP8, M, N, K, A, lda, a_col_major, nullptr, 4, B, ldb, b_col_major,
+    Call c = make_call(0, FMT_MX, MCE_MX_E4M3, M, N, K, A, lda, a_col_major, nullptr, 4, B, ldb, b_col_major,
                        nullptr, 4, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
     if (M < 0 || N < 0 || K < 0 || a_col_major != 0 || b_col_major != 1)
+        return 0;
+    return pick_level(c);
+}
+
+int gemm_mx(int elem_format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+            int a_col_major, const void *SA, int64_t ld_sa, const void *B, int64_t ldb,
+            int b_col_major, const void *SB, int64_t ld_sb, void *C, int64_t ldc, int c_col_major,
+            int c_dtype, float alpha, float beta, void *stream)
+{
+    return run(make_call(0, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                         b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta, stream));
+}
+
+int gemm_mx_level(int level, int elem_format, int64_t M, int64_t N, int64_t K, const void *A,
+                  int64_t lda, int a_col_major, const void *SA, int64_t ld_sa, const void *B,
+                  int64_t ldb, int b_col_major, const void *SB, int64_t ld_sb, void *C, int64_t ldc,
+                  int c_col_major, int c_dtype, float alpha, float beta, void *stream)
+{
+    if (level < 1 || level > 7)
+        return MCE_EUNSUPPORTED;
+    return run(make_call(level, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B,
+                         ldb, b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
+                         stream));
+}
+
+int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                       int a_col_major, const void *B, int64_t ldb, int b_col_major)
+{
+    Call c = make_call(0, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, nullptr, 4, B, ldb,
+                       b_col_major, nullptr, 4, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
+    if (M < 0 || N < 0 || K < 0 || a_col_major != 0 || b_col_major != 1 ||
+        elem_format < MCE_MX_E4M3 || elem_format > MCE_MX_E2M1)
         return 0;
     return pick_level(c);
 }

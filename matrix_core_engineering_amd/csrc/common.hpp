@@ -35,7 +35,13 @@ struct GemmArgs {
     int ldc;
     int c_dtype;
     float alpha, beta;
+    int mx_fmt;         // MX only: element format code of both operands (MX_E4M3 ...)
 };
+
+// MX element formats, numbered as the block-scaled instruction's format
+// operand (cbsz / blgp); bits per element 8, 8, 6, 6, 4.
+enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M3 = 2, MX_E3M2 = 3, MX_E2M1 = 4 };
+constexpr int mx_bits(int fmt) { return fmt <= MX_E5M2 ? 8 : fmt <= MX_E3M2 ? 6 : 4; }
 
 // ---------------------------------------------------------------- MFMA maps
 //
@@ -52,6 +58,10 @@ struct GemmArgs {
 //   scale: block 0 (k 0..31) takes the E8M0 byte of lane l % 32, block 1
 //          (k 32..63) that of lane 32 + l % 32, each picked from the lane's
 //          32-bit scale register by op_sel.  D map as above.
+//   E5M2 (format 1) uses the same map.  The 6- and 4-bit formats (2-4) hold
+//   one whole 32-K block per lane: lane l holds k = 32h .. 32h + 31 of row
+//   (column) l % 32 packed at 6 or 4 bits per element from bit 0 of the
+//   first register (24 or 16 bytes), the rest of the 8 registers unused.
 //   The instruction sums each group of 8 consecutive products in fixed
 //   point, truncated 13 bits below the group's largest exponent sum, and
 //   adds the group sums in fp32 (measured; exact for small-integer data).
@@ -66,12 +76,20 @@ __device__ __forceinline__ floatx16 mfma_bf16(const bf16x8 &a, const bf16x8 &b, 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Block-scaled E4M3 x E4M3 -> fp32.  OPSEL picks the scale byte of sa/sb.
+// Block-scaled FMT x FMT -> fp32 (FMT: an MX_* element format code).  OPSEL
+// picks the scale byte of sa/sb.
+template <int FMT, int OPSEL>
+__device__ __forceinline__ floatx16 mfma_mx(const intx8 &a, const intx8 &b, const floatx16 &c, int sa,
+                                            int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, OPSEL, sa, OPSEL, sb);
+}
+
 template <int OPSEL>
 __device__ __forceinline__ floatx16 mfma_mxfp8(const intx8 &a, const intx8 &b, const floatx16 &c,
                                                int sa, int sb)
 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
+    return mfma_mx<MX_E4M3, OPSEL>(a, b, c, sa, sb);
 }
 
 __device__ __forceinline__ floatx16 zero16()

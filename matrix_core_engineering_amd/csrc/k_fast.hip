@@ -86,8 +86,12 @@ struct Bf16Op {
 };
 struct Mxfp8Op {
     static constexpr bool MX = true;
+    static constexpr int FMT = MX_E4M3;   // element format (instruction format code)
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
+};
+struct E5m2Op : Mxfp8Op {
+    static constexpr int FMT = MX_E5M2;
 };
 
 template <class Op, int BM, int BN, int STAGES>
@@ -323,9 +327,9 @@ void gemm_fast(GemmArgs p, int group_m)
 #pragma unroll
                     for (int j = 0; j < G::TJ; ++j) {
                         if (ks == 0)
-                            acc[i][j] = mfma_mxfp8<0>(fb[j], fa[i], acc[i][j], sb[j], sa[i]);
+                            acc[i][j] = mfma_mx<Op::FMT, 0>(fb[j], fa[i], acc[i][j], sb[j], sa[i]);
                         else
-                            acc[i][j] = mfma_mxfp8<2>(fb[j], fa[i], acc[i][j], sb[j], sa[i]);
+                            acc[i][j] = mfma_mx<Op::FMT, 2>(fb[j], fa[i], acc[i][j], sb[j], sa[i]);
                     }
             }
         }
@@ -411,6 +415,7 @@ struct Bf16Ring {                     // 64-byte rows
 };
 struct Mxfp8Ring {                    // 64-byte rows
     static constexpr bool MX = true, SG = false;
+    static constexpr int FMT = MX_E4M3;
     static constexpr int ELT = 1;
     static constexpr int BK = 64;
     static constexpr int NKS = 1;     // one 32x32x64 k-step per K tile
@@ -495,6 +500,7 @@ struct Bf16Ring64 {                   // 128-byte rows
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
     static constexpr bool MX = true, SG = false;
+    static constexpr int FMT = MX_E4M3;
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
     static constexpr int NKS = 2;
@@ -508,6 +514,17 @@ struct Mxfp8Ring128 {                 // 128-byte rows
 struct Mxfp8Ring128G : Mxfp8Ring128 {
     static constexpr bool SG = true;
     static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2;
+};
+// E5M2 elements have E4M3's byte layout and fragment map: the same kernels
+// with the instruction's format code 1.
+struct E5m2Ring : Mxfp8Ring {
+    static constexpr int FMT = MX_E5M2;
+};
+struct E5m2Ring128 : Mxfp8Ring128 {
+    static constexpr int FMT = MX_E5M2;
+};
+struct E5m2Ring128G : Mxfp8Ring128G {
+    static constexpr int FMT = MX_E5M2;
 };
 
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
@@ -743,9 +760,9 @@ void gemm_early(GemmArgs p, int group_m)
             if constexpr (!Op::MX)
                 acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
             else if (ks == 0)
-                acc[i][j] = mfma_mxfp8<0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+                acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
             else
-                acc[i][j] = mfma_mxfp8<2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+                acc[i][j] = mfma_mx<Op::FMT, 2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
         }
     };
 
@@ -1145,7 +1162,7 @@ void gemm_pingpong(GemmArgs p, int group_m)
                         if constexpr (!Op::MX)
                             acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
                         else
-                            acc[i][j] = mfma_mxfp8<0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+                            acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
                     }
             __builtin_amdgcn_s_setprio(0);
             barrier();
@@ -1290,26 +1307,39 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
     }
 }
 
-hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s)
+namespace {
+
+// Levels 5-7 for one 8-bit element format: Op (the older ring), Ring (64-byte
+// rows, level 7), Ring128 / Ring128G (gemm_early without / with scale groups).
+template <class Op, class Ring, class Ring128, class Ring128G>
+hipError_t launch_fast_mx8(int level, const GemmArgs &p, hipStream_t s)
 {
-    const bool ring_ok = p.K > Mxfp8Ring128::BK && p.K % Mxfp8Ring128::BK == 0;   // whole K tiles
+    const bool ring_ok = p.K > Ring128::BK && p.K % Ring128::BK == 0;   // whole K tiles
     // whole groups of 16 scale blocks, 16-byte aligned scale rows
     const bool groups = p.K % 512 == 0 && p.ld_sa % 16 == 0 && p.ld_sb % 16 == 0 &&
                         (uintptr_t)p.SA % 16 == 0 && (uintptr_t)p.SB % 16 == 0;
     switch (level) {
     case 5:
         if (ring_ok && groups)
-            return launch_early<Mxfp8Ring128G, 256, 256, false>(p, s);
-        return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, false>(p, s)
-                       : launch<Mxfp8Op, 256, 256, 2, false>(p, s);
+            return launch_early<Ring128G, 256, 256, false>(p, s);
+        return ring_ok ? launch_early<Ring128, 256, 256, false>(p, s) : launch<Op, 256, 256, 2, false>(p, s);
     case 6:
         if (ring_ok && groups)
-            return launch_early<Mxfp8Ring128G, 256, 256, true>(p, s);
-        return ring_ok ? launch_early<Mxfp8Ring128, 256, 256, true>(p, s)
-                       : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
+            return launch_early<Ring128G, 256, 256, true>(p, s);
+        return ring_ok ? launch_early<Ring128, 256, 256, true>(p, s) : launch<Op, 256, 256, 2, true>(p, s);
     case 7:
-        return p.K > 3 * Mxfp8Ring::BK ? launch_pingpong<Mxfp8Ring, true>(p, s)
-                                       : launch<Mxfp8Op, 256, 256, 2, true>(p, s);
+        return p.K > 3 * Ring::BK ? launch_pingpong<Ring, true>(p, s) : launch<Op, 256, 256, 2, true>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace
+
+hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s)
+{
+    switch (p.mx_fmt) {
+    case MX_E4M3: return launch_fast_mx8<Mxfp8Op, Mxfp8Ring, Mxfp8Ring128, Mxfp8Ring128G>(level, p, s);
+    case MX_E5M2: return launch_fast_mx8<E5m2Op, E5m2Ring, E5m2Ring128, E5m2Ring128G>(level, p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -8,8 +8,9 @@
 //   level 3: a grid of workgroups over M and N          -- spatial tiling
 //
 // The same kernel body serves the three levels; the host restricts the
-// problem and the grid for levels 1 and 2.  An MX block-scaled fp8 variant
-// (level 3 only) uses the same structure with 64-byte K tiles.
+// problem and the grid for levels 1 and 2.  A block-scaled MX variant (level
+// 3 only, any MX element format) uses the same structure with K tiles of 64
+// elements.
 //
 // Workgroup: 256 threads = 4 waves in a 2x2 arrangement, each wave owning a
 // 64x64 sub-tile = 2x2 blocks of the 32x32 matrix-core instruction.
@@ -113,26 +114,36 @@ __global__ __launch_bounds__(256) void gemm_simple_bf16(GemmArgs p)
             }
 }
 
-// ---------------------------------------------------------------- MX fp8
+// ---------------------------------------------------------------- MX
 //
-// K tile of 64 E4M3 bytes = two 32-element scale blocks = one
-// 32x32x64 block-scaled instruction per (i, j) per K tile.
+// K tile of 64 elements = two 32-element scale blocks = one 32x32x64
+// block-scaled instruction per (i, j) per K tile.  Both operands are
+// K-contiguous; a K tile of a row is 64 * bits / 8 bytes (64, 48 or 32),
+// copied byte by byte into an LDS row of that length plus 16 bytes of
+// padding.  Bytes past K are zero (for the packed formats K fills whole
+// bytes, so no element past K shares a byte with one inside).
 constexpr int MX_BK = 64;
-constexpr int MX_ROW = MX_BK + 16;   // bytes per LDS row (80 B)
 
-__device__ __forceinline__ void load_tile_fp8(const uint8_t *g, int ld, int rows, int K, int row0,
-                                              int k0, uint8_t *lds)
+template <int FMT>
+struct MxTile {
+    static constexpr int BYTES = MX_BK * mx_bits(FMT) / 8;   // K-tile bytes per row
+    static constexpr int ROW = BYTES + 16;                   // LDS row pitch
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_tile_mx(const uint8_t *g, int64_t ld_bytes, int rows,
+                                             int64_t k_bytes, int row0, int64_t kb0, uint8_t *lds)
 {
+    using T = MxTile<FMT>;
     const int tid = threadIdx.x;
-#pragma unroll 4
-    for (int e = 0; e < (BM * MX_BK) / 256; ++e) {
-        int idx = tid + 256 * e;
-        int r = idx / MX_BK, k = idx % MX_BK;
-        int gr = row0 + r, gk = k0 + k;
+    for (int idx = tid; idx < BM * T::BYTES; idx += 256) {
+        const int r = idx / T::BYTES, b = idx % T::BYTES;
+        const int gr = row0 + r;
+        const int64_t gb = kb0 + b;
         uint8_t v = 0;
-        if (gr < rows && gk < K)
-            v = g[(size_t)gr * ld + gk];
-        lds[r * MX_ROW + k] = v;
+        if (gr < rows && gb < k_bytes)
+            v = g[(size_t)gr * ld_bytes + gb];
+        lds[r * T::ROW + b] = v;
     }
 }
 
@@ -145,10 +156,30 @@ __device__ __forceinline__ int scale_byte(const uint8_t *s, int ld, int rows, in
     return 127;
 }
 
-__global__ __launch_bounds__(256) void gemm_simple_mxfp8(GemmArgs p)
+// A lane's fragment of one row of the K tile (see the map in common.hpp):
+// 8-bit formats two 16-byte halves (k 16h.. and 32+16h..), the packed
+// formats the whole block h (k 32h .. 32h + 31) from its first bit.
+template <int FMT>
+__device__ __forceinline__ intx8 mx_fragment(const uint8_t *row, int h)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t As[BM * MX_ROW];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * MX_ROW];
+    if constexpr (mx_bits(FMT) == 8) {
+        const intx4 lo = *(const intx4 *)(row + 16 * h), hi = *(const intx4 *)(row + 32 + 16 * h);
+        return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else if constexpr (mx_bits(FMT) == 6) {
+        const int *w = (const int *)(row + 24 * h);   // 8-byte aligned: rows are 64-byte pitched
+        return intx8{w[0], w[1], w[2], w[3], w[4], w[5], 0, 0};
+    } else {
+        const intx4 v = *(const intx4 *)(row + 16 * h);
+        return intx8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm_simple_mx(GemmArgs p)
+{
+    using T = MxTile<FMT>;
+    __shared__ __attribute__((aligned(16))) uint8_t As[BM * T::ROW];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * T::ROW];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -158,6 +189,9 @@ __global__ __launch_bounds__(256) void gemm_simple_mxfp8(GemmArgs p)
     const uint8_t *A = (const uint8_t *)p.A;
     const uint8_t *B = (const uint8_t *)p.B;
     const int nblk = (p.K + 31) / 32;
+    constexpr int BITS = mx_bits(FMT);
+    const int64_t lda_b = (int64_t)p.lda * BITS / 8, ldb_b = (int64_t)p.ldb * BITS / 8;
+    const int64_t k_bytes = (int64_t)p.K * BITS / 8;
 
     floatx16 acc[2][2];
 #pragma unroll
@@ -168,34 +202,30 @@ __global__ __launch_bounds__(256) void gemm_simple_mxfp8(GemmArgs p)
 
     const int ktiles = (p.K + MX_BK - 1) / MX_BK;
     for (int kt = 0; kt < ktiles; ++kt) {
-        const int k0 = kt * MX_BK;
-        load_tile_fp8(A, p.lda, p.M, p.K, m0, k0, As);
-        load_tile_fp8(B, p.ldb, p.N, p.K, n0, k0, Bs);
+        const int64_t kb0 = (int64_t)kt * T::BYTES;
+        load_tile_mx<FMT>(A, lda_b, p.M, k_bytes, m0, kb0, As);
+        load_tile_mx<FMT>(B, ldb_b, p.N, k_bytes, n0, kb0, Bs);
         __syncthreads();
-        const int kb = k0 / 32 + (lane >> 5);
+        const int kb = kt * (MX_BK / 32) + (lane >> 5);
         intx8 fa[2], fb[2];
         int sa[2], sb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int r = wm * 64 + i * 32 + (lane & 31);
-            const uint8_t *row = &As[r * MX_ROW + 16 * (lane >> 5)];
-            intx4 lo = *(const intx4 *)row, hi = *(const intx4 *)(row + 32);
-            fa[i] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            fa[i] = mx_fragment<FMT>(&As[r * T::ROW], lane >> 5);
             sa[i] = scale_byte(p.SA, p.ld_sa, p.M, nblk, m0 + r, kb);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             int c = wn * 64 + j * 32 + (lane & 31);
-            const uint8_t *row = &Bs[c * MX_ROW + 16 * (lane >> 5)];
-            intx4 lo = *(const intx4 *)row, hi = *(const intx4 *)(row + 32);
-            fb[j] = intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            fb[j] = mx_fragment<FMT>(&Bs[c * T::ROW], lane >> 5);
             sb[j] = scale_byte(p.SB, p.ld_sb, p.N, nblk, n0 + c, kb);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                acc[i][j] = mfma_mxfp8<0>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
+                acc[i][j] = mfma_mx<FMT, 0>(fa[i], fb[j], acc[i][j], sa[i], sb[j]);
         __syncthreads();
     }
 
@@ -246,10 +276,17 @@ hipError_t launch_simple_bf16(int level, const GemmArgs &p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_simple_mxfp8(const GemmArgs &p, hipStream_t s)
+hipError_t launch_simple_mx(const GemmArgs &p, hipStream_t s)
 {
     dim3 grid(((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM));
-    hipLaunchKernelGGL(gemm_simple_mxfp8, grid, dim3(256), 0, s, p);
+    switch (p.mx_fmt) {
+    case MX_E4M3: hipLaunchKernelGGL(gemm_simple_mx<MX_E4M3>, grid, dim3(256), 0, s, p); break;
+    case MX_E5M2: hipLaunchKernelGGL(gemm_simple_mx<MX_E5M2>, grid, dim3(256), 0, s, p); break;
+    case MX_E2M3: hipLaunchKernelGGL(gemm_simple_mx<MX_E2M3>, grid, dim3(256), 0, s, p); break;
+    case MX_E3M2: hipLaunchKernelGGL(gemm_simple_mx<MX_E3M2>, grid, dim3(256), 0, s, p); break;
+    case MX_E2M1: hipLaunchKernelGGL(gemm_simple_mx<MX_E2M1>, grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -9,16 +9,17 @@ namespace mce {
 
 // Levels 1-3 (bf16): generic synchronous copies; level selects the grid.
 hipError_t launch_simple_bf16(int level, const GemmArgs &p, hipStream_t s);
-// Level 3 (MX fp8): generic synchronous copies, K-contiguous operands.
-hipError_t launch_simple_mxfp8(const GemmArgs &p, hipStream_t s);
+// Level 3 (MX, any element format): generic synchronous copies, K-contiguous
+// operands.
+hipError_t launch_simple_mx(const GemmArgs &p, hipStream_t s);
 // C <- beta * C (alpha == 0 or K == 0).
 hipError_t launch_scale_c(const GemmArgs &p, hipStream_t s);
 
 // Levels 4-7 (bf16): direct global->LDS loads of K-contiguous operands.
 // Returns hipErrorInvalidValue if the level has no kernel.
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s);
-// Levels 5-6 (MX fp8).
-hipError_t launch_fast_mxfp8(int level, const GemmArgs &p, hipStream_t s);
+// Levels 5-7 (MX E4M3 and E5M2; p.mx_fmt): direct loads, as for bf16.
+hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s);
 // Levels 5-6 (bf16) for operands the direct-load kernels cannot take: any
 // layout, alignment and K, through registers.
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);

@@ -4,10 +4,13 @@ import numpy as np
 import torch
 
 import matrix_core_engineering_amd as mce
-from matrix_core_engineering_amd.inputs import BF16, OUT_BF16
+from matrix_core_engineering_amd.inputs import BF16, E2M1, E2M3, E3M2, E4M3FN, E5M2, OUT_BF16
 from helpers import bf16_bits_to_f64, f64_to_bf16_bits
 
 DEV = torch.device("cuda:0")
+# generator format -> the library's element format code
+MCE_FORMAT = {E4M3FN: mce.MCE_MX_E4M3, E5M2: mce.MCE_MX_E5M2, E2M3: mce.MCE_MX_E2M3,
+              E3M2: mce.MCE_MX_E3M2, E2M1: mce.MCE_MX_E2M1}
 GUARD_ROWS = 3
 SENTINEL_F32 = 0x7F8ABCDE    # bit patterns no kernel writes
 SENTINEL_BF16 = 0x7F8B
@@ -67,9 +70,14 @@ class DeviceProblem:
         args = (p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.SA, p.ld_sa, self.B, p.ldb,
                 p.b_col_major, self.SB, p.ld_sb, self.c_ptr, p.ldc, p.c_col_major, p.c_dtype,
                 p.alpha, p.beta)
+        if p.fmt == E4M3FN:
+            if level is None:
+                return mce.gemm_mxfp8(*args, raise_on_error=raise_on_error)
+            return mce.gemm_mxfp8_level(level, *args, raise_on_error=raise_on_error)
+        fmt = MCE_FORMAT[p.fmt]
         if level is None:
-            return mce.gemm_mxfp8(*args, raise_on_error=raise_on_error)
-        return mce.gemm_mxfp8_level(level, *args, raise_on_error=raise_on_error)
+            return mce.gemm_mx(fmt, *args, raise_on_error=raise_on_error)
+        return mce.gemm_mx_level(level, fmt, *args, raise_on_error=raise_on_error)
 
     def result(self):
         """(logical M x N float64 result, raw logical storage, guards intact)."""

@@ -93,3 +93,39 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mce, "lib_path", lambda: str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         mce.load()
+
+
+def mx_call(fmt, M=64, N=64, K=64, lda=None, ldb=None, A=0x1000, B=0x9000, level=None):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    args = (M, N, K, A, lda, 0, 0x20000, 2, B, ldb, 1, 0x30000, 2, 0x40000, N, 0, 0, 1.0, 0.0, 0)
+    if level is None:
+        return mce.load().gemm_mx(fmt, *args)
+    return mce.load().gemm_mx_level(level, fmt, *args)
+
+
+def test_mx_unknown_format_is_einval():
+    for fmt in (-1, 5, 99):
+        assert mx_call(fmt) == mce.MCE_EINVAL
+        assert mce.gemm_mx_pick_level(fmt, 64, 64, 64, 0x1000, 64, 0, 0x9000, 64, 1) == 0
+
+
+@pytest.mark.parametrize("fmt,unit", [(mce.MCE_MX_E2M3, 4), (mce.MCE_MX_E3M2, 4), (mce.MCE_MX_E2M1, 2)])
+def test_mx_packed_formats_need_whole_bytes(fmt, unit):
+    """K and the leading dimensions of the packed formats must fill whole
+    bytes (multiples of 4 elements for 6 bits, 2 for 4 bits)."""
+    assert mx_call(fmt, K=64 + unit - 1 if unit > 1 else 63, lda=68, ldb=68) == mce.MCE_EINVAL
+    assert mx_call(fmt, K=64, lda=64 + 1, ldb=64) == mce.MCE_EINVAL
+    assert mx_call(fmt, K=64, lda=64, ldb=64 + 1) == mce.MCE_EINVAL
+
+
+def test_mx_pick_level_by_format():
+    """8-bit formats pick the pipelined level when the operands allow it;
+    the packed formats run level 3."""
+    for fmt in (mce.MCE_MX_E4M3, mce.MCE_MX_E5M2):
+        assert mce.gemm_mx_pick_level(fmt, 8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) == 6
+    for fmt in (mce.MCE_MX_E2M3, mce.MCE_MX_E3M2, mce.MCE_MX_E2M1):
+        assert mce.gemm_mx_pick_level(fmt, 8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) == 3
+    assert mce.gemm_mx_pick_level(mce.MCE_MX_E5M2, 64, 64, 64, 0x1000, 64, 1, 0x9000, 64, 1) == 0
+    assert (mce.gemm_mxfp8_pick_level(8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) ==
+            mce.gemm_mx_pick_level(mce.MCE_MX_E4M3, 8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1))

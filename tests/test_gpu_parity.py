@@ -19,7 +19,8 @@ import torch
 
 import matrix_core_engineering_amd as mce
 import oracle
-from matrix_core_engineering_amd.inputs import (BF16, CONFIGS, E4M3FN, OUT_BF16, OUT_F32,
+from matrix_core_engineering_amd.inputs import (BF16, CONFIGS, E2M1, E2M3, E3M2, E4M3FN, E5M2,
+                                                OUT_BF16, OUT_F32,
                                                 config_problem, integer_problem,
                                                 make_problem)
 from helpers import oracle_entries, oracle_full, torch_decode_elements, logical
@@ -229,6 +230,91 @@ def test_mx_small_integer_bitwise(level, shape):
         r = run_level(p, level)
         if r is not None:
             assert_bitwise(p, r[1])
+
+
+# ---------------------------------------- the other MX element formats
+
+OTHER_MX = [E5M2, E2M3, E3M2, E2M1]
+OTHER_MX_IDS = ["e5m2", "e2m3", "e3m2", "e2m1"]
+# K a multiple of 4 (whole bytes for the packed formats); ragged M, N, K
+MXF_SHAPES = [(1, 1, 32), (5, 3, 40), (128, 128, 64), (127, 129, 100), (64, 96, 132),
+              (200, 150, 512), (33, 65, 1000)]
+
+
+def mx_format_accepts(fmt, level, p):
+    """Levels 5-7 exist for the 8-bit formats only, and need K-contiguous,
+    16-byte aligned rows (lda, ldb, K multiples of 16) and 4-byte scale rows."""
+    if level in (None, 3):
+        return True
+    if fmt != E5M2:
+        return False
+    return p.lda % 16 == 0 and p.ldb % 16 == 0 and p.K % 16 == 0 and p.ld_sa % 4 == 0 and p.ld_sb % 4 == 0
+
+
+def run_mx_format(p, level):
+    r = run_level(p, level)
+    if mx_format_accepts(p.fmt, level, p):
+        assert r is not None, f"level {level} declined a problem it documents"
+    else:
+        assert r is None, f"level {level} ran a problem it documents as unsupported"
+    return r
+
+
+@pytest.mark.parametrize("level", [3, 5, 6, 7, None])
+@pytest.mark.parametrize("shape", MXF_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("fmt", OTHER_MX, ids=OTHER_MX_IDS)
+def test_mx_formats_integer_bitwise(fmt, shape, level):
+    """Integer elements -4..4, scale exponents 0..2: every partial sum is
+    exact, so each format's result must equal the oracle bitwise."""
+    M, N, K = shape
+    for out in (OUT_F32, OUT_BF16):
+        p = make_problem(M, N, K, fmt=fmt, a_col_major=False, b_col_major=True, c_dtype=out,
+                         dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2,
+                         ld_sa=4 * ((K + 127) // 128), ld_sb=4 * ((K + 127) // 128),
+                         seed=8000 + K + out + 10 * fmt)
+        r = run_mx_format(p, level)
+        if r is not None:
+            assert_bitwise(p, r[1])
+
+
+@pytest.mark.parametrize("level", [3, 6, None])
+@pytest.mark.parametrize("shape", [(127, 129, 100), (200, 150, 512), (33, 65, 1000)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("fmt", OTHER_MX, ids=OTHER_MX_IDS)
+def test_mx_formats_random_within_bound(fmt, shape, level):
+    """Every code of the format equally likely (E5M2: U[-4096, 4096] rounded),
+    scale exponents -8..8, alpha/beta update of the output."""
+    M, N, K = shape
+    kw = dict(dist="uniform", lo=-4096.0, hi=4096.0) if fmt == E5M2 else dict(dist="codes")
+    for out in (OUT_F32, OUT_BF16):
+        p = make_problem(M, N, K, fmt=fmt, a_col_major=False, b_col_major=True, c_dtype=out,
+                         alpha=0.75, beta=-0.5, ld_sa=4 * ((K + 127) // 128),
+                         ld_sb=4 * ((K + 127) // 128), seed=8500 + K + out + 10 * fmt, **kw)
+        r = run_mx_format(p, level)
+        if r is not None:
+            assert_close(p, r[0])
+
+
+@pytest.mark.parametrize("level", [5, 6, 7, None])
+def test_e5m2_large_groups_integer_exact(level):
+    """E5M2 through the pipelined kernels at a ragged large shape with whole
+    scale groups (K a multiple of 512, 16-byte scale rows)."""
+    M, N, K = 4100, 8200, 1536
+    p = make_problem(M, N, K, fmt=E5M2, c_dtype=OUT_F32, dist="int", lo=-4, hi=4,
+                     scale_exp_lo=0, scale_exp_hi=2, ld_sa=48, ld_sb=48, seed=8900 + (level or 0),
+                     name="large_e5m2_int")
+    r = run_mx_format(p, level)
+    vals = r[0]
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    from helpers import torch_decode_scales
+    A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+    B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    assert np.array_equal(vals.sum(axis=1), A @ B.sum(axis=1))
+    assert np.array_equal(vals.sum(axis=0), A.sum(axis=0) @ B)
+    ii, jj = sample_indices(M, N, 1000, 74)
+    cref, _ = oracle_entries(p, ii, jj)
+    assert np.array_equal(vals[ii, jj], cref)
 
 
 @pytest.mark.parametrize("level", MX_LEVELS)
