@@ -160,8 +160,10 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K,
  * section A1 case 2: block-scaled MMA; the pages name no element format.)
  *
  * Levels: 3 for every format; 5-7 for E4M3 and E5M2 under the rules of
- * gemm_mxfp8_level; the 6- and 4-bit formats run level 3 (other levels
- * return MCE_EUNSUPPORTED).
+ * gemm_mxfp8_level; 5-6 for E2M1 when lda and ldb are multiples of 32, K a
+ * multiple of 512, A, B, SA and SB 16-byte aligned and ld_sa, ld_sb
+ * multiples of 16; the 6-bit formats run level 3 only (other levels return
+ * MCE_EUNSUPPORTED).
  */
 int gemm_mx(int elem_format, int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda, int a_col_major,

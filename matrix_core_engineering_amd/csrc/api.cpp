@@ -100,6 +100,17 @@ bool fast_eligible(const Call &c)
            (c.K % per_chunk) == 0 && ((uintptr_t)c.A % 16) == 0 && ((uintptr_t)c.B % 16) == 0;
 }
 
+// FP4 levels 5-6: K-contiguous 16-byte aligned rows (lda, ldb multiples of
+// 32 elements), K a multiple of 512 and scale rows in whole, aligned
+// 16-byte groups.
+bool fp4_fast_eligible(const Call &c)
+{
+    return c.fmt == FMT_MX && c.mx_fmt == MCE_MX_E2M1 && c.a_cm == 0 && c.b_cm == 1 &&
+           c.K % 512 == 0 && c.lda % 32 == 0 && c.ldb % 32 == 0 && c.ld_sa % 16 == 0 &&
+           c.ld_sb % 16 == 0 && ((uintptr_t)c.A % 16) == 0 && ((uintptr_t)c.B % 16) == 0 &&
+           ((uintptr_t)c.SA % 16) == 0 && ((uintptr_t)c.SB % 16) == 0;
+}
+
 bool mx_scales_eligible(const Call &c)
 {
     // the pipelined MX kernels read four scale bytes per 32-bit load
@@ -115,6 +126,8 @@ int pick_level(const Call &c)
     if (c.fmt == FMT_BF16)   // levels 5-6 take any bf16 problem
         return kBestBf16Level;
     if (kBestMxLevel >= 5 && fast_eligible(c) && mx_scales_eligible(c))
+        return kBestMxLevel;
+    if (fp4_fast_eligible(c))
         return kBestMxLevel;
     return 3;
 }
@@ -133,7 +146,8 @@ bool level_accepts(const Call &c, int level)
     }
     switch (level) {
     case 3: return true;
-    case 5: case 6: case 7: return fast_eligible(c) && mx_scales_eligible(c);   // 8-bit formats
+    case 5: case 6: return (fast_eligible(c) && mx_scales_eligible(c)) || fp4_fast_eligible(c);
+    case 7: return fast_eligible(c) && mx_scales_eligible(c);   // 8-bit formats
     default: return false;
     }
 }

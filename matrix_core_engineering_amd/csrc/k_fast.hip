@@ -492,14 +492,16 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // instruction order needs A fragment i only from the (TJ*i)-th instruction
 // on).
 struct Bf16Ring64 {                   // 128-byte rows
-    static constexpr bool MX = false, SG = false;
+    static constexpr bool MX = false, SG = false, FP4 = false;
+    static constexpr int EPU = 1;     // elements per K unit (FP4: two per byte)
     static constexpr int ELT = 2;
     static constexpr int BK = 64;
     static constexpr int NKS = 4;
     static constexpr int KA = 1, XM = 32, LX = 16, LY = 0, YA = 2;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
-    static constexpr bool MX = true, SG = false;
+    static constexpr bool MX = true, SG = false, FP4 = false;
+    static constexpr int EPU = 1;
     static constexpr int FMT = MX_E4M3;
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
@@ -526,6 +528,22 @@ struct E5m2Ring128 : Mxfp8Ring128 {
 struct E5m2Ring128G : Mxfp8Ring128G {
     static constexpr int FMT = MX_E5M2;
 };
+// FP4 (E2M1), two elements per byte.  The kernel runs in byte units (the
+// host passes K, lda and ldb halved), so the loads are those of E4M3: a K
+// tile is 128 bytes of a row = 256 elements = 8 scale blocks.  A lane's
+// fragment of a k-step (64 elements, 32 bytes of the row) is the 16 bytes of
+// its block, logical chunk 2ks + h, as for bf16; four k-steps per K tile;
+// two scale words per row and K tile, a scale group (16 bytes per row)
+// covers two K tiles.
+struct Fp4Ring128G {
+    static constexpr bool MX = true, SG = true, FP4 = true;
+    static constexpr int EPU = 2;
+    static constexpr int FMT = MX_E2M1;
+    static constexpr int ELT = 1;
+    static constexpr int BK = 128;    // K units (bytes) per K tile
+    static constexpr int NKS = 4;
+    static constexpr int KA = 1, XM = 32, LX = 16, LY = 0, YA = 2;
+};
 
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -534,7 +552,10 @@ void gemm_early(GemmArgs p, int group_m)
     using G = RingGeometry<Op, BM, BN, 2>;
     constexpr int NKS = Op::NKS;
     constexpr int NM = G::TI * G::TJ;                      // matrix-core instructions per k-step
-    constexpr int RPF = Op::MX ? 2 : 1;                    // LDS reads per fragment
+    constexpr int RPF = Op::MX && !Op::FP4 ? 2 : 1;       // LDS reads per fragment
+    constexpr int BPK = Op::BK * Op::EPU / 32;             // scale blocks per K tile
+    constexpr int GK = 16 / BPK;                           // K tiles per scale group
+    constexpr int SW = BPK / 4;                            // scale words per row and K tile
     constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
     constexpr int KA = Op::KA, AM = KA * NM;                // phase A
     constexpr int XM = Op::XM, YM = (NKS - KA) * NM - XM;  // phases X and Y
@@ -565,7 +586,7 @@ void gemm_early(GemmArgs p, int group_m)
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
     const int total = my_tiles * nk;
 
-    const int nblk = (p.K + 31) / 32;                      // MX scale blocks per row
+    const int nblk = (p.K * Op::EPU + 31) / 32;            // MX scale blocks per row
 
     auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
 
@@ -656,20 +677,20 @@ void gemm_early(GemmArgs p, int group_m)
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sa, t.nsa);
                 const uint32_t voff = vsa;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sbase + wave * 256), 4, voff,
-                                                         kt * (Op::BK / 32), 0, 0);
+                                                         kt * BPK, 0, 0);
             } else {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.sb, t.nsb);
                 const uint32_t voff = vsb;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sbase + G::SA_BYTES + wave * 256),
-                                                         4, voff, kt * (Op::BK / 32), 0, 0);
+                                                         4, voff, kt * BPK, 0, 0);
             }
         }
     };
 
     typedef typename std::conditional<Op::MX, intx8, bf16x8>::type Frag;
     Frag fa[NKS][G::TI], fb[NKS][G::TJ];   // one register set per k-step of a K tile
-    int sc_a[G::TI], sc_b[G::TJ];          // MX scale words of the K tile being consumed
-    int sn_a[G::TI], sn_b[G::TJ];          // ... of the next K tile
+    int sc_a[G::TI][SW], sc_b[G::TJ][SW];  // MX scale words of the K tile being consumed
+    int sn_a[G::TI][SW], sn_b[G::TJ][SW];  // ... of the next K tile
     // rows a lane reads differ by multiples of 32: the swizzle is lane-constant
     const int swz_lane = swz8(l32);
 
@@ -677,6 +698,11 @@ void gemm_early(GemmArgs p, int group_m)
     auto frag = [&](const char *rowp, int ks) -> Frag {
         if constexpr (!Op::MX) {
             return *(const bf16x8 *)(rowp + ((2 * ks + h) ^ swz_lane) * 16);
+        } else if constexpr (Op::FP4) {
+            // lane (l32, h): block 2ks + h = elements 64ks + 32h .. +31; the
+            // instruction reads four registers, the rest stay undefined
+            const intx4 v = *(const intx4 *)(rowp + ((2 * ks + h) ^ swz_lane) * 16);
+            return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
         } else {
             // lane (l32, h): k = 64ks + 16h .. +15 and 64ks + 32 + 16h .. +15
             intx4 lo = *(const intx4 *)(rowp + ((4 * ks + h) ^ swz_lane) * 16);
@@ -700,16 +726,32 @@ void gemm_early(GemmArgs p, int group_m)
     // buffer (gk / 4) % 2, gk counting K tiles over the workgroup's tiles,
     // and every block is valid (K is a multiple of 512).
     auto read_scales = [&](int stage, int kt, int gk) {
-        if constexpr (Op::MX && Op::SG) {
+        if constexpr (Op::MX && Op::SG && Op::FP4) {
+            // two words (8 blocks) of group buffer (gk / 2) % 2 at word 2 (gk % 2)
+            const uint2 *SAs = (const uint2 *)(smem + G::LDS_BYTES + ((gk >> 1) & 1) * (BM + BN) * 16) + (gk & 1);
+            const uint2 *SBs = SAs + BM * 2;
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i) {
+                const uint2 w = SAs[(wm * G::WM + i * 32 + l32) * 2];
+                sn_a[i][0] = (int)(w.x >> (8 * h));
+                sn_a[i][SW - 1] = (int)(w.y >> (8 * h));
+            }
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j) {
+                const uint2 w = SBs[(wn * G::WN + j * 32 + l32) * 2];
+                sn_b[j][0] = (int)(w.x >> (8 * h));
+                sn_b[j][SW - 1] = (int)(w.y >> (8 * h));
+            }
+        } else if constexpr (Op::MX && Op::SG) {
             const uint32_t *SAs =
                 (const uint32_t *)(smem + G::LDS_BYTES + ((gk >> 2) & 1) * (BM + BN) * 16) + (gk & 3);
             const uint32_t *SBs = SAs + BM * 4;
 #pragma unroll
             for (int i = 0; i < G::TI; ++i)
-                sn_a[i] = (int)(SAs[(wm * G::WM + i * 32 + l32) * 4] >> (8 * h));
+                sn_a[i][0] = (int)(SAs[(wm * G::WM + i * 32 + l32) * 4] >> (8 * h));
 #pragma unroll
             for (int j = 0; j < G::TJ; ++j)
-                sn_b[j] = (int)(SBs[(wn * G::WN + j * 32 + l32) * 4] >> (8 * h));
+                sn_b[j][0] = (int)(SBs[(wn * G::WN + j * 32 + l32) * 4] >> (8 * h));
         } else if constexpr (Op::MX) {
             const uint32_t *SAs =
                 (const uint32_t *)(smem + stage * G::STAGE_BYTES + G::A_BYTES + G::B_BYTES);
@@ -722,10 +764,10 @@ void gemm_early(GemmArgs p, int group_m)
             }
 #pragma unroll
             for (int i = 0; i < G::TI; ++i)
-                sn_a[i] = (int)(((SAs[wm * G::WM + i * 32 + l32] & keep) | force) >> (8 * h));
+                sn_a[i][0] = (int)(((SAs[wm * G::WM + i * 32 + l32] & keep) | force) >> (8 * h));
 #pragma unroll
             for (int j = 0; j < G::TJ; ++j)
-                sn_b[j] = (int)(((SBs[wn * G::WN + j * 32 + l32] & keep) | force) >> (8 * h));
+                sn_b[j][0] = (int)(((SBs[wn * G::WN + j * 32 + l32] & keep) | force) >> (8 * h));
         }
     };
 
@@ -744,7 +786,7 @@ void gemm_early(GemmArgs p, int group_m)
             char *gb = smem + G::LDS_BYTES + buf * (BM + BN) * 16;
             char *sink = smem + G::LDS_BYTES + 2 * (BM + BN) * 16;   // shared by every wave
             char *da = real ? gb + wave * 1024 : sink, *db = real ? gb + BM * 16 + wave * 1024 : sink;
-            const int soff = kt * (Op::BK / 32);
+            const int soff = kt * BPK;
             const uint32_t voa = vsa, vob = vsb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)da, 16, voa, soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)db, 16, vob, soff, 0, 0);
@@ -757,12 +799,17 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
         for (int q = lo; q < hi; ++q) {
             const int ks = q / NM, i = (q % NM) / G::TJ, j = q % G::TJ;
+            // MX: k-step ks takes blocks 2ks, 2ks+1 of the K tile: byte
+            // 2 (ks % 2) of scale word ks / 2 (the upper half-wave's words
+            // are shifted one byte down, so it supplies block 2ks + 1)
             if constexpr (!Op::MX)
                 acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
-            else if (ks == 0)
-                acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+            else if (ks % 2 == 0)
+                acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j][ks / 2],
+                                                sc_a[i][ks / 2]);
             else
-                acc[i][j] = mfma_mx<Op::FMT, 2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j], sc_a[i]);
+                acc[i][j] = mfma_mx<Op::FMT, 2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j][ks / 2],
+                                                sc_a[i][ks / 2]);
         }
     };
 
@@ -770,7 +817,7 @@ void gemm_early(GemmArgs p, int group_m)
     // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
     // issues (a direct load always writes LDS, so no placeholder load may
     // target a stage in use)
-    issue_group(false, 0, 0, true);                // scale group 0 (four K tiles)
+    issue_group(false, 0, 0, true);                // scale group 0 (GK K tiles)
     issue(0, G::LOADS, false, 0, 0);
     issue(0, LX + LY, false, 1, 1);
     wait_vmcnt<LX + LY>();                         // K tile 0 (and scale group 0) landed
@@ -783,11 +830,14 @@ void gemm_early(GemmArgs p, int group_m)
         read_b(0, 0, j);
     read_scales(0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < G::TI; ++i)
-        sc_a[i] = sn_a[i];
+    for (int w = 0; w < SW; ++w) {
 #pragma unroll
-    for (int j = 0; j < G::TJ; ++j)
-        sc_b[j] = sn_b[j];
+        for (int i = 0; i < G::TI; ++i)
+            sc_a[i][w] = sn_a[i][w];
+#pragma unroll
+        for (int j = 0; j < G::TJ; ++j)
+            sc_b[j][w] = sn_b[j][w];
+    }
 
     int g = 0;
     // the last LA loads of the K tile whose loads began last iteration
@@ -879,20 +929,24 @@ void gemm_early(GemmArgs p, int group_m)
             }
             if constexpr (Op::SG) {
                 // at a group's first K tile: the next group's scale words into
-                // the other group buffer, whose last reads (two groups back)
-                // ended before this iteration's barrier 1; they land long
-                // before their first reader, phase Y of iteration g+3 (other
+                // the other group buffer, whose last reads (a group back)
+                // ended before this iteration's barrier 1; the wait before
+                // barrier 2 of the next iteration covers them, ahead of
+                // their first reader, phase Y of iteration g + GK - 1 (other
                 // iterations issue the same loads into the sink)
-                const bool gnext = kt + 4 >= nk;
-                issue_group(gnext, gnext ? 0 : kt + 4, ((g >> 2) + 1) & 1, (g & 3) == 0);
+                const bool gnext = kt + GK >= nk;
+                issue_group(gnext, gnext ? 0 : kt + GK, ((g / GK) + 1) & 1, (g % GK) == 0);
             }
             if constexpr (Op::MX) {
 #pragma unroll
-                for (int i = 0; i < G::TI; ++i)
-                    sc_a[i] = sn_a[i];
+                for (int w = 0; w < SW; ++w) {
 #pragma unroll
-                for (int j = 0; j < G::TJ; ++j)
-                    sc_b[j] = sn_b[j];
+                    for (int i = 0; i < G::TI; ++i)
+                        sc_a[i][w] = sn_a[i][w];
+#pragma unroll
+                    for (int j = 0; j < G::TJ; ++j)
+                        sc_b[j][w] = sn_b[j][w];
+                }
             }
         }
         int tm, tn;
@@ -1335,9 +1389,28 @@ hipError_t launch_fast_mx8(int level, const GemmArgs &p, hipStream_t s)
 
 } // namespace
 
+// FP4: gemm_early in byte units, with whole scale groups (K a multiple of
+// 512 elements, 16-byte scale rows) and 16-byte aligned rows.
+hipError_t launch_fast_fp4(int level, const GemmArgs &p, hipStream_t s)
+{
+    if (p.K % 512 != 0 || p.lda % 32 != 0 || p.ldb % 32 != 0 || p.ld_sa % 16 != 0 ||
+        p.ld_sb % 16 != 0 || (uintptr_t)p.SA % 16 != 0 || (uintptr_t)p.SB % 16 != 0)
+        return hipErrorInvalidValue;
+    GemmArgs q = p;
+    q.K = p.K / 2;
+    q.lda = p.lda / 2;
+    q.ldb = p.ldb / 2;
+    switch (level) {
+    case 5: return launch_early<Fp4Ring128G, 256, 256, false>(q, s);
+    case 6: return launch_early<Fp4Ring128G, 256, 256, true>(q, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s)
 {
     switch (p.mx_fmt) {
+    case MX_E2M1: return launch_fast_fp4(level, p, s);
     case MX_E4M3: return launch_fast_mx8<Mxfp8Op, Mxfp8Ring, Mxfp8Ring128, Mxfp8Ring128G>(level, p, s);
     case MX_E5M2: return launch_fast_mx8<E5m2Op, E5m2Ring, E5m2Ring128, E5m2Ring128G>(level, p, s);
     default: return hipErrorInvalidValue;

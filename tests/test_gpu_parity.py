@@ -242,10 +242,15 @@ MXF_SHAPES = [(1, 1, 32), (5, 3, 40), (128, 128, 64), (127, 129, 100), (64, 96, 
 
 
 def mx_format_accepts(fmt, level, p):
-    """Levels 5-7 exist for the 8-bit formats only, and need K-contiguous,
-    16-byte aligned rows (lda, ldb, K multiples of 16) and 4-byte scale rows."""
+    """Levels 5-7 of E5M2 need K-contiguous, 16-byte aligned rows (lda, ldb,
+    K multiples of 16) and 4-byte scale rows; levels 5-6 of E2M1 need lda,
+    ldb multiples of 32, K a multiple of 512 and 16-byte scale rows; the
+    6-bit formats run level 3 only."""
     if level in (None, 3):
         return True
+    if fmt == E2M1:
+        return (level in (5, 6) and p.K % 512 == 0 and p.lda % 32 == 0 and p.ldb % 32 == 0 and
+                p.ld_sa % 16 == 0 and p.ld_sb % 16 == 0)
     if fmt != E5M2:
         return False
     return p.lda % 16 == 0 and p.ldb % 16 == 0 and p.K % 16 == 0 and p.ld_sa % 4 == 0 and p.ld_sb % 4 == 0
@@ -295,19 +300,23 @@ def test_mx_formats_random_within_bound(fmt, shape, level):
             assert_close(p, r[0])
 
 
-@pytest.mark.parametrize("level", [5, 6, 7, None])
-def test_e5m2_large_groups_integer_exact(level):
-    """E5M2 through the pipelined kernels at a ragged large shape with whole
-    scale groups (K a multiple of 512, 16-byte scale rows)."""
+@pytest.mark.parametrize("fmt,level", [(E5M2, 5), (E5M2, 6), (E5M2, 7), (E5M2, None),
+                                       (E2M1, 5), (E2M1, 6), (E2M1, None)],
+                         ids=["e5m2-5", "e5m2-6", "e5m2-7", "e5m2-default", "e2m1-5", "e2m1-6",
+                              "e2m1-default"])
+def test_mx_formats_large_groups_integer_exact(fmt, level):
+    """E5M2 and E2M1 through the pipelined kernels at a ragged large shape
+    with whole scale groups (K a multiple of 512, 16-byte scale rows): row
+    and column sums exact, sampled entries bitwise."""
     M, N, K = 4100, 8200, 1536
-    p = make_problem(M, N, K, fmt=E5M2, c_dtype=OUT_F32, dist="int", lo=-4, hi=4,
-                     scale_exp_lo=0, scale_exp_hi=2, ld_sa=48, ld_sb=48, seed=8900 + (level or 0),
-                     name="large_e5m2_int")
+    p = make_problem(M, N, K, fmt=fmt, c_dtype=OUT_F32, dist="int", lo=-4, hi=4,
+                     scale_exp_lo=0, scale_exp_hi=2, ld_sa=48, ld_sb=48,
+                     seed=8900 + (level or 0) + 10 * fmt, name="large_mx_format_int")
     r = run_mx_format(p, level)
     vals = r[0]
-    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
-    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
-    from helpers import torch_decode_scales
+    from helpers import decode_elements, torch_decode_scales
+    A = decode_elements(p, p.A, p.M, p.K, p.a_col_major, p.lda)
+    B = decode_elements(p, p.B, p.K, p.N, p.b_col_major, p.ldb)
     A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
     B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
     assert np.array_equal(vals.sum(axis=1), A @ B.sum(axis=1))
