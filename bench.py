@@ -15,9 +15,12 @@ dominant (longest) kernel, timed with HIP events on the stream it runs on;
 `cpu_baseline` times the fp64 oracle on a bounded row sample of the bf16
 GEMM on the host cores and checks those rows of the GPU result.
 
-Modes for profiling (no JSON): --only bf16|mxfp8|copy --reps R runs just
-that kernel R times after one warm-up (copy: a 1 GiB device-to-device copy,
-the calibration of the HBM byte counters).
+Modes for profiling (no JSON): --only bf16|mxfp8|copy|e4m3|e5m2|e2m3|e3m2|e2m1
+--reps R runs just that kernel R times after one warm-up (copy: a 1 GiB
+device-to-device copy, the calibration of the HBM byte counters; the MX
+element-format names: the 8192^3 MX GEMM in that format).
+--mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
+element format at its default level, with W warm-up and K timed launches.
 """
 import argparse
 import hashlib
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2516.6     # TFLOP/s dense: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_FP8 = 5033.2      # TFLOP/s dense: 256 CU x 8192 flop/clk x 2.4 GHz
+PEAK_FP4 = 10066.3     # TFLOP/s dense fp6 / fp4: 256 CU x 16384 flop/clk x 2.4 GHz
 PEAK_HBM = 8000.0      # GB/s
 METRIC = "GEMM TFLOP/s and % of dense MFMA peak (bf16, MX-fp8) at 8192³ on 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_8192.txt")
@@ -55,7 +59,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy"], default=None)
+    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy"] + list(MX_FORMAT_NAMES), default=None)
+    ap.add_argument("--mx-formats", action="store_true",
+                    help="time the 8192^3 MX GEMM in every element format (one JSON line)")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -100,6 +106,79 @@ class Workload:
                                             p.ldb, p.b_col_major)
         return mce.gemm_mxfp8_pick_level(p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.B,
                                          p.ldb, p.b_col_major)
+
+
+# MX element formats: name -> (generator format, library code, dense peak)
+MX_FORMAT_NAMES = ("e4m3", "e5m2", "e2m3", "e3m2", "e2m1")
+
+
+def mx_format_table():
+    import matrix_core_engineering_amd as mce
+    from matrix_core_engineering_amd.inputs import E2M1, E2M3, E3M2, E4M3FN, E5M2
+    return {"e4m3": (E4M3FN, mce.MCE_MX_E4M3, PEAK_FP8), "e5m2": (E5M2, mce.MCE_MX_E5M2, PEAK_FP8),
+            "e2m3": (E2M3, mce.MCE_MX_E2M3, PEAK_FP4), "e3m2": (E3M2, mce.MCE_MX_E3M2, PEAK_FP4),
+            "e2m1": (E2M1, mce.MCE_MX_E2M1, PEAK_FP4)}
+
+
+class MxFormatWorkload:
+    """The 8192^3 MX workload (A row-major, B column-major, one E8M0 scale
+    per 32 K with exponents -8..8, bf16 out) in one element format: 8-bit
+    codes from U[-448, 448], the packed formats every code equally likely."""
+
+    def __init__(self, name, dev):
+        import torch
+        from matrix_core_engineering_amd.inputs import E4M3FN, E5M2, OUT_BF16, make_problem
+        gfmt, self.code, self.peak = mx_format_table()[name]
+        kw = (dict(dist="uniform", lo=-448.0, hi=448.0) if gfmt in (E4M3FN, E5M2)
+              else dict(dist="codes"))
+        self.p = p = make_problem(8192, 8192, 8192, fmt=gfmt, a_col_major=False, b_col_major=True,
+                                  c_dtype=OUT_BF16, seed=5, name=f"mx_{name}_8192", **kw)
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self.A, self.B, self.SA, self.SB = up(p.A), up(p.B), up(p.SA), up(p.SB)
+        self.C = torch.zeros((p.M, p.ldc), dtype=torch.int16, device=dev)
+
+    def run(self, stream):
+        import matrix_core_engineering_amd as mce
+        p = self.p
+        return mce.gemm_mx(self.code, p.M, p.N, p.K, self.A, p.lda, 0, self.SA, p.ld_sa, self.B,
+                           p.ldb, 1, self.SB, p.ld_sb, self.C, p.ldc, 0, p.c_dtype, p.alpha,
+                           p.beta, stream=stream)
+
+    def level(self):
+        import matrix_core_engineering_amd as mce
+        p = self.p
+        return mce.gemm_mx_pick_level(self.code, p.M, p.N, p.K, self.A, p.lda, 0, self.SA, p.ld_sa,
+                                      self.B, p.ldb, 1, self.SB, p.ld_sb)
+
+
+def mx_formats(args, dev, stream):
+    """One JSON line: each element format's 8192^3 GEMM at its default level,
+    HIP events on the launch stream around each launch."""
+    import torch
+    res = {}
+    for name in MX_FORMAT_NAMES:
+        w = MxFormatWorkload(name, dev)
+        for _ in range(args.warmup):
+            w.run(stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record(stream)
+        for s in range(args.steps):
+            w.run(stream)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)])) * 1e3
+        tf = w.p.flops / (us * 1e-6) / 1e12
+        res[name] = {"level": w.level(), "us_per_launch": us, "tflops": tf, "peak_tflops": w.peak,
+                     "frac_of_peak": tf / w.peak}
+        del w
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "MX GEMM TFLOP/s by element format, 8192^3, bf16 out",
+                      "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic", "per_format": res}), flush=True)
 
 
 def read_traffic():
@@ -174,6 +253,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"copied {args.reps + 1} x {n} bytes", flush=True)
+        return
+    if args.mx_formats:
+        mx_formats(args, dev, stream)
+        return
+    if args.only in MX_FORMAT_NAMES:
+        work = MxFormatWorkload(args.only, dev)
+        for _ in range(args.reps + 1):
+            work.run(stream)
+        torch.cuda.synchronize()
+        print(f"ran {args.only} level {work.level()} x {args.reps + 1}", flush=True)
         return
     if args.only:
         work = Workload(4 if args.only == "bf16" else 5, dev)

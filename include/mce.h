@@ -188,10 +188,13 @@ int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K,
 int gemm_mxfp8_pick_level(int64_t M, int64_t N, int64_t K,
                           const void *A, int64_t lda, int a_col_major,
                           const void *B, int64_t ldb, int b_col_major);
-/* Level gemm_mx would run for this format and problem (0 if none). */
+/* Level gemm_mx would run for this format and problem (0 if none); the
+   scale pointers and leading dimensions matter for the E2M1 levels. */
 int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
                        const void *A, int64_t lda, int a_col_major,
-                       const void *B, int64_t ldb, int b_col_major);
+                       const void *SA, int64_t ld_sa,
+                       const void *B, int64_t ldb, int b_col_major,
+                       const void *SB, int64_t ld_sb);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char *gemm_status_string(int status);

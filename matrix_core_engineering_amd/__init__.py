@@ -67,7 +67,7 @@ def load():
     lib.gemm_mxfp8_pick_level.argtypes = pick
     lib.gemm_mx.argtypes = [i32] + mx_args
     lib.gemm_mx_level.argtypes = [i32, i32] + mx_args
-    lib.gemm_mx_pick_level.argtypes = [i32] + pick
+    lib.gemm_mx_pick_level.argtypes = [i32] + mnk + [vp, i64, i32, vp, i64, vp, i64, i32, vp, i64]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = i32
     lib.gemm_status_string.argtypes = [i32]
@@ -167,9 +167,11 @@ def gemm_mx_level(level, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B
     return _check(st, f"gemm_mx_level({level}, {elem_format})", raise_on_error)
 
 
-def gemm_mx_pick_level(elem_format, M, N, K, A, lda, a_col_major, B, ldb, b_col_major):
+def gemm_mx_pick_level(elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                       b_col_major, SB, ld_sb):
     return load().gemm_mx_pick_level(int(elem_format), M, N, K, _ptr(A), lda,
-                                     int(a_col_major), _ptr(B), ldb, int(b_col_major))
+                                     int(a_col_major), _ptr(SA), ld_sa, _ptr(B), ldb,
+                                     int(b_col_major), _ptr(SB), ld_sb)
 
 
 def gemm_status_string(status):

@@ -408,10 +408,11 @@ int gemm_mx_level(int level, int elem_format, int64_t M, int64_t N, int64_t K, c
 }
 
 int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-                       int a_col_major, const void *B, int64_t ldb, int b_col_major)
+                       int a_col_major, const void *SA, int64_t ld_sa, const void *B, int64_t ldb,
+                       int b_col_major, const void *SB, int64_t ld_sb)
 {
-    Call c = make_call(0, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, nullptr, 4, B, ldb,
-                       b_col_major, nullptr, 4, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
+    Call c = make_call(0, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                       b_col_major, SB, ld_sb, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
     if (M < 0 || N < 0 || K < 0 || a_col_major != 0 || b_col_major != 1 ||
         elem_format < MCE_MX_E4M3 || elem_format > MCE_MX_E2M1)
         return 0;

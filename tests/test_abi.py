@@ -107,7 +107,7 @@ def mx_call(fmt, M=64, N=64, K=64, lda=None, ldb=None, A=0x1000, B=0x9000, level
 def test_mx_unknown_format_is_einval():
     for fmt in (-1, 5, 99):
         assert mx_call(fmt) == mce.MCE_EINVAL
-        assert mce.gemm_mx_pick_level(fmt, 64, 64, 64, 0x1000, 64, 0, 0x9000, 64, 1) == 0
+        assert mce.gemm_mx_pick_level(fmt, 64, 64, 64, 0x1000, 64, 0, 0x20000, 2, 0x9000, 64, 1, 0x30000, 2) == 0
 
 
 @pytest.mark.parametrize("fmt,unit", [(mce.MCE_MX_E2M3, 4), (mce.MCE_MX_E3M2, 4), (mce.MCE_MX_E2M1, 2)])
@@ -122,10 +122,16 @@ def test_mx_packed_formats_need_whole_bytes(fmt, unit):
 def test_mx_pick_level_by_format():
     """8-bit formats pick the pipelined level when the operands allow it;
     the packed formats run level 3."""
-    for fmt in (mce.MCE_MX_E4M3, mce.MCE_MX_E5M2):
-        assert mce.gemm_mx_pick_level(fmt, 8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) == 6
-    for fmt in (mce.MCE_MX_E2M3, mce.MCE_MX_E3M2, mce.MCE_MX_E2M1):
-        assert mce.gemm_mx_pick_level(fmt, 8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) == 3
-    assert mce.gemm_mx_pick_level(mce.MCE_MX_E5M2, 64, 64, 64, 0x1000, 64, 1, 0x9000, 64, 1) == 0
+    def pick(fmt, K=8192, lda=8192, ld_s=256, a_cm=0):
+        return mce.gemm_mx_pick_level(fmt, 8192, 8192, K, 0x1000, lda, a_cm, 0x20000, ld_s, 0x9000,
+                                      lda, 1, 0x30000, ld_s)
+    for fmt in (mce.MCE_MX_E4M3, mce.MCE_MX_E5M2, mce.MCE_MX_E2M1):
+        assert pick(fmt) == 6
+    for fmt in (mce.MCE_MX_E2M3, mce.MCE_MX_E3M2):
+        assert pick(fmt) == 3
+    # E2M1's pipelined level needs 16-byte scale rows and K a multiple of 512
+    assert pick(mce.MCE_MX_E2M1, ld_s=260) == 3
+    assert pick(mce.MCE_MX_E2M1, K=8192 - 256, lda=8192, ld_s=256) == 3
+    assert pick(mce.MCE_MX_E5M2, a_cm=1) == 0
     assert (mce.gemm_mxfp8_pick_level(8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) ==
-            mce.gemm_mx_pick_level(mce.MCE_MX_E4M3, 8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1))
+            pick(mce.MCE_MX_E4M3))
