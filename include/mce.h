@@ -49,8 +49,8 @@
  *                    c_dtype not MCE_OUT_F32/MCE_OUT_BF16; C overlapping A, B
  *                    or a scale array; an operand spanning 2^31 bytes or more
  *  MCE_EUNSUPPORTED  device is not gfx950; a level that cannot take this
- *                    problem (see gemm_bf16_level); MX operand not
- *                    K-contiguous
+ *                    problem (see gemm_bf16_level); a packed (6- or 4-bit)
+ *                    MX operand that is not K-contiguous
  *  MCE_ELAUNCH       the kernel launch itself failed (hipGetLastError)
  */
 #ifndef MCE_H
@@ -96,9 +96,11 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
  * MX block-scaled fp8 GEMM.  A and B hold E4M3FN codes (one byte each).
  * SA is M x ceil(K/32) E8M0 bytes, row-major with leading dimension ld_sa:
  * a(i,k) = e4m3(A(i,k)) * 2^(SA[i*ld_sa + k/32] - 127).  SB is N x ceil(K/32)
- * bytes, row-major with leading dimension ld_sb, scaling b(k,j) the same way.
- * Both operands must be K-contiguous (a_col_major == 0, b_col_major == 1),
- * else MCE_EUNSUPPORTED.  The scale byte 0xFF (NaN) propagates NaN.
+ * bytes, row-major with leading dimension ld_sb, scaling b(k,j) the same way
+ * (the scale layout does not follow the operand layout).  Any operand layout;
+ * MN-major operands (a_col_major == 1 or b_col_major == 0) run level 3, the
+ * pipelined levels need both operands K-contiguous.  The scale byte 0xFF
+ * (NaN) propagates NaN.
  * ("B200 TMEM Lifecycle Planner", section A1 case 2: block-scaled MMA.)
  */
 int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
@@ -132,7 +134,7 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  * run a kernel that stages the operands through registers (any layout,
  * alignment and K).  gemm_mxfp8_level accepts levels 3 and 5-7, 5-7 with the
  * K-contiguity and alignment rules above and scale rows padded to 4 bytes
- * (same meaning; its level 3 also takes any K).
+ * (same meaning; its level 3 also takes any K and either operand layout).
  */
 int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, int a_col_major,
@@ -155,7 +157,8 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K,
  * a row is the 6 (4) bits at bit offset 6k (4k) of the row's little-endian
  * bit string, so two E2M1 share a byte (lower k in the low nibble) and four
  * E2M3 / E3M2 share three bytes; lda and ldb stay in elements and, like K,
- * must be multiples of 2 (E2M1) or 4 (E2M3, E3M2), else MCE_EINVAL.  An
+ * must be multiples of 2 (E2M1) or 4 (E2M3, E3M2), else MCE_EINVAL; packed
+ * operands must be K-contiguous (else MCE_EUNSUPPORTED).  An
  * unknown elem_format is MCE_EINVAL.  ("B200 TMEM Lifecycle Planner",
  * section A1 case 2: block-scaled MMA; the pages name no element format.)
  *

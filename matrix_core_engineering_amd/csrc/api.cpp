@@ -162,9 +162,10 @@ int validate(const Call &c)
         return MCE_EINVAL;
     if (c.fmt == FMT_MX && (c.mx_fmt < MCE_MX_E4M3 || c.mx_fmt > MCE_MX_E2M1))
         return MCE_EINVAL;
-    if (c.fmt == FMT_MX && !(c.a_cm == 0 && c.b_cm == 1))
-        return MCE_EUNSUPPORTED;
     const int bits = elem_bits(c);
+    // MN-major MX operands: 8-bit formats only (the packed ones are packed along K)
+    if (c.fmt == FMT_MX && bits != 8 && !(c.a_cm == 0 && c.b_cm == 1))
+        return MCE_EUNSUPPORTED;
     // packed 6- and 4-bit rows: every row and the K extent fill whole bytes
     const int64_t per_byte_group = bits == 6 ? 4 : bits == 4 ? 2 : 1;
     if (c.K % per_byte_group || c.lda % per_byte_group || c.ldb % per_byte_group)
@@ -381,7 +382,7 @@ int gemm_mxfp8_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_
 {
     Call c = make_call(0, FMT_MX, MCE_MX_E4M3, M, N, K, A, lda, a_col_major, nullptr, 4, B, ldb, b_col_major,
                        nullptr, 4, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
-    if (M < 0 || N < 0 || K < 0 || a_col_major != 0 || b_col_major != 1)
+    if (M < 0 || N < 0 || K < 0)
         return 0;
     return pick_level(c);
 }
@@ -413,9 +414,10 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K, const v
 {
     Call c = make_call(0, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
                        b_col_major, SB, ld_sb, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
-    if (M < 0 || N < 0 || K < 0 || a_col_major != 0 || b_col_major != 1 ||
-        elem_format < MCE_MX_E4M3 || elem_format > MCE_MX_E2M1)
+    if (M < 0 || N < 0 || K < 0 || elem_format < MCE_MX_E4M3 || elem_format > MCE_MX_E2M1)
         return 0;
+    if (mce::mx_bits(elem_format) != 8 && (a_col_major != 0 || b_col_major != 1))
+        return 0;   // the packed formats are packed along K
     return pick_level(c);
 }
 

@@ -117,8 +117,9 @@ __global__ __launch_bounds__(256) void gemm_simple_bf16(GemmArgs p)
 // ---------------------------------------------------------------- MX
 //
 // K tile of 64 elements = two 32-element scale blocks = one 32x32x64
-// block-scaled instruction per (i, j) per K tile.  Both operands are
-// K-contiguous; a K tile of a row is 64 * bits / 8 bytes (64, 48 or 32),
+// block-scaled instruction per (i, j) per K tile.  The packed formats are
+// K-contiguous, the 8-bit ones either layout; a K tile of a row is
+// 64 * bits / 8 bytes (64, 48 or 32),
 // copied byte by byte into an LDS row of that length plus 16 bytes of
 // padding.  Bytes past K are zero (for the packed formats K fills whole
 // bytes, so no element past K shares a byte with one inside).
@@ -130,19 +131,23 @@ struct MxTile {
     static constexpr int ROW = BYTES + 16;                   // LDS row pitch
 };
 
+// One operand's K tile into LDS rows (one row per M or N index, K along
+// the row).  KC: byte b of row r at g[r * ld_bytes + b]; otherwise (an
+// MN-major 8-bit operand, ld in elements = bytes) element (r, k) at
+// g[k * ld_bytes + r], consecutive threads taking consecutive rows.
 template <int FMT>
-__device__ __forceinline__ void load_tile_mx(const uint8_t *g, int64_t ld_bytes, int rows,
+__device__ __forceinline__ void load_tile_mx(const uint8_t *g, int64_t ld_bytes, bool kc, int rows,
                                              int64_t k_bytes, int row0, int64_t kb0, uint8_t *lds)
 {
     using T = MxTile<FMT>;
     const int tid = threadIdx.x;
     for (int idx = tid; idx < BM * T::BYTES; idx += 256) {
-        const int r = idx / T::BYTES, b = idx % T::BYTES;
+        const int r = kc ? idx / T::BYTES : idx % BM, b = kc ? idx % T::BYTES : idx / BM;
         const int gr = row0 + r;
         const int64_t gb = kb0 + b;
         uint8_t v = 0;
         if (gr < rows && gb < k_bytes)
-            v = g[(size_t)gr * ld_bytes + gb];
+            v = kc ? g[(size_t)gr * ld_bytes + gb] : g[(size_t)gb * ld_bytes + gr];
         lds[r * T::ROW + b] = v;
     }
 }
@@ -203,8 +208,8 @@ __global__ __launch_bounds__(256) void gemm_simple_mx(GemmArgs p)
     const int ktiles = (p.K + MX_BK - 1) / MX_BK;
     for (int kt = 0; kt < ktiles; ++kt) {
         const int64_t kb0 = (int64_t)kt * T::BYTES;
-        load_tile_mx<FMT>(A, lda_b, p.M, k_bytes, m0, kb0, As);
-        load_tile_mx<FMT>(B, ldb_b, p.N, k_bytes, n0, kb0, Bs);
+        load_tile_mx<FMT>(A, lda_b, !p.a_cm, p.M, k_bytes, m0, kb0, As);
+        load_tile_mx<FMT>(B, ldb_b, p.b_cm, p.N, k_bytes, n0, kb0, Bs);
         __syncthreads();
         const int kb = kt * (MX_BK / 32) + (lane >> 5);
         intx8 fa[2], fb[2];

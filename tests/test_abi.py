@@ -70,14 +70,23 @@ def test_level_out_of_range():
     assert bf16(4, 4, 4, 4, 0, 4, 1, 4, level=8) == mce.MCE_EUNSUPPORTED
 
 
-def test_mx_rejects_mn_major_operands_and_short_scale_ld():
+def test_mx_layouts_and_short_scale_ld():
+    """8-bit MX operands may be MN-major (level 3); packed ones may not; a
+    scale row shorter than ceil(K/32) is invalid."""
     def mx(a_cm, b_cm, ld_sa=1, ld_sb=1, K=32):
         return mce.gemm_mxfp8(4, 4, K, FAKE_A, 4 if a_cm else K, a_cm, 0x40000000, ld_sa,
                               FAKE_B, K if b_cm else 4, b_cm, 0x50000000, ld_sb, FAKE_C, 4, 0,
                               0, 1.0, 0.0, stream=0, raise_on_error=False)
-    assert mx(1, 1) == mce.MCE_EUNSUPPORTED
-    assert mx(0, 0) == mce.MCE_EUNSUPPORTED
     assert mx(0, 1, ld_sa=1, K=64) == mce.MCE_EINVAL     # needs ceil(64/32) = 2
+    assert mce.gemm_mxfp8_pick_level(64, 64, 64, FAKE_A, 64, 1, FAKE_B, 64, 0) == 3
+    assert mce.gemm_mx_pick_level(mce.MCE_MX_E5M2, 64, 64, 64, FAKE_A, 64, 1, 0x40000000, 4,
+                                  FAKE_B, 64, 0, 0x50000000, 4) == 3
+    for fmt in (mce.MCE_MX_E2M3, mce.MCE_MX_E2M1):
+        assert mce.gemm_mx_pick_level(fmt, 64, 64, 64, FAKE_A, 64, 1, 0x40000000, 4,
+                                      FAKE_B, 64, 1, 0x50000000, 4) == 0
+        st = mce.gemm_mx(fmt, 4, 4, 32, FAKE_A, 4, 1, 0x40000000, 1, FAKE_B, 32, 1, 0x50000000, 1,
+                         FAKE_C, 4, 0, 0, 1.0, 0.0, stream=0, raise_on_error=False)
+        assert st == mce.MCE_EUNSUPPORTED
 
 
 def test_pick_level_reports_a_level():
@@ -85,7 +94,7 @@ def test_pick_level_reports_a_level():
     # row-major B with 2-byte aligned rows: the register-staged kernel of level 6
     assert mce.gemm_bf16_pick_level(4093, 3001, 1027, FAKE_A, 1027, 0, FAKE_B, 3001, 0) == 6
     assert mce.gemm_mxfp8_pick_level(8192, 8192, 8192, FAKE_A, 8192, 0, FAKE_B, 8192, 1) >= 3
-    assert mce.gemm_mxfp8_pick_level(8, 8, 64, FAKE_A, 8, 1, FAKE_B, 64, 1) == 0
+    assert mce.gemm_mxfp8_pick_level(-8, 8, 64, FAKE_A, 8, 1, FAKE_B, 64, 1) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -132,6 +141,6 @@ def test_mx_pick_level_by_format():
     # E2M1's pipelined level needs 16-byte scale rows and K a multiple of 512
     assert pick(mce.MCE_MX_E2M1, ld_s=260) == 3
     assert pick(mce.MCE_MX_E2M1, K=8192 - 256, lda=8192, ld_s=256) == 3
-    assert pick(mce.MCE_MX_E5M2, a_cm=1) == 0
+    assert pick(mce.MCE_MX_E5M2, a_cm=1) == 3
     assert (mce.gemm_mxfp8_pick_level(8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) ==
             pick(mce.MCE_MX_E4M3))

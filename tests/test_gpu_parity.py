@@ -326,6 +326,31 @@ def test_mx_formats_large_groups_integer_exact(fmt, level):
     assert np.array_equal(vals[ii, jj], cref)
 
 
+@pytest.mark.parametrize("level", [3, 5, None])
+@pytest.mark.parametrize("layout", [(True, True), (False, False), (True, False)],
+                         ids=["a_col_b_col", "a_row_b_row", "a_col_b_row"])
+@pytest.mark.parametrize("fmt", [E4M3FN, E5M2], ids=["e4m3", "e5m2"])
+def test_mx_mn_major_operands(fmt, layout, level):
+    """8-bit MX operands stored MN-major (scales stay one row per M or N
+    index): level 3 runs them, the pipelined levels decline; integer data
+    bitwise, random data within the bound, ragged shapes."""
+    a_cm, b_cm = layout
+    for t, (M, N, K) in enumerate([(5, 3, 40), (127, 129, 100), (200, 150, 512), (33, 65, 1000)]):
+        p = make_problem(M, N, K, fmt=fmt, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_F32,
+                         dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2, seed=9100 + t)
+        r = run_level(p, level)
+        if level == 5:
+            assert r is None, "the pipelined levels take K-contiguous operands only"
+            continue
+        assert r is not None
+        assert_bitwise(p, r[1])
+        kw = dict(dist="uniform", lo=-448.0, hi=448.0)
+        p = make_problem(M, N, K, fmt=fmt, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_BF16,
+                         alpha=0.5, beta=1.5, seed=9200 + t, **kw)
+        r = run_level(p, level)
+        assert_close(p, r[0])
+
+
 @pytest.mark.parametrize("level", MX_LEVELS)
 def test_mx_scale_semantics(level):
     """All data 1.0; scale bytes chosen per (row, block): the result is the
