@@ -487,17 +487,18 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // Per format: KA k-steps in phase A (the K tile's fragment reads spread
 // over them: four waves read LDS at about 108 B/clk per CU); XM matrix-core
 // instructions in phase X; LX and LY of a K tile's direct loads issued in
-// phases X and Y, the rest in the next phase A; YA of the next K tile's
-// first A fragments read in phase Y, the rest in the next phase A (the
-// instruction order needs A fragment i only from the (TJ*i)-th instruction
-// on).
+// phases X and Y, the rest in the next phase A; the next K tile's first YK
+// k-steps of fragments read whole in phase Y (into the registers of k-steps
+// whose instructions all precede phase Y), then k-step YK's B fragments and
+// its first YA A fragments, the rest in the next phase A (the instruction
+// order needs A fragment i only from the (TJ*i)-th instruction on).
 struct Bf16Ring64 {                   // 128-byte rows
     static constexpr bool MX = false, SG = false, FP4 = false;
     static constexpr int EPU = 1;     // elements per K unit (FP4: two per byte)
     static constexpr int ELT = 2;
     static constexpr int BK = 64;
     static constexpr int NKS = 4;
-    static constexpr int KA = 1, XM = 32, LX = 16, LY = 0, YA = 2;
+    static constexpr int KA = 1, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
     static constexpr bool MX = true, SG = false, FP4 = false;
@@ -506,7 +507,7 @@ struct Mxfp8Ring128 {                 // 128-byte rows
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
     static constexpr int NKS = 2;
-    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2;
+    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2, YK = 0;
 };
 // MX with K a multiple of 512 (whole groups of 16 scale blocks): the scale
 // words of four K tiles travel together, 16 bytes per row, in a separate
@@ -515,7 +516,7 @@ struct Mxfp8Ring128 {                 // 128-byte rows
 // instruction doubled the K tile's line requests.
 struct Mxfp8Ring128G : Mxfp8Ring128 {
     static constexpr bool SG = true;
-    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2;
+    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 1, YK = 0;
 };
 // E5M2 elements have E4M3's byte layout and fragment map: the same kernels
 // with the instruction's format code 1.
@@ -542,7 +543,7 @@ struct Fp4Ring128G {
     static constexpr int ELT = 1;
     static constexpr int BK = 128;    // K units (bytes) per K tile
     static constexpr int NKS = 4;
-    static constexpr int KA = 1, XM = 32, LX = 16, LY = 0, YA = 2;
+    static constexpr int KA = 1, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
@@ -559,10 +560,12 @@ void gemm_early(GemmArgs p, int group_m)
     constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
     constexpr int KA = Op::KA, AM = KA * NM;                // phase A
     constexpr int XM = Op::XM, YM = (NKS - KA) * NM - XM;  // phases X and Y
-    constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA;
+    constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA, YK = Op::YK;
     static_assert(G::CH == 8, "128-byte LDS rows");
     static_assert(XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
     static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
+    static_assert(YK >= 0 && YK < NKS && AM + XM >= (YK + 1) * NM,
+                  "phase Y overwrites only k-steps whose instructions precede it");
     static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
     // LDS: the two stages, then (scale groups) two buffers of 16 bytes per
     // A and B row and a 1 KiB sink for the loads of iterations that load no
@@ -813,6 +816,41 @@ void gemm_early(GemmArgs p, int group_m)
         }
     };
 
+    // a K tile's fragment reads in two parts: the head (phase Y of the
+    // previous K tile: k-steps 0 .. YK-1 whole, then k-step YK's B fragments
+    // and first YA A fragments) and the tail (phase A: the rest)
+    auto read_head = [&](int stage) {
+#pragma unroll
+        for (int ks = 0; ks < YK; ++ks) {
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i)
+                read_a(ks, stage, i);
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                read_b(ks, stage, j);
+        }
+#pragma unroll
+        for (int i = 0; i < YA; ++i)
+            read_a(YK, stage, i);
+#pragma unroll
+        for (int j = 0; j < G::TJ; ++j)
+            read_b(YK, stage, j);
+    };
+    auto read_tail = [&](int stage) {
+#pragma unroll
+        for (int i = YA; i < G::TI; ++i)
+            read_a(YK, stage, i);
+#pragma unroll
+        for (int ks = YK + 1; ks < NKS; ++ks) {
+#pragma unroll
+            for (int i = 0; i < G::TI; ++i)
+                read_a(ks, stage, i);
+#pragma unroll
+            for (int j = 0; j < G::TJ; ++j)
+                read_b(ks, stage, j);
+        }
+    };
+
     // ---------------------------------------------------------- prologue
     // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
     // issues (a direct load always writes LDS, so no placeholder load may
@@ -822,12 +860,7 @@ void gemm_early(GemmArgs p, int group_m)
     issue(0, LX + LY, false, 1, 1);
     wait_vmcnt<LX + LY>();                         // K tile 0 (and scale group 0) landed
     barrier();
-#pragma unroll
-    for (int i = 0; i < YA; ++i)
-        read_a(0, 0, i);
-#pragma unroll
-    for (int j = 0; j < G::TJ; ++j)
-        read_b(0, 0, j);
+    read_head(0);
     read_scales(0, 0, 0);
 #pragma unroll
     for (int w = 0; w < SW; ++w) {
@@ -851,24 +884,13 @@ void gemm_early(GemmArgs p, int group_m)
                 acc[i][j] = zero16();
         for (int kt = 0; kt < nk; ++kt, ++g) {
             const int stage = g & 1;
-            // phase A: the first KA k-steps; the K tile's other fragments into
-            // registers; the last loads of K tile g+1
-#pragma unroll
-            for (int i = YA; i < G::TI; ++i)
-                read_a(0, stage, i);
-#pragma unroll
-            for (int ks = 1; ks < NKS; ++ks) {
-#pragma unroll
-                for (int i = 0; i < G::TI; ++i)
-                    read_a(ks, stage, i);
-#pragma unroll
-                for (int j = 0; j < G::TJ; ++j)
-                    read_b(ks, stage, j);
-            }
+            // phase A: the first KA k-steps; the K tile's other fragments (its
+            // tail) into registers; the last loads of K tile g+1
+            read_tail(stage);
             issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
             mfmas(0, AM);
             {
-                constexpr int R = (G::TI - YA) * RPF + FRAG_READS * (NKS - 1);
+                constexpr int R = (G::TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
                 constexpr int PER = (R + AM - 1) / AM;
 #pragma unroll
                 for (int x = 0; x < AM; ++x) {
@@ -902,13 +924,9 @@ void gemm_early(GemmArgs p, int group_m)
             wait_vmcnt<LX>();                      // this wave's loads of K tile g+1 landed
             barrier();                             // ready: K tile g+1 in the other stage
             __builtin_amdgcn_sched_barrier(0);
-            // phase Y: the rest of K tile g; K tile g+1's first fragments
-#pragma unroll
-            for (int i = 0; i < YA; ++i)
-                read_a(0, stage ^ 1, i);
-#pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
-                read_b(0, stage ^ 1, j);
+            // phase Y: the rest of K tile g; K tile g+1's first fragments (its
+            // head)
+            read_head(stage ^ 1);
             read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1);
             issue(LX, LX + LY, lnext, lkt, stage);
             pn_next = lnext;
@@ -916,7 +934,7 @@ void gemm_early(GemmArgs p, int group_m)
             pn_stage = stage;
             mfmas(AM + XM, NKS * NM);
             {
-                constexpr int R = (YA + G::TJ) * RPF + (Op::MX ? G::TI + G::TJ : 0);
+                constexpr int R = YK * FRAG_READS + (YA + G::TJ) * RPF + (Op::MX ? G::TI + G::TJ : 0);
                 constexpr int PER = (R + YM - 1) / YM;
 #pragma unroll
                 for (int x = 0; x < YM; ++x) {
