@@ -15,10 +15,15 @@ dominant (longest) kernel, timed with HIP events on the stream it runs on;
 `cpu_baseline` times the fp64 oracle on a bounded row sample of the bf16
 GEMM on the host cores and checks those rows of the GPU result.
 
+`matrix_core_loop` gives the rate of a pure matrix-core loop per instruction
+shape (no memory traffic), the power-limited ceiling the GEMMs run under;
+`roofline` relates the dominant kernel to it as well as to the published peak.
+
 Modes for profiling (no JSON): --only bf16|mxfp8|copy|e4m3|e5m2|e2m3|e3m2|e2m1
 --reps R runs just that kernel R times after one warm-up (copy: a 1 GiB
 device-to-device copy, the calibration of the HBM byte counters; the MX
-element-format names: the 8192^3 MX GEMM in that format).
+element-format names: the 8192^3 MX GEMM in that format).  --only loop prints
+the matrix-core loop rates alone.
 --mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
 element format at its default level, with W warm-up and K timed launches.
 """
@@ -59,7 +64,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy"] + list(MX_FORMAT_NAMES), default=None)
+    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop"] + list(MX_FORMAT_NAMES),
+                    default=None)
     ap.add_argument("--mx-formats", action="store_true",
                     help="time the 8192^3 MX GEMM in every element format (one JSON line)")
     ap.add_argument("--reps", type=int, default=3)
@@ -181,6 +187,44 @@ def mx_formats(args, dev, stream):
                       "data": "synthetic", "per_format": res}), flush=True)
 
 
+CEILING_SHAPES = (("bf16_32x32x16", 0, "bf16", PEAK_BF16),
+                  ("bf16_16x16x32", 1, "bf16", PEAK_BF16),
+                  ("mxfp8_32x32x64", 2, "e4m3", PEAK_FP8))
+
+
+def matrix_core_ceiling(dev, stream, iters=2000, reps=3):
+    """Sustained rate of the pure matrix-core loop (mce_matrix_core_loop, one
+    workgroup per CU, one wave per SIMD, no memory traffic in the loop) per
+    instruction shape, on the bench workloads' value distributions (bf16 from
+    N(0, 0.02^2), E4M3 from U[-448, 448]): the power-limited ceiling that the
+    GEMM kernels run under."""
+    import torch
+    import matrix_core_engineering_amd as mce
+    g = torch.Generator().manual_seed(7)
+    nfrag = 1 << 16
+    bufs = {"bf16": (torch.randn(nfrag * 8, generator=g) * 0.02).to(torch.bfloat16)
+                    .view(torch.int16).to(dev),
+            "e4m3": (torch.rand(nfrag * 32, generator=g) * 896.0 - 448.0)
+                    .to(torch.float8_e4m3fn).view(torch.uint8).to(dev)}
+    blocks = 256
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = blocks * 4 * iters * float(1 << 21)
+    res = {}
+    for name, shape, data, peak in CEILING_SHAPES:
+        mce.mce_matrix_core_loop(shape, bufs[data], nfrag, out, blocks, iters // 4, stream=stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            mce.mce_matrix_core_loop(shape, bufs[data], nfrag, out, blocks, iters, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = flops / (us * 1e-6) / 1e12
+        res[name] = {"tflops": tf, "frac_of_peak": tf / peak, "us_per_launch": us}
+    return res
+
+
 def read_traffic():
     """HBM bytes per launch of the bf16 kernel from the committed counter
     summary, or None if it is missing or was taken on other kernel code."""
@@ -257,6 +301,10 @@ def main():
     if args.mx_formats:
         mx_formats(args, dev, stream)
         return
+    if args.only == "loop":
+        res = matrix_core_ceiling(dev, stream, reps=args.reps)
+        print(json.dumps({"matrix_core_loop": res}), flush=True)
+        return
     if args.only in MX_FORMAT_NAMES:
         work = MxFormatWorkload(args.only, dev)
         for _ in range(args.reps + 1):
@@ -304,6 +352,7 @@ def main():
         per_workload[n] = {"us_per_launch": per_ms[n] * 1e3, "tflops": tf,
                            "peak_tflops": peak, "frac_of_peak": tf / peak,
                            "level": works[n].level()}
+    ceiling = matrix_core_ceiling(dev, stream)
     dom = max(names, key=lambda n: per_ms[n])
     traffic = read_traffic() if dom.startswith("bf16") else None
     roofline = {"bound": "mfma", "achieved": per_workload[dom]["tflops"],
@@ -311,6 +360,11 @@ def main():
                 "frac": per_workload[dom]["frac_of_peak"], "traffic": traffic,
                 "kernel": f"{dom} (level {per_workload[dom]['level']})",
                 "flops_per_launch": flops[dom], "us_per_launch": per_ms[dom] * 1e3}
+    # the same kernel against the rate its instruction sustains with no memory
+    # traffic at all (the chip's power-limited matrix-core ceiling)
+    loop = ceiling["bf16_32x32x16" if dom.startswith("bf16") else "mxfp8_32x32x64"]["tflops"]
+    roofline["sustained_loop_tflops"] = loop
+    roofline["frac_of_sustained_loop"] = per_workload[dom]["tflops"] / loop
 
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -319,7 +373,7 @@ def main():
            "config": {"workload": "8192^3 bf16 GEMM + 8192^3 MX-fp8 GEMM per step",
                       "M": 8192, "N": 8192, "K": 8192, "a": "row-major", "b": "column-major",
                       "out": "bf16", "alpha": 1.0, "beta": 0.0},
-           "per_workload": per_workload, "roofline": roofline,
+           "per_workload": per_workload, "roofline": roofline, "matrix_core_loop": ceiling,
            "wall_s_timed": wall}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(works["bf16_8192"], args.cpu_seconds)

@@ -199,6 +199,35 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
                        const void *B, int64_t ldb, int b_col_major,
                        const void *SB, int64_t ld_sb);
 
+/*
+ * Matrix-core ceiling (a measurement aid beside the GEMM, which never calls
+ * it).  The pages ask to stop tuning near the practical roofline ("B200 GEMM
+ * Optimization Ladder", section E step 11); on MI355X the rate a dense
+ * contraction can sustain is set by the socket's power limit and depends on
+ * the instruction shape and the operand values.  This call launches `blocks`
+ * workgroups of four waves (one wave per SIMD, as the GEMM kernels run); each
+ * wave loads sixteen operand fragments per lane once from `frags`, then
+ * repeats the matrix-core instruction sequence of a 128x128 fp32 accumulator
+ * tile `iters` times with no other memory traffic, and finally writes the sum
+ * of its lane's accumulators to out[blockIdx * 256 + lane_in_block].  Every
+ * call does blocks * 4 * iters * 2^21 flops; timing it gives the sustained
+ * matrix-core rate for that shape and data.
+ *   shape   MCE_LOOP_BF16_32X32X16 (the GEMM's bf16 instruction),
+ *           MCE_LOOP_BF16_16X16X32, or MCE_LOOP_MXFP8_32X32X64 (the MX
+ *           instruction with E4M3 operands, every scale 1)
+ *   frags   device pointer to n_frag fragments of 16 bytes (bf16 shapes:
+ *           eight bf16) or 32 bytes (MX: 32 E4M3 codes); fragment
+ *           (gid * 16 + i) % n_frag is lane gid's i-th operand register set
+ *   out     device pointer to blocks * 256 floats, written
+ * Errors: MCE_EINVAL for an unknown shape, a NULL pointer, n_frag < 1,
+ * blocks outside [1, 65535] or iters outside [1, 2^24]; MCE_EUNSUPPORTED
+ * on a device other than gfx950; MCE_ELAUNCH for a failed launch.  Allocates
+ * nothing; asynchronous on `stream`.
+ */
+enum { MCE_LOOP_BF16_32X32X16 = 0, MCE_LOOP_BF16_16X16X32 = 1, MCE_LOOP_MXFP8_32X32X64 = 2 };
+int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *out,
+                         int blocks, int iters, void *stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char *gemm_status_string(int status);
 

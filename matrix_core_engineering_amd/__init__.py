@@ -16,16 +16,18 @@ __all__ = ["gemm_bf16", "gemm_mxfp8", "gemm_bf16_level", "gemm_mxfp8_level",
            "MCE_MX_E2M3", "MCE_MX_E3M2", "MCE_MX_E2M1",
            "gemm_status_string", "MceError", "lib_path", "load",
            "EXPORTED_SYMBOLS", "MCE_OK", "MCE_EINVAL", "MCE_EUNSUPPORTED",
-           "MCE_ELAUNCH", "MCE_OUT_F32", "MCE_OUT_BF16"]
+           "MCE_ELAUNCH", "MCE_OUT_F32", "MCE_OUT_BF16", "mce_matrix_core_loop",
+           "MCE_LOOP_BF16_32X32X16", "MCE_LOOP_BF16_16X16X32", "MCE_LOOP_MXFP8_32X32X64"]
 
 MCE_OK, MCE_EINVAL, MCE_EUNSUPPORTED, MCE_ELAUNCH = 0, 1, 2, 3
 MCE_OUT_F32, MCE_OUT_BF16 = 0, 1
 MCE_MX_E4M3, MCE_MX_E5M2, MCE_MX_E2M3, MCE_MX_E3M2, MCE_MX_E2M1 = 0, 1, 2, 3, 4
+MCE_LOOP_BF16_32X32X16, MCE_LOOP_BF16_16X16X32, MCE_LOOP_MXFP8_32X32X64 = 0, 1, 2
 
 EXPORTED_SYMBOLS = ("gemm_bf16", "gemm_mxfp8", "gemm_bf16_level",
                     "gemm_mxfp8_level", "gemm_bf16_pick_level",
                     "gemm_mxfp8_pick_level", "gemm_mx", "gemm_mx_level",
-                    "gemm_mx_pick_level", "gemm_status_string")
+                    "gemm_mx_pick_level", "mce_matrix_core_loop", "gemm_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -68,6 +70,7 @@ def load():
     lib.gemm_mx.argtypes = [i32] + mx_args
     lib.gemm_mx_level.argtypes = [i32, i32] + mx_args
     lib.gemm_mx_pick_level.argtypes = [i32] + mnk + [vp, i64, i32, vp, i64, vp, i64, i32, vp, i64]
+    lib.mce_matrix_core_loop.argtypes = [i32, vp, i64, vp, i32, i32, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = i32
     lib.gemm_status_string.argtypes = [i32]
@@ -172,6 +175,13 @@ def gemm_mx_pick_level(elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, 
     return load().gemm_mx_pick_level(int(elem_format), M, N, K, _ptr(A), lda,
                                      int(a_col_major), _ptr(SA), ld_sa, _ptr(B), ldb,
                                      int(b_col_major), _ptr(SB), ld_sb)
+
+
+def mce_matrix_core_loop(shape, frags, n_frag, out, blocks, iters, stream=None,
+                         raise_on_error=True):
+    st = load().mce_matrix_core_loop(int(shape), _ptr(frags), int(n_frag), _ptr(out),
+                                     int(blocks), int(iters), _stream(stream))
+    return _check(st, f"mce_matrix_core_loop({shape})", raise_on_error)
 
 
 def gemm_status_string(status):

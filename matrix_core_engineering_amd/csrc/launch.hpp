@@ -24,4 +24,9 @@ hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s);
 // layout, alignment and K, through registers.
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);
 
+// The matrix-core ceiling loop (shape: MCE_LOOP_*); returns
+// hipErrorInvalidValue for an unknown shape.
+hipError_t launch_matrix_core_loop(int shape, const void *frags, int n_frag, float *out, int blocks,
+                                   int iters, hipStream_t s);
+
 } // namespace mce

@@ -144,3 +144,19 @@ def test_mx_pick_level_by_format():
     assert pick(mce.MCE_MX_E5M2, a_cm=1) == 3
     assert (mce.gemm_mxfp8_pick_level(8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) ==
             pick(mce.MCE_MX_E4M3))
+
+
+@pytest.mark.parametrize("shape,frags,n_frag,out,blocks,iters", [
+    (3, FAKE_A, 16, FAKE_C, 1, 1),            # unknown shape
+    (-1, FAKE_A, 16, FAKE_C, 1, 1),
+    (0, 0, 16, FAKE_C, 1, 1),                 # frags NULL
+    (0, FAKE_A, 16, 0, 1, 1),                 # out NULL
+    (0, FAKE_A, 0, FAKE_C, 1, 1),             # no fragment
+    (1, FAKE_A, 16, FAKE_C, 0, 1),            # no workgroup
+    (1, FAKE_A, 16, FAKE_C, 65536, 1),        # grid too large
+    (2, FAKE_A, 16, FAKE_C, 1, 0),            # no iteration
+    (2, FAKE_A, 16, FAKE_C, 1, (1 << 24) + 1),
+])
+def test_matrix_core_loop_rejects_bad_arguments(shape, frags, n_frag, out, blocks, iters):
+    assert mce.mce_matrix_core_loop(shape, frags, n_frag, out, blocks, iters, stream=0,
+                                    raise_on_error=False) == mce.MCE_EINVAL

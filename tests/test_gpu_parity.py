@@ -567,3 +567,24 @@ def test_whole_tiles_bf16_output_bitwise(level, fmt):
     expect = f64_to_bf16_bits(A @ B)
     bad = np.argwhere(raw != expect)
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("shape", [mce.MCE_LOOP_BF16_32X32X16, mce.MCE_LOOP_BF16_16X16X32,
+                                   mce.MCE_LOOP_MXFP8_32X32X64])
+def test_matrix_core_loop_closed_form(shape):
+    """The ceiling loop on all-ones operands: every instruction adds its K
+    depth to each accumulator, 64 per iteration for every shape (4 k-steps of
+    16, 2 of 32, 1 of 64), and each lane holds 256 accumulators, so every
+    lane writes 256 * 64 * iters exactly."""
+    announce(f"matrix_core_loop shape={shape}")
+    dev = torch.device("cuda:0")
+    n_frag, blocks, iters = 64, 8, 6
+    if shape == mce.MCE_LOOP_MXFP8_32X32X64:
+        one = torch.ones(n_frag * 32).to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        one = torch.ones(n_frag * 8, dtype=torch.bfloat16).view(torch.int16)
+    frags = one.to(dev)
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device=dev)
+    mce.mce_matrix_core_loop(shape, frags, n_frag, out, blocks, iters)
+    torch.cuda.synchronize()
+    assert torch.all(out.cpu() == 256.0 * 64.0 * iters)
