@@ -472,22 +472,26 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // delivers about half the bytes per clock of one of 128-byte rows.  With
 // only two stages the next-but-one K tile can be loaded only once the stage
 // is released, so each wave reads the whole K tile's fragments into
-// registers during its first k-step and releases the stage early.  Two
-// barriers per K tile g (stage s = g % 2):
-//   phase A  the first KA k-steps on the matrix cores; the fragments of
-//            k-steps 1.. read;
+// registers during its first matrix-core instructions and releases the
+// stage early.  Two barriers per K tile g (stage s = g % 2):
+//   phase A  the first AM matrix-core instructions; the rest of the K
+//            tile's fragments read;
 //   barrier 1 (free):  every wave's reads of stage s are in registers;
-//   phase X  the next k-steps; the loads of K tile g+2 into stage s begin;
+//   phase X  the next XM instructions; the loads of K tile g+2 into stage
+//            s begin;
 //   barrier 2 (ready): each wave waited for its loads of K tile g+1;
 //   phase Y  the last matrix-core instructions of K tile g; K tile g+1's
 //            first fragments (and MX scales) read; the remaining loads.
 // The loads of a K tile spread over phases X and Y of one iteration and have
 // until barrier 2 of the next to land.  Needs at least two K tiles and K a
 // multiple of the K tile.
-// Per format: KA k-steps in phase A (the K tile's fragment reads spread
-// over them: four waves read LDS at about 108 B/clk per CU); XM matrix-core
-// instructions in phase X; LX and LY of a K tile's direct loads issued in
-// phases X and Y, the rest in the next phase A; the next K tile's first YK
+// Per format: AM matrix-core instructions in phase A (the K tile's fragment
+// reads spread over them: four waves read LDS at about 108 B/clk per CU; AM
+// need not be a whole k-step: the stage is free once every fragment is in
+// registers); XM in phase X; LX and LY of a K tile's direct loads issued in
+// phases X and Y (the address unit takes about one 1 KiB direct load per
+// 21 clocks per CU, so the loads need phases X and Y to be long enough), the
+// rest in the next phase A; the next K tile's first YK
 // k-steps of fragments read whole in phase Y (into the registers of k-steps
 // whose instructions all precede phase Y), then k-step YK's B fragments and
 // its first YA A fragments, the rest in the next phase A (the instruction
@@ -498,7 +502,7 @@ struct Bf16Ring64 {                   // 128-byte rows
     static constexpr int ELT = 2;
     static constexpr int BK = 64;
     static constexpr int NKS = 4;
-    static constexpr int KA = 1, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
+    static constexpr int AM = 16, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
     static constexpr bool MX = true, SG = false, FP4 = false;
@@ -507,7 +511,7 @@ struct Mxfp8Ring128 {                 // 128-byte rows
     static constexpr int ELT = 1;
     static constexpr int BK = 128;
     static constexpr int NKS = 2;
-    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 2, YK = 0;
+    static constexpr int AM = 16, XM = 12, LX = 12, LY = 4, YA = 2, YK = 0;
 };
 // MX with K a multiple of 512 (whole groups of 16 scale blocks): the scale
 // words of four K tiles travel together, 16 bytes per row, in a separate
@@ -516,7 +520,7 @@ struct Mxfp8Ring128 {                 // 128-byte rows
 // instruction doubled the K tile's line requests.
 struct Mxfp8Ring128G : Mxfp8Ring128 {
     static constexpr bool SG = true;
-    static constexpr int KA = 1, XM = 12, LX = 12, LY = 4, YA = 1, YK = 0;
+    static constexpr int AM = 12, XM = 16, LX = 14, LY = 2, YA = 1, YK = 0;
 };
 // E5M2 elements have E4M3's byte layout and fragment map: the same kernels
 // with the instruction's format code 1.
@@ -543,7 +547,7 @@ struct Fp4Ring128G {
     static constexpr int ELT = 1;
     static constexpr int BK = 128;    // K units (bytes) per K tile
     static constexpr int NKS = 4;
-    static constexpr int KA = 1, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
+    static constexpr int AM = 16, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
@@ -558,11 +562,11 @@ void gemm_early(GemmArgs p, int group_m)
     constexpr int GK = 16 / BPK;                           // K tiles per scale group
     constexpr int SW = BPK / 4;                            // scale words per row and K tile
     constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
-    constexpr int KA = Op::KA, AM = KA * NM;                // phase A
-    constexpr int XM = Op::XM, YM = (NKS - KA) * NM - XM;  // phases X and Y
+    constexpr int AM = Op::AM;                             // phase A
+    constexpr int XM = Op::XM, YM = NKS * NM - AM - XM;    // phases X and Y
     constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA, YK = Op::YK;
     static_assert(G::CH == 8, "128-byte LDS rows");
-    static_assert(XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
+    static_assert(AM > 0 && XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
     static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
     static_assert(YK >= 0 && YK < NKS && AM + XM >= (YK + 1) * NM,
                   "phase Y overwrites only k-steps whose instructions precede it");
@@ -884,7 +888,7 @@ void gemm_early(GemmArgs p, int group_m)
                 acc[i][j] = zero16();
         for (int kt = 0; kt < nk; ++kt, ++g) {
             const int stage = g & 1;
-            // phase A: the first KA k-steps; the K tile's other fragments (its
+            // phase A: the first AM instructions; the K tile's other fragments (its
             // tail) into registers; the last loads of K tile g+1
             read_tail(stage);
             issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
