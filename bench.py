@@ -361,8 +361,9 @@ def main():
                 "kernel": f"{dom} (level {per_workload[dom]['level']})",
                 "flops_per_launch": flops[dom], "us_per_launch": per_ms[dom] * 1e3}
     # the same kernel against the rate its instruction sustains with no memory
-    # traffic at all (the chip's power-limited matrix-core ceiling)
-    loop = ceiling["bf16_32x32x16" if dom.startswith("bf16") else "mxfp8_32x32x64"]["tflops"]
+    # traffic at all (the chip's power-limited matrix-core ceiling); the
+    # default bf16 kernel for whole 256x256 bf16 tiles runs 16x16x32
+    loop = ceiling["bf16_16x16x32" if dom.startswith("bf16") else "mxfp8_32x32x64"]["tflops"]
     roofline["sustained_loop_tflops"] = loop
     roofline["frac_of_sustained_loop"] = per_workload[dom]["tflops"] / loop
 

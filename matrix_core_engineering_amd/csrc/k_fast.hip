@@ -172,6 +172,44 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
         }
 }
 
+// The same for 16x16 blocks (the 16x16x32 format): with the B operand fed
+// first, lane l holds row l % 16 and columns 4(l/16) .. +3 of each block.
+// Per block row and group of four blocks (16 rows x 64 columns), every lane
+// writes its four 8-byte pieces into the wave's buffer, then eight
+// consecutive lanes read back one row's 128 bytes and store 16 bytes each.
+template <class G, int TI, int TJ>
+__device__ __forceinline__ void store_tile_lds16(const GemmArgs &p, floatx4 (&acc)[TI][TJ], int m_tile,
+                                                 int n_tile, int wm, int wn, int lane, char *buf)
+{
+    static_assert(TJ % 4 == 0, "blocks staged in fours");
+    const int l16 = lane & 15, q = lane >> 4;
+    const int rrow = lane >> 3, rchunk = lane & 7;       // read-back position
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int jq = 0; jq < TJ / 4; ++jq) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const floatx4 &a = acc[i][4 * jq + jj];
+                *(u16x4 *)(buf + l16 * EPI_PITCH + jj * 32 + q * 8) =
+                    u16x4{f32_to_bf16_rne(p.alpha * a[0]), f32_to_bf16_rne(p.alpha * a[1]),
+                          f32_to_bf16_rne(p.alpha * a[2]), f32_to_bf16_rne(p.alpha * a[3])};
+            }
+            wait_lgkm0();
+            uint16_t *c0 = (uint16_t *)p.C + (size_t)(m_tile + wm * G::WM + i * 16) * p.ldc + n_tile +
+                           wn * G::WN + jq * 64 + rchunk * 8;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int row = s * 8 + rrow;
+                const intx4 v = *(const intx4 *)(buf + row * EPI_PITCH + rchunk * 16);
+                *(intx4 *)(c0 + (size_t)row * p.ldc) = v;
+            }
+            // the next round's writes may not overtake these reads
+            wait_lgkm0();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
 template <class Op, int BM, int BN, int STAGES, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fast(GemmArgs p, int group_m)
@@ -503,9 +541,23 @@ struct Bf16Ring64 {                   // 128-byte rows
     static constexpr int BK = 64;
     static constexpr int NKS = 4;
     static constexpr int AM = 16, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
+    static constexpr bool S16 = false;
+};
+// bf16 on the 16x16x32 instruction, which sustains 4-7% more flops than
+// 32x32x16 at the chip's power limit (measured with the ceiling loop): each
+// wave's 128x128 tile is 8x8 blocks of 16x16, a K tile two k-steps of 32 K
+// (128 instructions of 16 clocks, the same 32 fragment reads per K tile).
+// A fragment is 16 rows x 32 K: lane l reads row l % 16 at logical chunk
+// 4ks + l / 16 of its 128-byte row; the swizzle swz8h keeps both 16-lane
+// read groups of every fragment read conflict-free.  Whole bf16 tiles with
+// the LDS-staged epilogue only.
+struct Bf16Ring64S16 : Bf16Ring64 {
+    static constexpr bool S16 = true;
+    static constexpr int NKS = 2;
+    static constexpr int AM = 32, XM = 88, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
-    static constexpr bool MX = true, SG = false, FP4 = false;
+    static constexpr bool MX = true, SG = false, FP4 = false, S16 = false;
     static constexpr int EPU = 1;
     static constexpr int FMT = MX_E4M3;
     static constexpr int ELT = 1;
@@ -541,7 +593,7 @@ struct E5m2Ring128G : Mxfp8Ring128G {
 // two scale words per row and K tile, a scale group (16 bytes per row)
 // covers two K tiles.
 struct Fp4Ring128G {
-    static constexpr bool MX = true, SG = true, FP4 = true;
+    static constexpr bool MX = true, SG = true, FP4 = true, S16 = false;
     static constexpr int EPU = 2;
     static constexpr int FMT = MX_E2M1;
     static constexpr int ELT = 1;
@@ -556,18 +608,22 @@ void gemm_early(GemmArgs p, int group_m)
 {
     using G = RingGeometry<Op, BM, BN, 2>;
     constexpr int NKS = Op::NKS;
-    constexpr int NM = G::TI * G::TJ;                      // matrix-core instructions per k-step
+    // matrix-core blocks of 32x32 (16x16 on the 16x16x32 format) per wave tile
+    constexpr bool S16 = Op::S16;
+    constexpr int BLK = S16 ? 16 : 32, TI = G::WM / BLK, TJ = G::WN / BLK;
+    static_assert(!S16 || EPI == EPI_BF16_LDS, "16x16 blocks: whole bf16 tiles staged through LDS");
+    constexpr int NM = TI * TJ;                            // matrix-core instructions per k-step
     constexpr int RPF = Op::MX && !Op::FP4 ? 2 : 1;       // LDS reads per fragment
     constexpr int BPK = Op::BK * Op::EPU / 32;             // scale blocks per K tile
     constexpr int GK = 16 / BPK;                           // K tiles per scale group
     constexpr int SW = BPK / 4;                            // scale words per row and K tile
-    constexpr int FRAG_READS = (G::TI + G::TJ) * RPF;
+    constexpr int FRAG_READS = (TI + TJ) * RPF;
     constexpr int AM = Op::AM;                             // phase A
     constexpr int XM = Op::XM, YM = NKS * NM - AM - XM;    // phases X and Y
     constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA, YK = Op::YK;
     static_assert(G::CH == 8, "128-byte LDS rows");
     static_assert(AM > 0 && XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
-    static_assert(YA >= 1 && YA <= G::TI, "first A fragment read in phase Y");
+    static_assert(YA >= 1 && YA <= TI, "first A fragment read in phase Y");
     static_assert(YK >= 0 && YK < NKS && AM + XM >= (YK + 1) * NM,
                   "phase Y overwrites only k-steps whose instructions precede it");
     static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
@@ -575,7 +631,7 @@ void gemm_early(GemmArgs p, int group_m)
     // A and B row and a 1 KiB sink for the loads of iterations that load no
     // group, then (staged epilogue) one buffer per wave
     constexpr int SG_BYTES = Op::SG ? 2 * (BM + BN) * 16 + 1024 : 0;
-    constexpr int EPI_RR = Op::SG ? 16 : 32;
+    constexpr int EPI_RR = Op::SG || S16 ? 16 : 32;
     constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? 4 * epi_wave_bytes<EPI_RR>() : 0;
     static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + SG_BYTES + EPI_BYTES];
@@ -606,8 +662,9 @@ void gemm_early(GemmArgs p, int group_m)
     // row (wave*N + t)*8 + l/8 at physical chunk l%8; swz8(row) = (l/8) ^
     // (t&1) (bit 3 of the row is the parity of wave*N + t, N even).
     const int lrow = lane >> 3;
-    const int kc_even = ((lane & 7) ^ lrow) * G::EPC;
-    const int kc_odd = ((lane & 7) ^ lrow ^ 1) * G::EPC;
+    // (16x16x32 format: swz8h(row) = swz8h(lrow), the same for every load)
+    const int kc_even = ((lane & 7) ^ (S16 ? swz8h(lrow) : lrow)) * G::EPC;
+    const int kc_odd = ((lane & 7) ^ (S16 ? swz8h(lrow) : lrow ^ 1)) * G::EPC;
     uint32_t va[G::NA], vb[G::NB];
 #pragma unroll
     for (int t = 0; t < G::NA; ++t)
@@ -695,15 +752,20 @@ void gemm_early(GemmArgs p, int group_m)
     };
 
     typedef typename std::conditional<Op::MX, intx8, bf16x8>::type Frag;
-    Frag fa[NKS][G::TI], fb[NKS][G::TJ];   // one register set per k-step of a K tile
-    int sc_a[G::TI][SW], sc_b[G::TJ][SW];  // MX scale words of the K tile being consumed
-    int sn_a[G::TI][SW], sn_b[G::TJ][SW];  // ... of the next K tile
-    // rows a lane reads differ by multiples of 32: the swizzle is lane-constant
-    const int swz_lane = swz8(l32);
+    Frag fa[NKS][TI], fb[NKS][TJ];   // one register set per k-step of a K tile
+    int sc_a[TI][SW], sc_b[TJ][SW];  // MX scale words of the K tile being consumed
+    int sn_a[TI][SW], sn_b[TJ][SW];  // ... of the next K tile
+    // rows a lane reads differ by multiples of 32 (16x16x32 format: 16, with
+    // the swizzle swz8h): the swizzle is lane-constant
+    const int lr = S16 ? (lane & 15) : l32;               // row inside a block
+    const int swz_lane = S16 ? swz8h(lr) : swz8(l32);
 
     // fragment i (A) or j (B) of k-step ks from `stage`
     auto frag = [&](const char *rowp, int ks) -> Frag {
-        if constexpr (!Op::MX) {
+        if constexpr (S16) {
+            // lane l: k = 32ks + 8(l/16) .. +7
+            return *(const bf16x8 *)(rowp + ((4 * ks + (lane >> 4)) ^ swz_lane) * 16);
+        } else if constexpr (!Op::MX) {
             return *(const bf16x8 *)(rowp + ((2 * ks + h) ^ swz_lane) * 16);
         } else if constexpr (Op::FP4) {
             // lane (l32, h): block 2ks + h = elements 64ks + 32h .. +31; the
@@ -718,11 +780,11 @@ void gemm_early(GemmArgs p, int group_m)
         }
     };
     auto read_a = [&](int ks, int stage, int i) {
-        fa[ks][i] = frag(smem + stage * G::STAGE_BYTES + (wm * G::WM + i * 32 + l32) * G::ROWB, ks);
+        fa[ks][i] = frag(smem + stage * G::STAGE_BYTES + (wm * G::WM + i * BLK + lr) * G::ROWB, ks);
     };
     auto read_b = [&](int ks, int stage, int j) {
         fb[ks][j] = frag(smem + stage * G::STAGE_BYTES + G::A_BYTES +
-                             (wn * G::WN + j * 32 + l32) * G::ROWB, ks);
+                             (wn * G::WN + j * BLK + lr) * G::ROWB, ks);
     };
 
     // MX: each lane's scale word of K tile kt (blocks 4kt .. 4kt+3 of its
@@ -738,13 +800,13 @@ void gemm_early(GemmArgs p, int group_m)
             const uint2 *SAs = (const uint2 *)(smem + G::LDS_BYTES + ((gk >> 1) & 1) * (BM + BN) * 16) + (gk & 1);
             const uint2 *SBs = SAs + BM * 2;
 #pragma unroll
-            for (int i = 0; i < G::TI; ++i) {
+            for (int i = 0; i < TI; ++i) {
                 const uint2 w = SAs[(wm * G::WM + i * 32 + l32) * 2];
                 sn_a[i][0] = (int)(w.x >> (8 * h));
                 sn_a[i][SW - 1] = (int)(w.y >> (8 * h));
             }
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j) {
+            for (int j = 0; j < TJ; ++j) {
                 const uint2 w = SBs[(wn * G::WN + j * 32 + l32) * 2];
                 sn_b[j][0] = (int)(w.x >> (8 * h));
                 sn_b[j][SW - 1] = (int)(w.y >> (8 * h));
@@ -754,10 +816,10 @@ void gemm_early(GemmArgs p, int group_m)
                 (const uint32_t *)(smem + G::LDS_BYTES + ((gk >> 2) & 1) * (BM + BN) * 16) + (gk & 3);
             const uint32_t *SBs = SAs + BM * 4;
 #pragma unroll
-            for (int i = 0; i < G::TI; ++i)
+            for (int i = 0; i < TI; ++i)
                 sn_a[i][0] = (int)(SAs[(wm * G::WM + i * 32 + l32) * 4] >> (8 * h));
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
+            for (int j = 0; j < TJ; ++j)
                 sn_b[j][0] = (int)(SBs[(wn * G::WN + j * 32 + l32) * 4] >> (8 * h));
         } else if constexpr (Op::MX) {
             const uint32_t *SAs =
@@ -770,10 +832,10 @@ void gemm_early(GemmArgs p, int group_m)
                 force = 0x7F7F7F7Fu & ~keep;
             }
 #pragma unroll
-            for (int i = 0; i < G::TI; ++i)
+            for (int i = 0; i < TI; ++i)
                 sn_a[i][0] = (int)(((SAs[wm * G::WM + i * 32 + l32] & keep) | force) >> (8 * h));
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
+            for (int j = 0; j < TJ; ++j)
                 sn_b[j][0] = (int)(((SBs[wn * G::WN + j * 32 + l32] & keep) | force) >> (8 * h));
         }
     };
@@ -800,16 +862,18 @@ void gemm_early(GemmArgs p, int group_m)
         }
     };
 
-    floatx16 acc[G::TI][G::TJ];
+    typename std::conditional<S16, floatx4, floatx16>::type acc[TI][TJ];
     // matrix-core instructions q in [LO, HI) of the K tile, q = ks*NM + i*TJ + j
     auto mfmas = [&](int lo, int hi) {
 #pragma unroll
         for (int q = lo; q < hi; ++q) {
-            const int ks = q / NM, i = (q % NM) / G::TJ, j = q % G::TJ;
+            const int ks = q / NM, i = (q % NM) / TJ, j = q % TJ;
             // MX: k-step ks takes blocks 2ks, 2ks+1 of the K tile: byte
             // 2 (ks % 2) of scale word ks / 2 (the upper half-wave's words
             // are shifted one byte down, so it supplies block 2ks + 1)
-            if constexpr (!Op::MX)
+            if constexpr (S16)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+            else if constexpr (!Op::MX)
                 acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
             else if (ks % 2 == 0)
                 acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j][ks / 2],
@@ -827,30 +891,30 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
         for (int ks = 0; ks < YK; ++ks) {
 #pragma unroll
-            for (int i = 0; i < G::TI; ++i)
+            for (int i = 0; i < TI; ++i)
                 read_a(ks, stage, i);
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
+            for (int j = 0; j < TJ; ++j)
                 read_b(ks, stage, j);
         }
 #pragma unroll
         for (int i = 0; i < YA; ++i)
             read_a(YK, stage, i);
 #pragma unroll
-        for (int j = 0; j < G::TJ; ++j)
+        for (int j = 0; j < TJ; ++j)
             read_b(YK, stage, j);
     };
     auto read_tail = [&](int stage) {
 #pragma unroll
-        for (int i = YA; i < G::TI; ++i)
+        for (int i = YA; i < TI; ++i)
             read_a(YK, stage, i);
 #pragma unroll
         for (int ks = YK + 1; ks < NKS; ++ks) {
 #pragma unroll
-            for (int i = 0; i < G::TI; ++i)
+            for (int i = 0; i < TI; ++i)
                 read_a(ks, stage, i);
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
+            for (int j = 0; j < TJ; ++j)
                 read_b(ks, stage, j);
         }
     };
@@ -869,10 +933,10 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
     for (int w = 0; w < SW; ++w) {
 #pragma unroll
-        for (int i = 0; i < G::TI; ++i)
+        for (int i = 0; i < TI; ++i)
             sc_a[i][w] = sn_a[i][w];
 #pragma unroll
-        for (int j = 0; j < G::TJ; ++j)
+        for (int j = 0; j < TJ; ++j)
             sc_b[j][w] = sn_b[j][w];
     }
 
@@ -882,10 +946,10 @@ void gemm_early(GemmArgs p, int group_m)
     int pn_kt = 1, pn_stage = 1;
     for (int r = 0; r < my_tiles; ++r) {
 #pragma unroll
-        for (int i = 0; i < G::TI; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int j = 0; j < G::TJ; ++j)
-                acc[i][j] = zero16();
+            for (int j = 0; j < TJ; ++j)
+                acc[i][j] = {};
         for (int kt = 0; kt < nk; ++kt, ++g) {
             const int stage = g & 1;
             // phase A: the first AM instructions; the K tile's other fragments (its
@@ -894,7 +958,7 @@ void gemm_early(GemmArgs p, int group_m)
             issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
             mfmas(0, AM);
             {
-                constexpr int R = (G::TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
+                constexpr int R = (TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
                 constexpr int PER = (R + AM - 1) / AM;
 #pragma unroll
                 for (int x = 0; x < AM; ++x) {
@@ -938,7 +1002,7 @@ void gemm_early(GemmArgs p, int group_m)
             pn_stage = stage;
             mfmas(AM + XM, NKS * NM);
             {
-                constexpr int R = YK * FRAG_READS + (YA + G::TJ) * RPF + (Op::MX ? G::TI + G::TJ : 0);
+                constexpr int R = YK * FRAG_READS + (YA + TJ) * RPF + (Op::MX ? TI + TJ : 0);
                 constexpr int PER = (R + YM - 1) / YM;
 #pragma unroll
                 for (int x = 0; x < YM; ++x) {
@@ -963,17 +1027,20 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
                 for (int w = 0; w < SW; ++w) {
 #pragma unroll
-                    for (int i = 0; i < G::TI; ++i)
+                    for (int i = 0; i < TI; ++i)
                         sc_a[i][w] = sn_a[i][w];
 #pragma unroll
-                    for (int j = 0; j < G::TJ; ++j)
+                    for (int j = 0; j < TJ; ++j)
                         sc_b[j][w] = sn_b[j][w];
                 }
             }
         }
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
-        if constexpr (EPI == EPI_BF16_LDS)
+        if constexpr (S16)
+            store_tile_lds16<G, TI, TJ>(p, acc, tm * BM, tn * BN, wm, wn, lane,
+                                        smem + G::LDS_BYTES + SG_BYTES + wave * epi_wave_bytes<EPI_RR>());
+        else if constexpr (EPI == EPI_BF16_LDS)
             store_tile_lds<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane,
                                               smem + G::LDS_BYTES + SG_BYTES +
                                                   wave * epi_wave_bytes<EPI_RR>());
@@ -1327,6 +1394,27 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
     return hipGetLastError();
 }
 
+// bf16 levels 5-6 on 256x256 tiles: whole bf16 tiles that take the
+// LDS-staged epilogue run the 16x16x32 format (more flops per clock at the
+// power limit), everything else the 32x32x16 one.
+constexpr bool kBf16On16x16 = true;
+
+template <bool PERSIST>
+hipError_t launch_early_bf16(const GemmArgs &p, hipStream_t s)
+{
+    if (!kBf16On16x16 || !whole_bf16(p, 256, 256) || p.ldc % 8 != 0 || (uintptr_t)p.C % 16 != 0)
+        return launch_early<Bf16Ring64, 256, 256, PERSIST>(p, s);
+    const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    const int ntiles = tiles_m * tiles_n;
+    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    if (PERSIST && ntiles <= num_cus())
+        return launch_early_bf16<false>(p, s);
+    const int grid = PERSIST ? (ntiles < num_cus() ? ntiles : num_cus()) : ntiles;
+    hipLaunchKernelGGL((gemm_early<Bf16Ring64S16, 256, 256, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
+                       s, p, group_m);
+    return hipGetLastError();
+}
+
 template <class Op, bool PERSIST>
 hipError_t launch_pingpong(const GemmArgs &p, hipStream_t s)
 {
@@ -1368,11 +1456,11 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
         return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
     case 5:
         if (big && ring_ok)
-            return launch_early<Bf16Ring64, 256, 256, false>(p, s);
+            return launch_early_bf16<false>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
     case 6:
         if (big && ring_ok)
-            return launch_early<Bf16Ring64, 256, 256, true>(p, s);
+            return launch_early_bf16<true>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
     case 7:
         if (p.K > 3 * Bf16Ring::BK)

@@ -61,6 +61,18 @@ MCE_HD int swz8(int row)
     return (row & 7) ^ ((row >> 3) & 1);
 }
 
+// XOR swizzle of 128-byte rows read by the 16x16x32 instruction: a fragment
+// read takes rows base + (lane & 15) (base a multiple of 16) at logical
+// chunk 4ks + (lane >> 4).  Of the two 16-lane read groups of a 32-lane half
+// (the lane quads of equal parity of (lane >> 2) & 7), each holds eight even
+// and eight odd rows, four at chunk c and four at chunk c ^ 1; row & 6 puts
+// the first four on even slots and the other four on odd ones, so each
+// parity of row covers all eight slots: the read is conflict-free.
+MCE_HD int swz8h(int row)
+{
+    return row & 6;
+}
+
 // XOR swizzle for 64-byte LDS rows (4 chunks of 16 bytes).  Among rows
 // r..r+7 (r even-aligned to 8) the rows of one parity map a logical chunk to
 // 4 distinct slots, and among rows r, r+4, r+8, r+12 it maps to 4 distinct

@@ -25,6 +25,7 @@ void h_grouped_tile(int id, int tm_, int tn_, int g, int *tm, int *tn)
 { mce::grouped_tile(id, tm_, tn_, g, *tm, *tn); }
 int h_persistent_tile_id(int wg, int nwg, int r) { return mce::persistent_tile_id(wg, nwg, r); }
 int h_swz8(int r) { return mce::swz8(r); }
+int h_swz8h(int r) { return mce::swz8h(r); }
 int h_swz4(int r) { return mce::swz4(r); }
 int h_swz4q(int r) { return mce::swz4q(r); }
 int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 0; }
@@ -170,9 +171,33 @@ def test_swz8_fragment_reads_conflict_free(lib, base, chunk):
     assert cycles_extra(addrs, 16, "read") == 0
 
 
+@pytest.mark.parametrize("base", range(0, 256, 16))
+@pytest.mark.parametrize("ks", range(2))
+def test_swz8h_fragment_reads_conflict_free(lib, base, ks):
+    """16x16x32 format, 128-byte rows: lane l reads row base + l % 16 at
+    logical chunk 4ks + l / 16.  The 32x32 swizzle would not do here."""
+    def addrs(swz):
+        return [(base + (l & 15)) * 128 + (((4 * ks + (l >> 4)) ^ swz(base + (l & 15))) * 16)
+                for l in range(64)]
+    assert cycles_extra(addrs(lib.h_swz8h), 16, "read") == 0
+    assert cycles_extra(addrs(lib.h_swz8), 16, "read") > 0
+
+
+def test_swz8h_direct_loads_fill_each_row_once(lib):
+    """A direct load writes lane l at row l / 8, slot l % 8 of its eight
+    rows, fetching logical chunk (l % 8) ^ swz8h(l / 8); rows of a load start
+    at multiples of 8, so swz8h(row) = swz8h(l / 8)."""
+    for first in range(0, 256, 8):
+        for l8 in range(8):
+            got = sorted(s ^ lib.h_swz8h(l8) for s in range(8))
+            assert got == list(range(8))
+            assert lib.h_swz8h(first + l8) == lib.h_swz8h(l8)
+
+
 def test_swizzles_are_permutations_per_row(lib):
     for r in range(512):
         assert sorted(c ^ lib.h_swz8(r) for c in range(8)) == list(range(8))
+        assert sorted(c ^ lib.h_swz8h(r) for c in range(8)) == list(range(8))
         assert sorted(c ^ lib.h_swz4(r) for c in range(4)) == list(range(4))
         assert sorted(c ^ lib.h_swz4q(r) for c in range(4)) == list(range(4))
 
