@@ -570,24 +570,26 @@ def test_whole_tiles_bf16_output_bitwise(level, fmt):
 
 
 @pytest.mark.parametrize("level", [5, 6])
-@pytest.mark.parametrize("shape", [(4096, 4352, 512), (8448, 4096, 256)], ids=["272tiles", "528tiles"])
-def test_whole_tiles_bf16_output_persistent_tail(level, shape):
+@pytest.mark.parametrize("shape,alpha", [((4096, 4352, 512), 1.0), ((8448, 4096, 256), 0.5)],
+                         ids=["272tiles", "528tiles-alpha0.5"])
+def test_whole_tiles_bf16_output_persistent_tail(level, shape, alpha):
     """Whole 256x256 bf16 tiles (the 16x16x32 format) with more tiles than
     CUs and a tile count that is not a multiple of the grid: at level 6 some
     workgroups of the persistent grid take one tile more than others, so the
-    ring runs across a ragged number of tiles.  Exact-integer inputs, the
-    whole bf16 result compared bitwise with the correctly rounded exact
-    product."""
+    ring runs across a ragged number of tiles.  Exact-integer inputs (alpha
+    0.5 keeps alpha * sum exact), the whole bf16 result compared bitwise with
+    the correctly rounded exact product."""
     M, N, K = shape
-    announce(f"whole tiles persistent tail level {level} {shape}")
-    p = integer_problem(M, N, K, c_dtype=OUT_BF16, seed=7400 + level + M, name="whole_tiles_tail")
+    announce(f"whole tiles persistent tail level {level} {shape} alpha {alpha}")
+    p = integer_problem(M, N, K, c_dtype=OUT_BF16, seed=7400 + level + M, alpha=alpha,
+                        name="whole_tiles_tail")
     r = run_level(p, level)
     assert r is not None
     raw = r[1]
     A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
     B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
     from helpers import f64_to_bf16_bits
-    expect = f64_to_bf16_bits(A @ B)
+    expect = f64_to_bf16_bits(alpha * (A @ B))
     bad = np.argwhere(raw != expect)
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
 
