@@ -28,7 +28,11 @@
 // The matrix-core instruction is fed B as its first operand and A as its
 // second, so each lane's 16 accumulators are C^T: lane l holds row
 // m = l % 32 and four groups of four consecutive columns, which the
-// epilogue writes as 8-byte (bf16) or 16-byte (fp32) vectors.
+// epilogue writes as 8-byte (bf16) or 16-byte (fp32) vectors.  Whole bf16
+// 256x256 tiles instead run the 16x16x32 instruction (Bf16Ring64S16: 16x16
+// blocks, four accumulators per lane and block, row l % 16, columns
+// 4(l/16) .. +3), which sustains more flops per clock at the chip's power
+// limit.
 //
 // The ring protocol (one barrier per K tile, no mbarrier on gfx950):
 //   ready[s]: each wave waits for its own direct loads into stage s
@@ -647,7 +651,6 @@ void gemm_early(GemmArgs p, int group_m)
     const int nwg = gridDim.x, wg = blockIdx.x;
     const int first = xcd_major(wg, nwg);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
-    const int total = my_tiles * nk;
 
     const int nblk = (p.K * Op::EPU + 31) / 32;            // MX scale blocks per row
 
