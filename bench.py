@@ -22,8 +22,10 @@ shape (no memory traffic), the power-limited ceiling the GEMMs run under;
 Modes for profiling (no JSON): --only bf16|mxfp8|copy|e4m3|e5m2|e2m3|e3m2|e2m1
 --reps R runs just that kernel R times after one warm-up (copy: a 1 GiB
 device-to-device copy, the calibration of the HBM byte counters; the MX
-element-format names: the 8192^3 MX GEMM in that format).  --only loop prints
-the matrix-core loop rates alone.
+element-format names: the 8192^3 MX GEMM in that format; cfg1-cfg3: the
+single-tile, 4096^3 and ragged workloads).  --only loop prints the
+matrix-core loop rates alone.  --configs prints one JSON line timing every
+standard workload against its own roofline.
 --mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
 element format at its default level, with W warm-up and K timed launches.
 """
@@ -64,8 +66,11 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop"] + list(MX_FORMAT_NAMES),
+    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop", "cfg1", "cfg2", "cfg3"]
+                    + list(MX_FORMAT_NAMES),
                     default=None)
+    ap.add_argument("--configs", action="store_true",
+                    help="time every standard workload against its roofline (one JSON line)")
     ap.add_argument("--mx-formats", action="store_true",
                     help="time the 8192^3 MX GEMM in every element format (one JSON line)")
     ap.add_argument("--reps", type=int, default=3)
@@ -225,6 +230,67 @@ def matrix_core_ceiling(dev, stream, iters=2000, reps=3):
     return res
 
 
+def algorithmic_bytes(p):
+    """HBM bytes a GEMM must move at least: A, B and the MX scales read once,
+    C read when beta != 0, C written once."""
+    elt = 1 if p.SA is not None else 2
+    c_elt = 2 if p.c_dtype == 1 else 4
+    scales = (p.M + p.N) * ((p.K + 31) // 32) if p.SA is not None else 0
+    c_bytes = p.M * p.N * c_elt
+    return p.M * p.K * elt + p.K * p.N * elt + scales + c_bytes * (2 if p.beta != 0 else 1)
+
+
+def configs(args, dev, stream):
+    """One JSON line: every standard workload through its default entry
+    point, each against the roofline that bounds it (matrix cores, or HBM
+    when its flops per algorithmic byte are below the ridge; a problem of
+    fewer 128x128 tiles than CUs occupies part of one CU set and is
+    reported as latency-bound, with no roofline fraction).  The
+    HBM-bound ragged workload is timed cold: a 512 MiB fill before every
+    launch evicts L2 and the Infinity Cache, and only the GEMM is timed."""
+    import torch
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    for cfg in (1, 2, 3, 4, 5):
+        w = Workload(cfg, dev)
+        p = w.p
+        peak = PEAK_FP8 if p.SA is not None else PEAK_BF16
+        nbytes = algorithmic_bytes(p)
+        latency = ((p.M + 127) // 128) * ((p.N + 127) // 128) < 256
+        hbm_bound = not latency and p.flops / nbytes < peak * 1e12 / (PEAK_HBM * 1e9)
+        for _ in range(args.warmup):
+            w.run(stream)
+        torch.cuda.synchronize()
+        # launches back to back (the scrub fill, when there is one, runs on
+        # the same stream just before each launch); events around each launch
+        evs = []
+        for _ in range(args.steps):
+            if hbm_bound:
+                scrub.fill_(cfg)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            w.run(stream)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        times = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+        us = float(np.median(times))
+        tf = p.flops / (us * 1e-6) / 1e12
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[p.name] = {"level": w.level(), "us_median": us, "us_min": float(min(times)),
+                       "tflops": tf, "algorithmic_bytes": nbytes, "gb_per_s": gbs,
+                       "bound": "latency" if latency else "hbm" if hbm_bound else "mfma",
+                       "frac": None if latency else gbs / PEAK_HBM if hbm_bound else tf / peak,
+                       "peak": None if latency else PEAK_HBM if hbm_bound else peak,
+                       "timed": "cold (512 MiB scrub before each launch)" if hbm_bound else "warm"}
+        del w
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "GEMM time per standard workload vs its roofline", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                      "per_config": res}), flush=True)
+
+
 def read_traffic():
     """HBM bytes per launch of the bf16 kernel from the committed counter
     summary, or None if it is missing or was taken on other kernel code."""
@@ -301,6 +367,9 @@ def main():
     if args.mx_formats:
         mx_formats(args, dev, stream)
         return
+    if args.configs:
+        configs(args, dev, stream)
+        return
     if args.only == "loop":
         res = matrix_core_ceiling(dev, stream, reps=args.reps)
         print(json.dumps({"matrix_core_loop": res}), flush=True)
@@ -313,7 +382,7 @@ def main():
         print(f"ran {args.only} level {work.level()} x {args.reps + 1}", flush=True)
         return
     if args.only:
-        work = Workload(4 if args.only == "bf16" else 5, dev)
+        work = Workload({"bf16": 4, "mxfp8": 5, "cfg1": 1, "cfg2": 2, "cfg3": 3}[args.only], dev)
         for _ in range(args.reps + 1):
             work.run(stream)
         torch.cuda.synchronize()
