@@ -25,7 +25,8 @@ device-to-device copy, the calibration of the HBM byte counters; the MX
 element-format names: the 8192^3 MX GEMM in that format; cfg1-cfg3: the
 single-tile, 4096^3 and ragged workloads).  --only loop prints the
 matrix-core loop rates alone.  --configs prints one JSON line timing every
-standard workload against its own roofline.
+standard workload against its own roofline; --levels one line timing every
+level of the ladder on every standard workload.
 --mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
 element format at its default level, with W warm-up and K timed launches.
 """
@@ -69,6 +70,8 @@ def parse_args():
     ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop", "cfg1", "cfg2", "cfg3"]
                     + list(MX_FORMAT_NAMES),
                     default=None)
+    ap.add_argument("--levels", action="store_true",
+                    help="time every level on every standard workload (one JSON line)")
     ap.add_argument("--configs", action="store_true",
                     help="time every standard workload against its roofline (one JSON line)")
     ap.add_argument("--mx-formats", action="store_true",
@@ -108,6 +111,20 @@ class Workload:
         return mce.gemm_mxfp8(p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.SA, p.ld_sa,
                               self.B, p.ldb, p.b_col_major, self.SB, p.ld_sb, self.C, p.ldc,
                               p.c_col_major, p.c_dtype, p.alpha, p.beta, stream=stream)
+
+    def run_level(self, level, stream):
+        """The same call at a fixed level; returns the library's status."""
+        import matrix_core_engineering_amd as mce
+        p = self.p
+        if p.SA is None:
+            return mce.gemm_bf16_level(level, p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.B,
+                                       p.ldb, p.b_col_major, self.C, p.ldc, p.c_col_major,
+                                       p.c_dtype, p.alpha, p.beta, stream=stream,
+                                       raise_on_error=False)
+        return mce.gemm_mxfp8_level(level, p.M, p.N, p.K, self.A, p.lda, p.a_col_major, self.SA,
+                                    p.ld_sa, self.B, p.ldb, p.b_col_major, self.SB, p.ld_sb,
+                                    self.C, p.ldc, p.c_col_major, p.c_dtype, p.alpha, p.beta,
+                                    stream=stream, raise_on_error=False)
 
     def level(self):
         import matrix_core_engineering_amd as mce
@@ -291,6 +308,42 @@ def configs(args, dev, stream):
                       "per_config": res}), flush=True)
 
 
+def levels(args, dev, stream):
+    """One JSON line: every level of the ladder on every standard workload
+    (warm, back to back, events around each launch, median), null where the
+    level declines the problem."""
+    import torch
+    import matrix_core_engineering_amd as mce
+    res = {}
+    for cfg in (1, 2, 3, 4, 5):
+        w = Workload(cfg, dev)
+        p = w.p
+        row = {}
+        for level in range(1, 8):
+            if w.run_level(level, stream) != mce.MCE_OK:
+                row[str(level)] = None
+                continue
+            for _ in range(args.warmup):
+                w.run_level(level, stream)
+            evs = []
+            for _ in range(args.steps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                w.run_level(level, stream)
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            row[str(level)] = {"us_median": us, "tflops": p.flops / (us * 1e-6) / 1e12}
+        res[p.name] = row
+        del w
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "GEMM time per level and standard workload", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                      "per_config": res}), flush=True)
+
+
 def read_traffic():
     """HBM bytes per launch of the bf16 kernel from the committed counter
     summary, or None if it is missing or was taken on other kernel code."""
@@ -369,6 +422,9 @@ def main():
         return
     if args.configs:
         configs(args, dev, stream)
+        return
+    if args.levels:
+        levels(args, dev, stream)
         return
     if args.only == "loop":
         res = matrix_core_ceiling(dev, stream, reps=args.reps)
