@@ -1400,12 +1400,10 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
 // bf16 levels 5-6 on 256x256 tiles: whole bf16 tiles that take the
 // LDS-staged epilogue run the 16x16x32 format (more flops per clock at the
 // power limit), everything else the 32x32x16 one.
-constexpr bool kBf16On16x16 = true;
-
 template <bool PERSIST>
 hipError_t launch_early_bf16(const GemmArgs &p, hipStream_t s)
 {
-    if (!kBf16On16x16 || !whole_bf16(p, 256, 256) || p.ldc % 8 != 0 || (uintptr_t)p.C % 16 != 0)
+    if (!whole_bf16(p, 256, 256) || p.ldc % 8 != 0 || (uintptr_t)p.C % 16 != 0)
         return launch_early<Bf16Ring64, 256, 256, PERSIST>(p, s);
     const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     const int ntiles = tiles_m * tiles_n;
