@@ -448,6 +448,17 @@ void gemm_fast(GemmArgs p, int group_m)
 // scalar offset.
 constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100;
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order:
+// a loop whose trip index is a compile-time constant in the body.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
 // 64-byte LDS rows (the role-specialised kernel)
 struct Bf16Ring {                     // 64-byte rows
     static constexpr bool MX = false, SG = false;
@@ -620,6 +631,7 @@ void gemm_early(GemmArgs p, int group_m)
     constexpr int RPF = Op::MX && !Op::FP4 ? 2 : 1;       // LDS reads per fragment
     constexpr int BPK = Op::BK * Op::EPU / 32;             // scale blocks per K tile
     constexpr int GK = 16 / BPK;                           // K tiles per scale group
+    constexpr int UNR = Op::SG ? GK : 1;                   // K tiles per K-loop trip
     constexpr int SW = BPK / 4;                            // scale words per row and K tile
     constexpr int FRAG_READS = (TI + TJ) * RPF;
     constexpr int AM = Op::AM;                             // phase A
@@ -632,9 +644,8 @@ void gemm_early(GemmArgs p, int group_m)
                   "phase Y overwrites only k-steps whose instructions precede it");
     static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
     // LDS: the two stages, then (scale groups) two buffers of 16 bytes per
-    // A and B row and a 1 KiB sink for the loads of iterations that load no
-    // group, then (staged epilogue) one buffer per wave
-    constexpr int SG_BYTES = Op::SG ? 2 * (BM + BN) * 16 + 1024 : 0;
+    // A and B row, then (staged epilogue) one buffer per wave
+    constexpr int SG_BYTES = Op::SG ? 2 * (BM + BN) * 16 : 0;
     constexpr int EPI_RR = Op::SG || S16 ? 16 : 32;
     constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? 4 * epi_wave_bytes<EPI_RR>() : 0;
     static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
@@ -846,18 +857,16 @@ void gemm_early(GemmArgs p, int group_m)
     // Scale groups: the 16 bytes (four K tiles) of each A and B row of the
     // group starting at K tile kt of the current (next) tile, into group
     // buffer buf; one load per wave and operand, lane l = row wave*64 + l.
-    // With `real` false the loads have no records (nothing is fetched) and
-    // write their zeros into the sink: issuing them every iteration keeps
-    // the loop free of branches, which would let the compiler sink the
-    // matrix-core instructions past the barriers.
-    auto issue_group = [&](bool next, int kt, int buf, bool real) {
+    // (The K loop issues them from the first of its GK unrolled K tiles: a
+    // run-time branch in the loop would let the compiler move matrix-core
+    // instructions past the barriers.)
+    auto issue_group = [&](bool next, int kt, int buf) {
         if constexpr (Op::SG) {
             const TileSpan &t = next ? nxt : cur;
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.sa, real ? t.nsa : 0u);
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.sb, real ? t.nsb : 0u);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.sa, t.nsa);
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.sb, t.nsb);
             char *gb = smem + G::LDS_BYTES + buf * (BM + BN) * 16;
-            char *sink = smem + G::LDS_BYTES + 2 * (BM + BN) * 16;   // shared by every wave
-            char *da = real ? gb + wave * 1024 : sink, *db = real ? gb + BM * 16 + wave * 1024 : sink;
+            char *da = gb + wave * 1024, *db = gb + BM * 16 + wave * 1024;
             const int soff = kt * BPK;
             const uint32_t voa = vsa, vob = vsb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)da, 16, voa, soff, 0, 0);
@@ -926,7 +935,7 @@ void gemm_early(GemmArgs p, int group_m)
     // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
     // issues (a direct load always writes LDS, so no placeholder load may
     // target a stage in use)
-    issue_group(false, 0, 0, true);                // scale group 0 (GK K tiles)
+    issue_group(false, 0, 0);                      // scale group 0 (GK K tiles)
     issue(0, G::LOADS, false, 0, 0);
     issue(0, LX + LY, false, 1, 1);
     wait_vmcnt<LX + LY>();                         // K tile 0 (and scale group 0) landed
@@ -953,90 +962,98 @@ void gemm_early(GemmArgs p, int group_m)
 #pragma unroll
             for (int j = 0; j < TJ; ++j)
                 acc[i][j] = {};
-        for (int kt = 0; kt < nk; ++kt, ++g) {
-            const int stage = g & 1;
-            // phase A: the first AM instructions; the K tile's other fragments (its
-            // tail) into registers; the last loads of K tile g+1
-            read_tail(stage);
-            issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
-            mfmas(0, AM);
-            {
-                constexpr int R = (TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
-                constexpr int PER = (R + AM - 1) / AM;
+        // With scale groups the K loop is unrolled by a group (GK K tiles;
+        // the host takes this path only when the K tiles come in whole
+        // groups), so the group load sits in the first copy at compile time:
+        // no branch in the loop and no placeholder loads in the others.
+        for (int kt0 = 0; kt0 < nk; kt0 += UNR) {
+            static_for<UNR>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                const int kt = kt0 + u;
+                const int stage = g & 1;
+                // phase A: the first AM instructions; the K tile's other fragments (its
+                // tail) into registers; the last loads of K tile g+1
+                read_tail(stage);
+                issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
+                mfmas(0, AM);
+                {
+                    constexpr int R = (TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
+                    constexpr int PER = (R + AM - 1) / AM;
 #pragma unroll
-                for (int x = 0; x < AM; ++x) {
+                    for (int x = 0; x < AM; ++x) {
+                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                        if (x * PER < R)
+                            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
+                        if (loads_after(x, AM, LA))
+                            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+                    }
+                }
+                // the waits and barriers are fences for the scheduler too: no
+                // matrix-core instruction may drift across them
+                __builtin_amdgcn_sched_barrier(0);
+                wait_lgkm0();
+                barrier();                             // free: stage `stage` read by every wave
+                __builtin_amdgcn_sched_barrier(0);
+                // phase X: the loads of K tile g+2 into the released stage begin
+                // (past the last K tile `lnext` holds: the zero-record resources)
+                const int kl = kt + 2;
+                const bool lnext = kl >= nk;
+                const int lkt = lnext ? kl - nk : kl;
+                issue(0, LX, lnext, lkt, stage);
+                mfmas(AM, AM + XM);
+#pragma unroll
+                for (int x = 0; x < XM; ++x) {
                     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    if (x * PER < R)
-                        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
-                    if (loads_after(x, AM, LA))
+                    if (loads_after(x, XM, LX))
                         __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
                 }
-            }
-            // the waits and barriers are fences for the scheduler too: no
-            // matrix-core instruction may drift across them
-            __builtin_amdgcn_sched_barrier(0);
-            wait_lgkm0();
-            barrier();                             // free: stage `stage` read by every wave
-            __builtin_amdgcn_sched_barrier(0);
-            // phase X: the loads of K tile g+2 into the released stage begin
-            // (past the last K tile `lnext` holds: the zero-record resources)
-            const int kl = kt + 2;
-            const bool lnext = kl >= nk;
-            const int lkt = lnext ? kl - nk : kl;
-            issue(0, LX, lnext, lkt, stage);
-            mfmas(AM, AM + XM);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<LX>();                      // this wave's loads of K tile g+1 landed
+                barrier();                             // ready: K tile g+1 in the other stage
+                __builtin_amdgcn_sched_barrier(0);
+                // phase Y: the rest of K tile g; K tile g+1's first fragments (its
+                // head)
+                read_head(stage ^ 1);
+                read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1);
+                issue(LX, LX + LY, lnext, lkt, stage);
+                pn_next = lnext;
+                pn_kt = lkt;
+                pn_stage = stage;
+                mfmas(AM + XM, NKS * NM);
+                {
+                    constexpr int R = YK * FRAG_READS + (YA + TJ) * RPF + (Op::MX ? TI + TJ : 0);
+                    constexpr int PER = (R + YM - 1) / YM;
 #pragma unroll
-            for (int x = 0; x < XM; ++x) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                if (loads_after(x, XM, LX))
-                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<LX>();                      // this wave's loads of K tile g+1 landed
-            barrier();                             // ready: K tile g+1 in the other stage
-            __builtin_amdgcn_sched_barrier(0);
-            // phase Y: the rest of K tile g; K tile g+1's first fragments (its
-            // head)
-            read_head(stage ^ 1);
-            read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1);
-            issue(LX, LX + LY, lnext, lkt, stage);
-            pn_next = lnext;
-            pn_kt = lkt;
-            pn_stage = stage;
-            mfmas(AM + XM, NKS * NM);
-            {
-                constexpr int R = YK * FRAG_READS + (YA + TJ) * RPF + (Op::MX ? TI + TJ : 0);
-                constexpr int PER = (R + YM - 1) / YM;
-#pragma unroll
-                for (int x = 0; x < YM; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    if (x * PER < R)
-                        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
-                    if (loads_after(x, YM, LY))
-                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+                    for (int x = 0; x < YM; ++x) {
+                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                        if (x * PER < R)
+                            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
+                        if (loads_after(x, YM, LY))
+                            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+                    }
                 }
-            }
-            if constexpr (Op::SG) {
-                // at a group's first K tile: the next group's scale words into
-                // the other group buffer, whose last reads (a group back)
-                // ended before this iteration's barrier 1; the wait before
-                // barrier 2 of the next iteration covers them, ahead of
-                // their first reader, phase Y of iteration g + GK - 1 (other
-                // iterations issue the same loads into the sink)
-                const bool gnext = kt + GK >= nk;
-                issue_group(gnext, gnext ? 0 : kt + GK, ((g / GK) + 1) & 1, (g % GK) == 0);
-            }
-            if constexpr (Op::MX) {
-#pragma unroll
-                for (int w = 0; w < SW; ++w) {
-#pragma unroll
-                    for (int i = 0; i < TI; ++i)
-                        sc_a[i][w] = sn_a[i][w];
-#pragma unroll
-                    for (int j = 0; j < TJ; ++j)
-                        sc_b[j][w] = sn_b[j][w];
+                if constexpr (Op::SG && u == 0) {
+                    // at a group's first K tile: the next group's scale words into
+                    // the other group buffer, whose last reads (a group back)
+                    // ended before this iteration's barrier 1; the wait before
+                    // barrier 2 of the next iteration covers them, ahead of
+                    // their first reader, phase Y of iteration g + GK - 1
+                    const bool gnext = kt + GK >= nk;
+                    issue_group(gnext, gnext ? 0 : kt + GK, ((g / GK) + 1) & 1);
                 }
-            }
+                if constexpr (Op::MX) {
+#pragma unroll
+                    for (int w = 0; w < SW; ++w) {
+#pragma unroll
+                        for (int i = 0; i < TI; ++i)
+                            sc_a[i][w] = sn_a[i][w];
+#pragma unroll
+                        for (int j = 0; j < TJ; ++j)
+                            sc_b[j][w] = sn_b[j][w];
+                    }
+                }
+                ++g;
+            });
         }
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
