@@ -20,7 +20,8 @@ shape (no memory traffic), the power-limited ceiling the GEMMs run under;
 `roofline` relates the dominant kernel to it as well as to the published peak.
 
 Modes for profiling (no JSON): --only bf16|mxfp8|copy|e4m3|e5m2|e2m3|e3m2|e2m1
---reps R runs just that kernel R times after one warm-up (copy: a 1 GiB
+--reps R runs just that kernel R times after one warm-up (--level L: at level
+L instead of the default one; copy: a 1 GiB
 device-to-device copy, the calibration of the HBM byte counters; the MX
 element-format names: the 8192^3 MX GEMM in that format; cfg1-cfg3: the
 single-tile, 4096^3 and ragged workloads).  --only loop prints the
@@ -77,6 +78,8 @@ def parse_args():
     ap.add_argument("--mx-formats", action="store_true",
                     help="time the 8192^3 MX GEMM in every element format (one JSON line)")
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--level", type=int, default=None,
+                    help="with --only bf16|mxfp8|cfgN: run that level instead of the default")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -440,9 +443,14 @@ def main():
     if args.only:
         work = Workload({"bf16": 4, "mxfp8": 5, "cfg1": 1, "cfg2": 2, "cfg3": 3}[args.only], dev)
         for _ in range(args.reps + 1):
-            work.run(stream)
+            if args.level is None:
+                work.run(stream)
+            elif work.run_level(args.level, stream) != mce.MCE_OK:
+                print(f"level {args.level} declines {args.only}", file=sys.stderr, flush=True)
+                sys.exit(2)
         torch.cuda.synchronize()
-        print(f"ran {args.only} level {work.level()} x {args.reps + 1}", flush=True)
+        lvl = work.level() if args.level is None else args.level
+        print(f"ran {args.only} level {lvl} x {args.reps + 1}", flush=True)
         return
 
     works = {"bf16_8192": Workload(4, dev), "mxfp8_8192": Workload(5, dev)}
