@@ -570,24 +570,32 @@ def test_whole_tiles_bf16_output_bitwise(level, fmt):
 
 
 @pytest.mark.parametrize("level", [5, 6])
-@pytest.mark.parametrize("shape,alpha", [((4096, 4352, 512), 1.0), ((8448, 4096, 256), 0.5)],
-                         ids=["272tiles", "528tiles-alpha0.5"])
-def test_whole_tiles_bf16_output_persistent_tail(level, shape, alpha):
-    """Whole 256x256 bf16 tiles (the 16x16x32 format) with more tiles than
-    CUs and a tile count that is not a multiple of the grid: at level 6 some
-    workgroups of the persistent grid take one tile more than others, so the
-    ring runs across a ragged number of tiles.  Exact-integer inputs (alpha
-    0.5 keeps alpha * sum exact), the whole bf16 result compared bitwise with
-    the correctly rounded exact product."""
+@pytest.mark.parametrize("fmt,shape,alpha", [(BF16, (4096, 4352, 512), 1.0),
+                                             (BF16, (8448, 4096, 256), 0.5),
+                                             (E4M3FN, (4096, 4352, 1024), 1.0)],
+                         ids=["bf16-272tiles", "bf16-528tiles-alpha0.5", "mx-272tiles"])
+def test_whole_tiles_bf16_output_persistent_tail(level, fmt, shape, alpha):
+    """Whole 256x256 tiles with bf16 output (bf16: the 16x16x32 format; MX
+    with K a multiple of 512: the K loop unrolled by a scale group) with more
+    tiles than CUs and a tile count that is not a multiple of the grid: at
+    level 6 some workgroups of the persistent grid take one tile more than
+    others, so the ring (and the scale-group count) runs across a ragged
+    number of tiles.  Exact-integer inputs (alpha 0.5 keeps alpha * sum
+    exact), the whole bf16 result compared bitwise with the correctly rounded
+    exact product."""
     M, N, K = shape
-    announce(f"whole tiles persistent tail level {level} {shape} alpha {alpha}")
-    p = integer_problem(M, N, K, c_dtype=OUT_BF16, seed=7400 + level + M, alpha=alpha,
+    announce(f"whole tiles persistent tail level {level} {fmt} {shape} alpha {alpha}")
+    p = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_BF16, seed=7400 + level + M, alpha=alpha,
                         name="whole_tiles_tail")
     r = run_level(p, level)
     assert r is not None
     raw = r[1]
     A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
     B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if fmt == E4M3FN:
+        from helpers import torch_decode_scales
+        A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+        B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
     from helpers import f64_to_bf16_bits
     expect = f64_to_bf16_bits(alpha * (A @ B))
     bad = np.argwhere(raw != expect)
