@@ -767,8 +767,11 @@ void gemm_early(GemmArgs p, int group_m)
 
     typedef typename std::conditional<Op::MX, intx8, bf16x8>::type Frag;
     Frag fa[NKS][TI], fb[NKS][TJ];   // one register set per k-step of a K tile
-    int sc_a[TI][SW], sc_b[TJ][SW];  // MX scale words of the K tile being consumed
-    int sn_a[TI][SW], sn_b[TJ][SW];  // ... of the next K tile
+    // MX scale words: two sets, one for the K tile being consumed and one
+    // being read for the next.  With the K loop unrolled by an even number
+    // of K tiles the sets alternate by unrolled copy; otherwise the next set
+    // is copied into the current one at the end of each K tile.
+    int sc_a[2][TI][SW], sc_b[2][TJ][SW];
     // rows a lane reads differ by multiples of 32 (16x16x32 format: 16, with
     // the swizzle swz8h): the swizzle is lane-constant
     const int lr = S16 ? (lane & 15) : l32;               // row inside a block
@@ -808,7 +811,9 @@ void gemm_early(GemmArgs p, int group_m)
     // scale groups the word is word (gk % 4) of the row's 16 bytes in group
     // buffer (gk / 4) % 2, gk counting K tiles over the workgroup's tiles,
     // and every block is valid (K is a multiple of 512).
-    auto read_scales = [&](int stage, int kt, int gk) {
+    auto read_scales = [&](int stage, int kt, int gk, int set) {
+        auto &sn_a = sc_a[set];
+        auto &sn_b = sc_b[set];
         if constexpr (Op::MX && Op::SG && Op::FP4) {
             // two words (8 blocks) of group buffer (gk / 2) % 2 at word 2 (gk % 2)
             const uint2 *SAs = (const uint2 *)(smem + G::LDS_BYTES + ((gk >> 1) & 1) * (BM + BN) * 16) + (gk & 1);
@@ -876,7 +881,7 @@ void gemm_early(GemmArgs p, int group_m)
 
     typename std::conditional<S16, floatx4, floatx16>::type acc[TI][TJ];
     // matrix-core instructions q in [LO, HI) of the K tile, q = ks*NM + i*TJ + j
-    auto mfmas = [&](int lo, int hi) {
+    auto mfmas = [&](int lo, int hi, int set) {
 #pragma unroll
         for (int q = lo; q < hi; ++q) {
             const int ks = q / NM, i = (q % NM) / TJ, j = q % TJ;
@@ -888,11 +893,11 @@ void gemm_early(GemmArgs p, int group_m)
             else if constexpr (!Op::MX)
                 acc[i][j] = mfma_bf16(fb[ks][j], fa[ks][i], acc[i][j]);
             else if (ks % 2 == 0)
-                acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j][ks / 2],
-                                                sc_a[i][ks / 2]);
+                acc[i][j] = mfma_mx<Op::FMT, 0>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[set][j][ks / 2],
+                                                sc_a[set][i][ks / 2]);
             else
-                acc[i][j] = mfma_mx<Op::FMT, 2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[j][ks / 2],
-                                                sc_a[i][ks / 2]);
+                acc[i][j] = mfma_mx<Op::FMT, 2>(fb[ks][j], fa[ks][i], acc[i][j], sc_b[set][j][ks / 2],
+                                                sc_a[set][i][ks / 2]);
         }
     };
 
@@ -941,16 +946,7 @@ void gemm_early(GemmArgs p, int group_m)
     wait_vmcnt<LX + LY>();                         // K tile 0 (and scale group 0) landed
     barrier();
     read_head(0);
-    read_scales(0, 0, 0);
-#pragma unroll
-    for (int w = 0; w < SW; ++w) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-            sc_a[i][w] = sn_a[i][w];
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-            sc_b[j][w] = sn_b[j][w];
-    }
+    read_scales(0, 0, 0, 0);
 
     int g = 0;
     // the last LA loads of the K tile whose loads began last iteration
@@ -969,13 +965,15 @@ void gemm_early(GemmArgs p, int group_m)
         for (int kt0 = 0; kt0 < nk; kt0 += UNR) {
             static_for<UNR>([&](auto U) {
                 constexpr int u = decltype(U)::value;
+                // scale-word sets of this K tile and of the next
+                constexpr int cur = UNR % 2 == 0 ? (u & 1) : 0, nxs = UNR % 2 == 0 ? ((u + 1) & 1) : 1;
                 const int kt = kt0 + u;
                 const int stage = g & 1;
                 // phase A: the first AM instructions; the K tile's other fragments (its
                 // tail) into registers; the last loads of K tile g+1
                 read_tail(stage);
                 issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
-                mfmas(0, AM);
+                mfmas(0, AM, cur);
                 {
                     constexpr int R = (TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
                     constexpr int PER = (R + AM - 1) / AM;
@@ -1000,7 +998,7 @@ void gemm_early(GemmArgs p, int group_m)
                 const bool lnext = kl >= nk;
                 const int lkt = lnext ? kl - nk : kl;
                 issue(0, LX, lnext, lkt, stage);
-                mfmas(AM, AM + XM);
+                mfmas(AM, AM + XM, cur);
 #pragma unroll
                 for (int x = 0; x < XM; ++x) {
                     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
@@ -1014,12 +1012,12 @@ void gemm_early(GemmArgs p, int group_m)
                 // phase Y: the rest of K tile g; K tile g+1's first fragments (its
                 // head)
                 read_head(stage ^ 1);
-                read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1);
+                read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1, nxs);
                 issue(LX, LX + LY, lnext, lkt, stage);
                 pn_next = lnext;
                 pn_kt = lkt;
                 pn_stage = stage;
-                mfmas(AM + XM, NKS * NM);
+                mfmas(AM + XM, NKS * NM, cur);
                 {
                     constexpr int R = YK * FRAG_READS + (YA + TJ) * RPF + (Op::MX ? TI + TJ : 0);
                     constexpr int PER = (R + YM - 1) / YM;
@@ -1041,15 +1039,15 @@ void gemm_early(GemmArgs p, int group_m)
                     const bool gnext = kt + GK >= nk;
                     issue_group(gnext, gnext ? 0 : kt + GK, ((g / GK) + 1) & 1);
                 }
-                if constexpr (Op::MX) {
+                if constexpr (Op::MX && UNR % 2 != 0) {
 #pragma unroll
                     for (int w = 0; w < SW; ++w) {
 #pragma unroll
                         for (int i = 0; i < TI; ++i)
-                            sc_a[i][w] = sn_a[i][w];
+                            sc_a[0][i][w] = sc_a[1][i][w];
 #pragma unroll
                         for (int j = 0; j < TJ; ++j)
-                            sc_b[j][w] = sn_b[j][w];
+                            sc_b[0][j][w] = sc_b[1][j][w];
                     }
                 }
                 ++g;
