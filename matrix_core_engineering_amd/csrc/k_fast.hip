@@ -968,7 +968,11 @@ void gemm_early(GemmArgs p, int group_m)
                 // scale-word sets of this K tile and of the next
                 constexpr int cur = UNR % 2 == 0 ? (u & 1) : 0, nxs = UNR % 2 == 0 ? ((u + 1) & 1) : 1;
                 const int kt = kt0 + u;
-                const int stage = g & 1;
+                // g equals u modulo UNR (tiles hold whole loop trips): written
+                // so that the compiler sees the low bits of the K-tile count,
+                // and with them the stage and the scale word, as constants
+                const int gg = (g & ~(UNR - 1)) | u;
+                const int stage = gg & 1;
                 // phase A: the first AM instructions; the K tile's other fragments (its
                 // tail) into registers; the last loads of K tile g+1
                 read_tail(stage);
@@ -1012,7 +1016,7 @@ void gemm_early(GemmArgs p, int group_m)
                 // phase Y: the rest of K tile g; K tile g+1's first fragments (its
                 // head)
                 read_head(stage ^ 1);
-                read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, g + 1, nxs);
+                read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, gg + 1, nxs);
                 issue(LX, LX + LY, lnext, lkt, stage);
                 pn_next = lnext;
                 pn_kt = lkt;
