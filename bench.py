@@ -214,7 +214,8 @@ def mx_formats(args, dev, stream):
 
 CEILING_SHAPES = (("bf16_32x32x16", 0, "bf16", PEAK_BF16),
                   ("bf16_16x16x32", 1, "bf16", PEAK_BF16),
-                  ("mxfp8_32x32x64", 2, "e4m3", PEAK_FP8))
+                  ("mxfp8_32x32x64", 2, "e4m3", PEAK_FP8),
+                  ("mxfp4_32x32x64", 3, "e2m1", PEAK_FP4))
 
 
 def matrix_core_ceiling(dev, stream, iters=2000, reps=3):
@@ -230,7 +231,9 @@ def matrix_core_ceiling(dev, stream, iters=2000, reps=3):
     bufs = {"bf16": (torch.randn(nfrag * 8, generator=g) * 0.02).to(torch.bfloat16)
                     .view(torch.int16).to(dev),
             "e4m3": (torch.rand(nfrag * 32, generator=g) * 896.0 - 448.0)
-                    .to(torch.float8_e4m3fn).view(torch.uint8).to(dev)}
+                    .to(torch.float8_e4m3fn).view(torch.uint8).to(dev),
+            # every E2M1 code equally likely, two per byte (no NaN or Inf codes)
+            "e2m1": torch.randint(0, 256, (nfrag * 32,), generator=g, dtype=torch.uint8).to(dev)}
     blocks = 256
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     flops = blocks * 4 * iters * float(1 << 21)

@@ -212,11 +212,14 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
  * of its lane's accumulators to out[blockIdx * 256 + lane_in_block].  Every
  * call does blocks * 4 * iters * 2^21 flops; timing it gives the sustained
  * matrix-core rate for that shape and data.
- *   shape   MCE_LOOP_BF16_32X32X16 (the GEMM's bf16 instruction),
- *           MCE_LOOP_BF16_16X16X32, or MCE_LOOP_MXFP8_32X32X64 (the MX
- *           instruction with E4M3 operands, every scale 1)
+ *   shape   MCE_LOOP_BF16_32X32X16 (the GEMM's 32x32 bf16 instruction),
+ *           MCE_LOOP_BF16_16X16X32, MCE_LOOP_MXFP8_32X32X64 (the MX
+ *           instruction with E4M3 operands) or MCE_LOOP_MXFP4_32X32X64 (the
+ *           same instruction with E2M1 operands); MX scales all 1
  *   frags   device pointer to n_frag fragments of 16 bytes (bf16 shapes:
- *           eight bf16) or 32 bytes (MX: 32 E4M3 codes); fragment
+ *           eight bf16) or 32 bytes (MX: 32 E4M3 codes; E2M1: 32 codes
+ *           packed two per byte in the first 16 bytes, the rest unread);
+ *           fragment
  *           (gid * 16 + i) % n_frag is lane gid's i-th operand register set
  *   out     device pointer to blocks * 256 floats, written
  * Errors: MCE_EINVAL for an unknown shape, a NULL pointer, n_frag < 1,
@@ -224,7 +227,8 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
  * on a device other than gfx950; MCE_ELAUNCH for a failed launch.  Allocates
  * nothing; asynchronous on `stream`.
  */
-enum { MCE_LOOP_BF16_32X32X16 = 0, MCE_LOOP_BF16_16X16X32 = 1, MCE_LOOP_MXFP8_32X32X64 = 2 };
+enum { MCE_LOOP_BF16_32X32X16 = 0, MCE_LOOP_BF16_16X16X32 = 1, MCE_LOOP_MXFP8_32X32X64 = 2,
+       MCE_LOOP_MXFP4_32X32X64 = 3 };
 int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *out,
                          int blocks, int iters, void *stream);
 

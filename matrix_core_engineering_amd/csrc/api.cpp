@@ -424,7 +424,7 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K, const v
 int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *out, int blocks,
                          int iters, void *stream)
 {
-    if (shape < MCE_LOOP_BF16_32X32X16 || shape > MCE_LOOP_MXFP8_32X32X64 || !frags || !out ||
+    if (shape < MCE_LOOP_BF16_32X32X16 || shape > MCE_LOOP_MXFP4_32X32X64 || !frags || !out ||
         n_frag < 1 || n_frag > INT32_MAX || blocks < 1 || blocks > 65535 || iters < 1 ||
         iters > (1 << 24))
         return MCE_EINVAL;

@@ -147,7 +147,7 @@ def test_mx_pick_level_by_format():
 
 
 @pytest.mark.parametrize("shape,frags,n_frag,out,blocks,iters", [
-    (3, FAKE_A, 16, FAKE_C, 1, 1),            # unknown shape
+    (4, FAKE_A, 16, FAKE_C, 1, 1),            # unknown shape
     (-1, FAKE_A, 16, FAKE_C, 1, 1),
     (0, 0, 16, FAKE_C, 1, 1),                 # frags NULL
     (0, FAKE_A, 16, 0, 1, 1),                 # out NULL

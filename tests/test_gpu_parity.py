@@ -603,17 +603,20 @@ def test_whole_tiles_bf16_output_persistent_tail(level, fmt, shape, alpha):
 
 
 @pytest.mark.parametrize("shape", [mce.MCE_LOOP_BF16_32X32X16, mce.MCE_LOOP_BF16_16X16X32,
-                                   mce.MCE_LOOP_MXFP8_32X32X64])
+                                   mce.MCE_LOOP_MXFP8_32X32X64, mce.MCE_LOOP_MXFP4_32X32X64])
 def test_matrix_core_loop_closed_form(shape):
     """The ceiling loop on all-ones operands: every instruction adds its K
     depth to each accumulator, 64 per iteration for every shape (4 k-steps of
-    16, 2 of 32, 1 of 64), and each lane holds 256 accumulators, so every
+    16, 2 of 32, 1 of 64; E2M1 1.0 is code 2), and each lane holds 256
+    accumulators, so every
     lane writes 256 * 64 * iters exactly."""
     announce(f"matrix_core_loop shape={shape}")
     dev = torch.device("cuda:0")
     n_frag, blocks, iters = 64, 8, 6
     if shape == mce.MCE_LOOP_MXFP8_32X32X64:
         one = torch.ones(n_frag * 32).to(torch.float8_e4m3fn).view(torch.uint8)
+    elif shape == mce.MCE_LOOP_MXFP4_32X32X64:
+        one = torch.full((n_frag * 32,), 0x22, dtype=torch.uint8)   # two E2M1 1.0 codes per byte
     else:
         one = torch.ones(n_frag * 8, dtype=torch.bfloat16).view(torch.int16)
     frags = one.to(dev)
