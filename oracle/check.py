@@ -8,9 +8,12 @@ NaN positions must match exactly, and so must the positions and signs of
 infinities ("B200 GEMM Optimization Ladder", section E step 11: NaN/Inf and
 error thresholds are part of every level's correctness gate).
 
-``fp32_slack`` adds 2^-23 * (|alpha*s| + |beta*c0|) for edge cases whose T is
-zero or tiny next to beta*C0: the fp32 epilogue rounds alpha*acc + beta*c0
-once, which the literal bound does not allow for when T == 0.
+``fp32_slack`` (edge cases only, none of the standard workloads) adds
+2^-24 * S, where the caller passes S = 2*|alpha|*T + |beta*c0|: the fp32
+epilogue rounds twice, once for alpha*acc (at most 2^-24 |alpha*acc| <=
+2^-24 |alpha| T) and once for the fused beta*c0 + that product (at most
+2^-24 (|alpha| T + |beta*c0|)), each within half an fp32 ulp.  The literal
+bound allows for neither when T is zero or tiny next to beta*c0.
 """
 import numpy as np
 
@@ -20,7 +23,7 @@ def tolerance(cref, tsum, out_bf16, fp32_slack=None):
     if out_bf16:
         tol = tol + 2.0 ** -8 * np.abs(cref)
     if fp32_slack is not None:
-        tol = tol + 2.0 ** -23 * fp32_slack
+        tol = tol + 2.0 ** -24 * fp32_slack
     return tol
 
 

@@ -100,6 +100,16 @@ def numpy_reference(p):
     return out, tsum
 
 
+def fp32_epilogue_slack(p, tsum):
+    """S = 2*|alpha|*T + |beta*c0| per logical C entry: the magnitudes the
+    fp32 epilogue's two roundings scale with (see oracle.check)."""
+    s = 2.0 * abs(p.alpha) * np.asarray(tsum, dtype=np.float64)
+    if p.beta != 0.0:
+        c0 = p.C0.astype(np.float64) if p.c_dtype != OUT_BF16 else bf16_bits_to_f64(p.C0)
+        s = s + np.abs(p.beta * logical(c0, p.M, p.N, p.c_col_major))
+    return s
+
+
 def oracle_full(p, row_begin=0, row_end=None):
     return oracle.gemm_rows(row_begin=row_begin, row_end=row_end,
                             **p.oracle_kwargs())

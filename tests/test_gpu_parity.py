@@ -23,7 +23,8 @@ from matrix_core_engineering_amd.inputs import (BF16, CONFIGS, E2M1, E2M3, E3M2,
                                                 OUT_BF16, OUT_F32,
                                                 config_problem, integer_problem,
                                                 make_problem)
-from helpers import oracle_entries, oracle_full, torch_decode_elements, logical
+from helpers import (fp32_epilogue_slack, oracle_entries, oracle_full, torch_decode_elements,
+                     logical)
 from gpu_util import DeviceProblem, expected_bits, run_problem
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +75,7 @@ def assert_close(p, vals, slack=False):
     cref, tsum = oracle_full(p)
     fp32_slack = None
     if slack:
-        fp32_slack = np.abs(cref) + 2 * tsum * abs(p.alpha)
+        fp32_slack = fp32_epilogue_slack(p, tsum)
     ok, worst, bad = oracle.check(vals, cref, tsum, p.c_dtype == OUT_BF16, fp32_slack)
     if not ok:
         err = np.abs(vals - cref)

@@ -354,9 +354,102 @@ def test_check_bound():
     assert ok
     ok, _, _ = oracle.check(np.array([1.0 + 1e-7]), np.array([1.0]), np.array([0.0]), False)
     assert not ok
-    ok, _, _ = oracle.check(np.array([1.0 + 1e-7]), np.array([1.0]), np.array([0.0]),
-                            False, fp32_slack=np.array([1.0]))
+    # half an fp32 ulp at 1.5 (2^-24) is inside 2^-24 * S for S = 1.5
+    ok, _, _ = oracle.check(np.array([1.5 + 2.0 ** -24]), np.array([1.5]), np.array([0.0]),
+                            False, fp32_slack=np.array([1.5]))
     assert ok
+
+
+def test_check_bound_failing_side():
+    """Each term of the bound, approached from both sides: 0.99x passes and
+    1.01x fails, for the 2e-4*T term alone, with the bf16 term 2^-8*|Cref|,
+    and with the fp32 slack 2^-24*S."""
+    rng = np.random.default_rng(11)
+    n = 4000
+    cref = rng.uniform(-3.0, 3.0, n) * 2.0 ** rng.integers(-20, 20, n)
+    tsum = np.abs(cref) * rng.uniform(0.0, 50.0, n)
+    slack = rng.uniform(0.0, 4.0, n) * np.abs(cref)
+    sign = rng.choice([-1.0, 1.0], n)
+    cases = [(False, None, 2e-4 * tsum),
+             (True, None, 2e-4 * tsum + np.abs(cref) / 256.0),
+             (False, slack, 2e-4 * tsum + slack / 16777216.0),
+             (True, slack, 2e-4 * tsum + np.abs(cref) / 256.0 + slack / 16777216.0)]
+    for out_bf16, sl, bound in cases:
+        ok, worst, bad = oracle.check(cref + sign * 0.99 * bound, cref, tsum, out_bf16, sl)
+        assert ok and bad == 0 and worst <= 0.99 + 1e-9
+        ok, worst, bad = oracle.check(cref + sign * 1.01 * bound, cref, tsum, out_bf16, sl)
+        assert not ok and bad == n and worst >= 1.01 - 1e-9
+
+
+def _bf16_neighbours(x):
+    """(round-to-nearest-even, round-toward-zero) of float64 x to bf16, from
+    the binary32 bit pattern of x (x exactly representable in binary32)."""
+    bits = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    low = bits & 0xFFFF
+    trunc = bits & ~np.uint64(0xFFFF)
+    up = (low > 0x8000) | ((low == 0x8000) & (((bits >> 16) & 1) == 1))
+    rne = np.where(up, trunc + 0x10000, trunc)
+    f = lambda b: b.astype(np.uint32).view(np.float32).astype(np.float64)
+    return f(rne), f(trunc)
+
+
+def test_check_bf16_term_is_half_an_ulp():
+    """The bf16 term is half a bf16 ulp at |Cref| (one round-to-nearest-even
+    step, 8 significant bits): with T = 0 every RNE rounding is accepted and
+    a truncation that lands more than half an ulp away is rejected.  A term
+    of 2^-7 |Cref| (a whole ulp) would accept those truncations."""
+    rng = np.random.default_rng(12)
+    n = 20000
+    # binary32 values with random low 16 bits over many binades, both signs
+    hi = rng.integers(0x3000, 0x4F00, n).astype(np.uint32)
+    lo = rng.integers(0, 0x10000, n).astype(np.uint32)
+    x = ((hi << 16) | lo).view(np.float32).astype(np.float64)
+    x *= rng.choice([-1.0, 1.0], n)
+    # exact midpoints and the largest low halves too
+    x[:100] = ((hi[:100] << 16) | 0x8000).view(np.float32)
+    x[100:200] = ((hi[100:200] << 16) | 0xFFFF).view(np.float32)
+    rne, trunc = _bf16_neighbours(x)
+    assert np.array_equal(rne, np.asarray(torch.from_numpy(x).to(torch.bfloat16).double()))
+    zero = np.zeros(n)
+    ok, worst, bad = oracle.check(rne, x, zero, out_bf16=True)
+    assert ok and worst <= 1.0
+    far = np.abs(trunc - x) > np.abs(x) / 256.0
+    assert far.sum() > n // 8
+    ok, _, bad = oracle.check(trunc[far], x[far], zero[far], out_bf16=True)
+    assert bad == far.sum()
+    # and without the bf16 term even the RNE results fail (T = 0)
+    moved = rne != x
+    ok, _, bad = oracle.check(rne[moved], x[moved], zero[moved], out_bf16=False)
+    assert bad == moved.sum()
+
+
+def test_check_fp32_slack_is_half_an_ulp_per_rounding():
+    """alpha = 0, T = 0: C = beta*c0 rounded once to fp32 is accepted with
+    S = |beta*c0| (half an ulp is at most 2^-24 |v|), while the fp32
+    neighbour on the far side of the exact value (an error between half an
+    ulp and one ulp) is rejected.  A factor of 2^-23 would accept it."""
+    rng = np.random.default_rng(13)
+    n = 20000
+    c0 = rng.uniform(1.0, 2.0, n).astype(np.float32).astype(np.float64)
+    c0 *= 2.0 ** rng.integers(-30, 30, n) * rng.choice([-1.0, 1.0], n)
+    beta = rng.uniform(0.1, 10.0, n).astype(np.float32).astype(np.float64)
+    exact = beta * c0                         # exact in float64 (24 x 24 bits)
+    got = exact.astype(np.float32).astype(np.float64)
+    ok, worst, _ = oracle.check(got, exact, np.zeros(n), False, fp32_slack=np.abs(exact))
+    assert ok and worst <= 1.0
+    # the fp32 neighbour of the rounded value on the far side of the exact
+    # one: never a correct rounding (it is more than half an ulp away); it
+    # is rejected wherever it is also more than 2^-24 |v| away, which holds
+    # for most values in the lower part of a binade (a whole ulp there is
+    # close to 2^-23 |v|, so a factor 2^-23 would accept all of them)
+    far = np.where(got > exact, np.nextafter(got.astype(np.float32), np.float32(-np.inf)),
+                   np.nextafter(got.astype(np.float32), np.float32(np.inf))).astype(np.float64)
+    sel = np.abs(far - exact) > 2.0 ** -24 * np.abs(exact)
+    assert sel.sum() > n // 4
+    assert np.all(np.abs(far - exact)[sel] < 2.0 ** -23 * np.abs(exact)[sel])
+    ok, _, bad = oracle.check(far[sel], exact[sel], np.zeros(sel.sum()), False,
+                              fp32_slack=np.abs(exact[sel]))
+    assert bad == sel.sum()
 
 
 # ---------------------------------------------------------- generators
