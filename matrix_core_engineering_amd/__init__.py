@@ -12,7 +12,8 @@ import os
 
 __all__ = ["gemm_bf16", "gemm_mxfp8", "gemm_bf16_level", "gemm_mxfp8_level",
            "gemm_bf16_pick_level", "gemm_mxfp8_pick_level", "gemm_mx",
-           "gemm_mx_level", "gemm_mx_pick_level", "MCE_MX_E4M3", "MCE_MX_E5M2",
+           "gemm_mx_level", "gemm_mx_pick_level", "gemm_bf16_order", "gemm_mx_order",
+           "MCE_MX_E4M3", "MCE_MX_E5M2",
            "MCE_MX_E2M3", "MCE_MX_E3M2", "MCE_MX_E2M1",
            "gemm_status_string", "MceError", "lib_path", "load",
            "EXPORTED_SYMBOLS", "MCE_OK", "MCE_EINVAL", "MCE_EUNSUPPORTED",
@@ -29,7 +30,8 @@ MCE_LOOP_MXFP4_32X32X64 = 3
 EXPORTED_SYMBOLS = ("gemm_bf16", "gemm_mxfp8", "gemm_bf16_level",
                     "gemm_mxfp8_level", "gemm_bf16_pick_level",
                     "gemm_mxfp8_pick_level", "gemm_mx", "gemm_mx_level",
-                    "gemm_mx_pick_level", "mce_matrix_core_loop", "gemm_status_string")
+                    "gemm_mx_pick_level", "gemm_bf16_order", "gemm_mx_order",
+                    "mce_matrix_core_loop", "gemm_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -72,6 +74,8 @@ def load():
     lib.gemm_mx.argtypes = [i32] + mx_args
     lib.gemm_mx_level.argtypes = [i32, i32] + mx_args
     lib.gemm_mx_pick_level.argtypes = [i32] + mnk + [vp, i64, i32, vp, i64, vp, i64, i32, vp, i64]
+    lib.gemm_bf16_order.argtypes = [i32, i32, i32] + bf16_args
+    lib.gemm_mx_order.argtypes = [i32, i32, i32, i32] + mx_args
     lib.mce_matrix_core_loop.argtypes = [i32, vp, i64, vp, i32, i32, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = i32
@@ -177,6 +181,27 @@ def gemm_mx_pick_level(elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, 
     return load().gemm_mx_pick_level(int(elem_format), M, N, K, _ptr(A), lda,
                                      int(a_col_major), _ptr(SA), ld_sa, _ptr(B), ldb,
                                      int(b_col_major), _ptr(SB), ld_sb)
+
+
+def gemm_bf16_order(level, xcd_order, group_m, M, N, K, A, lda, a_col_major, B, ldb,
+                    b_col_major, C, ldc, c_col_major, c_dtype, alpha, beta, stream=None,
+                    raise_on_error=True):
+    st = load().gemm_bf16_order(int(level), int(xcd_order), int(group_m), M, N, K, _ptr(A), lda,
+                                int(a_col_major), _ptr(B), ldb, int(b_col_major), _ptr(C), ldc,
+                                int(c_col_major), int(c_dtype), float(alpha), float(beta),
+                                _stream(stream))
+    return _check(st, f"gemm_bf16_order({level}, {xcd_order}, {group_m})", raise_on_error)
+
+
+def gemm_mx_order(level, xcd_order, group_m, elem_format, M, N, K, A, lda, a_col_major, SA,
+                  ld_sa, B, ldb, b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha,
+                  beta, stream=None, raise_on_error=True):
+    st = load().gemm_mx_order(int(level), int(xcd_order), int(group_m), int(elem_format), M, N,
+                              K, _ptr(A), lda, int(a_col_major), _ptr(SA), ld_sa, _ptr(B), ldb,
+                              int(b_col_major), _ptr(SB), ld_sb, _ptr(C), ldc, int(c_col_major),
+                              int(c_dtype), float(alpha), float(beta), _stream(stream))
+    return _check(st, f"gemm_mx_order({level}, {xcd_order}, {group_m}, {elem_format})",
+                  raise_on_error)
 
 
 def mce_matrix_core_loop(shape, frags, n_frag, out, blocks, iters, stream=None,

@@ -1,6 +1,7 @@
 // The C ABI boundary: argument validation, the BLAS special cases, the
 // column-major-C transposition, level choice and the launch on the caller's
-// stream.  No allocation, no state beyond a per-device architecture check.
+// stream.  No allocation; the only state is a per-device record of whether
+// the device is a gfx950 and how many compute units it has.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -18,31 +19,47 @@ enum Fmt { FMT_BF16 = 0, FMT_MX = 1 };
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;   // 32-bit buffer offsets
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_arch_ok[kMaxDevices];            // 0 unknown, 1 gfx950, 2 other
+// Per device, queried once: 0 not yet known, -1 not gfx950, else its
+// compute-unit count (the persistent grids' size).  Concurrent first calls
+// may both query; they store the same value.
+std::atomic<int> g_device_cus[kMaxDevices];
 
-bool device_is_gfx950()
+// Compute units of the current device if it is a gfx950, else 0.
+int gfx950_cus()
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return false;
-    int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+        return 0;
+    int state = g_device_cus[dev].load(std::memory_order_acquire);
     if (state == 0) {
         hipDeviceProp_t prop;
-        state = 2;
+        state = -1;
         if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
             std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
-            state = 1;
-        g_arch_ok[dev].store(state, std::memory_order_relaxed);
+            state = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+        g_device_cus[dev].store(state, std::memory_order_release);
     }
-    return state == 1;
+    return state > 0 ? state : 0;
 }
 
-// Bytes spanned by a rows x cols matrix with the given contiguous extent.
-int64_t span_bytes(int64_t outer, int64_t inner, int64_t ld, int64_t elt)
+// Bytes spanned by rows x cols elements of `bits` bits with leading
+// dimension ld (>= inner), saturated at kMaxBytes: every caller only
+// compares the result with that limit, and saturating first keeps the
+// products below int64 overflow for any 32-bit sizes.
+int64_t span_bytes_bits(int64_t outer, int64_t inner, int64_t ld, int bits)
 {
     if (outer == 0 || inner == 0)
         return 0;
-    return ((outer - 1) * ld + inner) * elt;
+    const int64_t max_elems = kMaxBytes * 8 / bits;
+    if (outer - 1 > max_elems / ld)
+        return kMaxBytes;
+    const int64_t elems = (outer - 1) * ld + inner;
+    return elems > max_elems ? kMaxBytes : (elems * bits + 7) / 8;
+}
+
+int64_t span_bytes(int64_t outer, int64_t inner, int64_t ld, int64_t elt)
+{
+    return span_bytes_bits(outer, inner, ld, (int)(8 * elt));
 }
 
 bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
@@ -74,18 +91,13 @@ struct Call {
     int c_dtype;
     float alpha, beta;
     hipStream_t stream;
+    int xcd_order;   // 1 XCD-major tile walk (default), 0 dispatch order
+    int group_m;     // tile rows per group; 0 = default
+    int ncu;         // set by run(): compute units of the device
 };
 
 // Bits per element of the call's operands.
 int elem_bits(const Call &c) { return c.fmt == FMT_BF16 ? 16 : mce::mx_bits(c.mx_fmt); }
-
-// Bytes spanned by rows x cols elements of `bits` with leading dimension ld.
-int64_t span_bytes_bits(int64_t outer, int64_t inner, int64_t ld, int bits)
-{
-    if (outer == 0 || inner == 0)
-        return 0;
-    return (((outer - 1) * ld + inner) * bits + 7) / 8;
-}
 
 // Levels 4-7 read operands with 16-byte direct loads: both operands
 // K-contiguous, 16-byte aligned rows, K a whole number of 16-byte chunks;
@@ -169,6 +181,15 @@ int validate(const Call &c)
     // packed 6- and 4-bit rows: every row and the K extent fill whole bytes
     const int64_t per_byte_group = bits == 6 ? 4 : bits == 4 ? 2 : 1;
     if (c.K % per_byte_group || c.lda % per_byte_group || c.ldb % per_byte_group)
+        return MCE_EINVAL;
+    // leading dimensions reach the kernels as 32-bit integers; bounding them
+    // here also keeps the span arithmetic below far from int64 overflow
+    if (c.lda > INT32_MAX || c.ldb > INT32_MAX || c.ldc > INT32_MAX ||
+        (c.fmt == FMT_MX && (c.ld_sa > INT32_MAX || c.ld_sb > INT32_MAX)))
+        return MCE_EINVAL;
+    if (c.xcd_order != 0 && c.xcd_order != 1)
+        return MCE_EINVAL;
+    if (c.group_m < 0)
         return MCE_EINVAL;
     const int64_t celt = c.c_dtype == MCE_OUT_F32 ? 4 : 2;
     // leading dimensions: at least the contiguous extent, and at least 1
@@ -255,6 +276,9 @@ GemmArgs kernel_args(const Call &c)
     p.alpha = c.alpha;
     p.beta = c.beta;
     p.mx_fmt = c.mx_fmt;
+    p.ncu = c.ncu;
+    p.xcd_order = c.xcd_order;
+    p.group_m = c.group_m;
     return p;
 }
 
@@ -263,9 +287,11 @@ int run(const Call &in)
     int st = validate(in);
     if (st != MCE_OK)
         return st;
-    if (!device_is_gfx950())
+    const int ncu = gfx950_cus();
+    if (ncu == 0)
         return MCE_EUNSUPPORTED;
     Call c = normalise(in);
+    c.ncu = ncu;
     if (in.level != 0 && !level_accepts(c, in.level))
         return MCE_EUNSUPPORTED;
     if (c.M == 0 || c.N == 0)
@@ -317,6 +343,9 @@ Call make_call(int level, Fmt fmt, int mx_fmt, int64_t M, int64_t N, int64_t K, 
     c.alpha = alpha;
     c.beta = beta;
     c.stream = (hipStream_t)stream;
+    c.xcd_order = 1;
+    c.group_m = 0;
+    c.ncu = 0;
     return c;
 }
 
@@ -408,6 +437,35 @@ int gemm_mx_level(int level, int elem_format, int64_t M, int64_t N, int64_t K, c
                          stream));
 }
 
+int gemm_bf16_order(int level, int xcd_order, int group_m, int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda, int a_col_major, const void *B, int64_t ldb,
+                    int b_col_major, void *C, int64_t ldc, int c_col_major, int c_dtype,
+                    float alpha, float beta, void *stream)
+{
+    if (level < 0 || level > 7)
+        return MCE_EUNSUPPORTED;
+    Call c = make_call(level, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
+                       b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta, stream);
+    c.xcd_order = xcd_order;
+    c.group_m = group_m;
+    return run(c);
+}
+
+int gemm_mx_order(int level, int xcd_order, int group_m, int elem_format, int64_t M, int64_t N,
+                  int64_t K, const void *A, int64_t lda, int a_col_major, const void *SA,
+                  int64_t ld_sa, const void *B, int64_t ldb, int b_col_major, const void *SB,
+                  int64_t ld_sb, void *C, int64_t ldc, int c_col_major, int c_dtype, float alpha,
+                  float beta, void *stream)
+{
+    if (level < 0 || level > 7)
+        return MCE_EUNSUPPORTED;
+    Call c = make_call(level, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
+                       b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta, stream);
+    c.xcd_order = xcd_order;
+    c.group_m = group_m;
+    return run(c);
+}
+
 int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                        int a_col_major, const void *SA, int64_t ld_sa, const void *B, int64_t ldb,
                        int b_col_major, const void *SB, int64_t ld_sb)
@@ -428,7 +486,7 @@ int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *ou
         n_frag < 1 || n_frag > INT32_MAX || blocks < 1 || blocks > 65535 || iters < 1 ||
         iters > (1 << 24))
         return MCE_EINVAL;
-    if (!device_is_gfx950())
+    if (gfx950_cus() == 0)
         return MCE_EUNSUPPORTED;
     return mce::launch_matrix_core_loop(shape, frags, (int)n_frag, out, blocks, iters,
                                         (hipStream_t)stream) == hipSuccess

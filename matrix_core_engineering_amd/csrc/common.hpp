@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "formats.hpp"
+
 namespace mce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -36,12 +38,11 @@ struct GemmArgs {
     int c_dtype;
     float alpha, beta;
     int mx_fmt;         // MX only: element format code of both operands (MX_E4M3 ...)
+    int ncu;            // compute units of the device (persistent grid size)
+    int xcd_order;      // tile walk: 1 XCD-major workgroup slots (default), 0 dispatch order
+    int group_m;        // tile rows per group of the grouped order; 0 = default (8)
 };
 
-// MX element formats, numbered as the block-scaled instruction's format
-// operand (cbsz / blgp); bits per element 8, 8, 6, 6, 4.
-enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M3 = 2, MX_E3M2 = 3, MX_E2M1 = 4 };
-constexpr int mx_bits(int fmt) { return fmt <= MX_E5M2 ? 8 : fmt <= MX_E3M2 ? 6 : 4; }
 
 // ---------------------------------------------------------------- MFMA maps
 //

@@ -1,0 +1,36 @@
+// bf16 levels 4-7 for K-contiguous operands with 16-byte aligned rows: the
+// launchers of the kernel templates in kernels_fast.hpp.
+#include "kernels_fast.hpp"
+
+namespace mce {
+
+// 256x256 tiles when they give every CU work (the early-release ring when K
+// is a whole number of 64-wide K tiles, at least two), else 128x128 tiles on
+// the older ring; level 7 the role-specialised kernel.
+hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
+{
+    // 256x256 tiles when they give every CU work, 128x128 otherwise; the
+    // early-release ring needs two or more whole K tiles
+    const bool big = big_tiles(p);
+    const bool ring_ok = p.K > Bf16Ring64::BK && p.K % Bf16Ring64::BK == 0;
+    switch (level) {
+    case 4:
+        return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
+    case 5:
+        if (big && ring_ok)
+            return launch_early_bf16<false>(p, s);
+        return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
+    case 6:
+        if (big && ring_ok)
+            return launch_early_bf16<true>(p, s);
+        return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
+    case 7:
+        if (p.K > 3 * Bf16Ring::BK)
+            return launch_pingpong<Bf16Ring, true>(p, s);
+        return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+} // namespace mce

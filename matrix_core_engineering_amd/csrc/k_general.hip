@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     const int nk = (p.K + BK - 1) / BK;
     const int nf = p.K / BK;   // K tiles wholly inside K
     const int nwg = gridDim.x, wg = blockIdx.x;
-    const int first = xcd_major(wg, nwg);
+    const int first = wg_slot(wg, nwg, p.xcd_order);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
     const uint16_t *A = (const uint16_t *)p.A, *B = (const uint16_t *)p.B;
 
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
 
     for (int r = 0; r < my_tiles; ++r) {
         int tm, tn;
-        grouped_tile(PERSIST ? persistent_tile_id(wg, nwg, r) : first, tiles_m, tiles_n, group_m, tm,
+        grouped_tile(PERSIST ? persistent_tile_id(wg, nwg, r, p.xcd_order) : first, tiles_m, tiles_n, group_m, tm,
                      tn);
         const int m0 = tm * GBM, n0 = tn * GBN;
 #pragma unroll
@@ -290,16 +290,13 @@ hipError_t launch_g(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + GBM - 1) / GBM, tiles_n = (p.N + GBN - 1) / GBN;
     const int ntiles = tiles_m * tiles_n;
-    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    const int group_m = group_rows(tiles_m, p.group_m);
     int grid = ntiles;
     if (PERSIST) {
         // three workgroups fit a CU (34 KiB of LDS, the kernel is held to 168
         // registers per lane): the persistent grid keeps all of them busy
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            ncu > 0 && ntiles > 3 * ncu)
-            grid = 3 * ncu;
+        if (ntiles > 3 * p.ncu)
+            grid = 3 * p.ncu;
     }
     hipLaunchKernelGGL((gemm_general<A_KC, B_KC, PERSIST, BK>), dim3(grid), dim3(256), 0, s, p, group_m);
     return hipGetLastError();
@@ -329,10 +326,7 @@ hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s)
         // persistent grid is the one-tile grid (whose kernel needs fewer
         // registers)
         const long ntiles = (long)((p.M + GBM - 1) / GBM) * ((p.N + GBN - 1) / GBN);
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            ntiles <= 3L * ncu)
+        if (ntiles <= 3L * p.ncu)
             return launch_g_layout<false, 32>(p, s);
         return launch_g_layout<true, 32>(p, s);
     }

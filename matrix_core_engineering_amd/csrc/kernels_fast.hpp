@@ -1,3 +1,7 @@
+// Kernel templates of levels 4-7 of the GEMM ladder (the launchers for each
+// operand format are instantiated in k_fast_*.hip, one translation unit per
+// format so that they compile in parallel).
+//
 // Levels 4-6 of the GEMM ladder ("B200 GEMM Optimization Ladder", section E
 // steps 5-7) for K-contiguous operands (A row-major, B column-major) with
 // 16-byte aligned rows, in bf16 and in MX block-scaled fp8.
@@ -42,9 +46,12 @@
 //             into the stage consumed one K tile earlier.
 // ("B200 TMA Pipeline Designer", section E steps 4-7: per-stage ready/free
 // protocol, initial phases, prologue / steady state / drain.)
+#pragma once
+
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "ring_plan.hpp"
 #include "sched.hpp"
 
 #include <type_traits>
@@ -230,7 +237,7 @@ void gemm_fast(GemmArgs p, int group_m)
     const int ntiles = tiles_m * tiles_n;
     const int nk = (p.K + Op::BK - 1) / Op::BK;
     const int nwg = gridDim.x, wg = blockIdx.x;
-    const int first = xcd_major(wg, nwg);
+    const int first = wg_slot(wg, nwg, p.xcd_order);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
     const int total = my_tiles * nk;
 
@@ -387,7 +394,7 @@ void gemm_fast(GemmArgs p, int group_m)
     // g counts K tiles over all tiles of this workgroup; the stage of K tile
     // g is g % STAGES.  The load side runs STAGES-1 K tiles ahead, possibly
     // into the next tile.
-    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
+    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r, p.xcd_order) : first; };
     int ld_r = 0, ld_kt = 0, ld_stage = 0, ld_left = total;   // next K tile to load
     auto issue_next = [&]() {
         if (ld_left <= 0)
@@ -473,34 +480,8 @@ struct Mxfp8Ring {                    // 64-byte rows
     static constexpr int BK = 64;
     static constexpr int NKS = 1;     // one 32x32x64 k-step per K tile
 };
-
-template <class Op, int BM, int BN, int S>
-struct RingGeometry {
-    static constexpr int ROWB = Op::BK * Op::ELT;          // 64 or 128 bytes per LDS row
-    static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
-    static constexpr int RPL = 1024 / ROWB;                // rows per direct load
-    static constexpr int EPC = 16 / Op::ELT;               // K elements per chunk
-    static constexpr int WM = BM / 2, WN = BN / 2;
-    static constexpr int TI = WM / 32, TJ = WN / 32;
-    static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-    // one aligned 4-byte scale word per row (the four blocks containing the K
-    // tile's blocks); a direct load of any size fills one 4-byte LDS slot per
-    // lane
-    static constexpr int SA_BYTES = Op::MX && !Op::SG ? BM * 4 : 0;
-    static constexpr int SB_BYTES = Op::MX && !Op::SG ? BN * 4 : 0;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-    static constexpr int LDS_BYTES = S * STAGE_BYTES;
-    static constexpr int NA = BM / RPL / 4;                // direct loads per wave per K tile
-    static constexpr int NB = BN / RPL / 4;
-    static constexpr int NSA = Op::MX && !Op::SG ? 1 : 0;  // 4-byte scale loads: 64 rows each
-    static constexpr int NSB = Op::MX && !Op::SG ? 1 : 0;
-    static constexpr int LOADS = NA + NB + NSA + NSB;
-    static_assert((ROWB == 64 && CH == 4 && RPL == 16) || (ROWB == 128 && CH == 8 && RPL == 8),
-                  "64- or 128-byte LDS rows");
-    static_assert(NA % 2 == 0 && NB % 2 == 0, "loads split in halves; swizzle parity");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static_assert((S - 2) * LOADS < 64, "vmcnt range");
-    static_assert(!Op::MX || (BM == 256 && BN == 256), "MX scale loads assume 256-row tiles");
+struct E5m2Ring : Mxfp8Ring {         // E5M2: the E4M3 layout with format code 1
+    static constexpr int FMT = MX_E5M2;
 };
 
 // Waits until at most n K tiles' loads (n <= 3) of LOADS direct loads each
@@ -538,114 +519,25 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // The loads of a K tile spread over phases X and Y of one iteration and have
 // until barrier 2 of the next to land.  Needs at least two K tiles and K a
 // multiple of the K tile.
-// Per format: AM matrix-core instructions in phase A (the K tile's fragment
-// reads spread over them: four waves read LDS at about 108 B/clk per CU; AM
-// need not be a whole k-step: the stage is free once every fragment is in
-// registers); XM in phase X; LX and LY of a K tile's direct loads issued in
-// phases X and Y (the address unit takes about one 1 KiB direct load per
-// 21 clocks per CU, so the loads need phases X and Y to be long enough), the
-// rest in the next phase A; the next K tile's first YK
-// k-steps of fragments read whole in phase Y (into the registers of k-steps
-// whose instructions all precede phase Y), then k-step YK's B fragments and
-// its first YA A fragments, the rest in the next phase A (the instruction
-// order needs A fragment i only from the (TJ*i)-th instruction on).
-struct Bf16Ring64 {                   // 128-byte rows
-    static constexpr bool MX = false, SG = false, FP4 = false;
-    static constexpr int EPU = 1;     // elements per K unit (FP4: two per byte)
-    static constexpr int ELT = 2;
-    static constexpr int BK = 64;
-    static constexpr int NKS = 4;
-    static constexpr int AM = 16, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
-    static constexpr bool S16 = false;
-};
-// bf16 on the 16x16x32 instruction, which sustains 4-7% more flops than
-// 32x32x16 at the chip's power limit (measured with the ceiling loop): each
-// wave's 128x128 tile is 8x8 blocks of 16x16, a K tile two k-steps of 32 K
-// (128 instructions of 16 clocks, the same 32 fragment reads per K tile).
-// A fragment is 16 rows x 32 K: lane l reads row l % 16 at logical chunk
-// 4ks + l / 16 of its 128-byte row; the swizzle swz8h keeps both 16-lane
-// read groups of every fragment read conflict-free.  Whole bf16 tiles with
-// the LDS-staged epilogue only.
-struct Bf16Ring64S16 : Bf16Ring64 {
-    static constexpr bool S16 = true;
-    static constexpr int NKS = 2;
-    static constexpr int AM = 32, XM = 88, LX = 16, LY = 0, YA = 2, YK = 0;
-};
-struct Mxfp8Ring128 {                 // 128-byte rows
-    static constexpr bool MX = true, SG = false, FP4 = false, S16 = false;
-    static constexpr int EPU = 1;
-    static constexpr int FMT = MX_E4M3;
-    static constexpr int ELT = 1;
-    static constexpr int BK = 128;
-    static constexpr int NKS = 2;
-    static constexpr int AM = 16, XM = 12, LX = 12, LY = 4, YA = 2, YK = 0;
-};
-// MX with K a multiple of 512 (whole groups of 16 scale blocks): the scale
-// words of four K tiles travel together, 16 bytes per row, in a separate
-// double-buffered area (see gemm_early).  A 4-byte load per row and K tile
-// touches as many cache lines as a 16-byte one, and 64 rows' worth per
-// instruction doubled the K tile's line requests.
-struct Mxfp8Ring128G : Mxfp8Ring128 {
-    static constexpr bool SG = true;
-    static constexpr int AM = 12, XM = 16, LX = 14, LY = 2, YA = 1, YK = 0;
-};
-// E5M2 elements have E4M3's byte layout and fragment map: the same kernels
-// with the instruction's format code 1.
-struct E5m2Ring : Mxfp8Ring {
-    static constexpr int FMT = MX_E5M2;
-};
-struct E5m2Ring128 : Mxfp8Ring128 {
-    static constexpr int FMT = MX_E5M2;
-};
-struct E5m2Ring128G : Mxfp8Ring128G {
-    static constexpr int FMT = MX_E5M2;
-};
-// FP4 (E2M1), two elements per byte.  The kernel runs in byte units (the
-// host passes K, lda and ldb halved), so the loads are those of E4M3: a K
-// tile is 128 bytes of a row = 256 elements = 8 scale blocks.  A lane's
-// fragment of a k-step (64 elements, 32 bytes of the row) is the 16 bytes of
-// its block, logical chunk 2ks + h, as for bf16; four k-steps per K tile;
-// two scale words per row and K tile, a scale group (16 bytes per row)
-// covers two K tiles.
-struct Fp4Ring128G {
-    static constexpr bool MX = true, SG = true, FP4 = true, S16 = false;
-    static constexpr int EPU = 2;
-    static constexpr int FMT = MX_E2M1;
-    static constexpr int ELT = 1;
-    static constexpr int BK = 128;    // K units (bytes) per K tile
-    static constexpr int NKS = 4;
-    static constexpr int AM = 16, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
-};
-
+// The formats, the stage geometry and the step tables of prologue and K-tile
+// iteration are in ring_plan.hpp, which the host model of the ring protocol
+// (tests/ring_model.cpp) replays.
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_early(GemmArgs p, int group_m)
 {
-    using G = RingGeometry<Op, BM, BN, 2>;
-    constexpr int NKS = Op::NKS;
-    // matrix-core blocks of 32x32 (16x16 on the 16x16x32 format) per wave tile
-    constexpr bool S16 = Op::S16;
-    constexpr int BLK = S16 ? 16 : 32, TI = G::WM / BLK, TJ = G::WN / BLK;
+    using P = EarlyPlan<Op, BM, BN>;
+    using G = typename P::G;
+    constexpr int NKS = P::NKS;
+    constexpr bool S16 = P::S16;
+    constexpr int BLK = P::BLK, TI = P::TI, TJ = P::TJ, NM = P::NM, RPF = P::RPF;
+    constexpr int BPK = P::BPK, GK = P::GK, UNR = P::UNR, SW = P::SW, FRAG_READS = P::FRAG_READS;
+    constexpr int AM = P::AM, XM = P::XM, YM = P::YM;
+    constexpr int LX = P::LX, LY = P::LY, LA = P::LA, YA = P::YA, YK = P::YK;
     static_assert(!S16 || EPI == EPI_BF16_LDS, "16x16 blocks: whole bf16 tiles staged through LDS");
-    constexpr int NM = TI * TJ;                            // matrix-core instructions per k-step
-    constexpr int RPF = Op::MX && !Op::FP4 ? 2 : 1;       // LDS reads per fragment
-    constexpr int BPK = Op::BK * Op::EPU / 32;             // scale blocks per K tile
-    constexpr int GK = 16 / BPK;                           // K tiles per scale group
-    constexpr int UNR = Op::SG ? GK : 1;                   // K tiles per K-loop trip
-    constexpr int SW = BPK / 4;                            // scale words per row and K tile
-    constexpr int FRAG_READS = (TI + TJ) * RPF;
-    constexpr int AM = Op::AM;                             // phase A
-    constexpr int XM = Op::XM, YM = NKS * NM - AM - XM;    // phases X and Y
-    constexpr int LX = Op::LX, LY = Op::LY, LA = G::LOADS - LX - LY, YA = Op::YA, YK = Op::YK;
-    static_assert(G::CH == 8, "128-byte LDS rows");
-    static_assert(AM > 0 && XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
-    static_assert(YA >= 1 && YA <= TI, "first A fragment read in phase Y");
-    static_assert(YK >= 0 && YK < NKS && AM + XM >= (YK + 1) * NM,
-                  "phase Y overwrites only k-steps whose instructions precede it");
-    static_assert(LX <= XM && LY <= YM && LA <= AM, "at most one load per matrix-core instruction");
     // LDS: the two stages, then (scale groups) two buffers of 16 bytes per
     // A and B row, then (staged epilogue) one buffer per wave
-    constexpr int SG_BYTES = Op::SG ? 2 * (BM + BN) * 16 : 0;
+    constexpr int SG_BYTES = P::SG_BYTES;
     constexpr int EPI_RR = Op::SG || S16 ? 16 : 32;
     constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? 4 * epi_wave_bytes<EPI_RR>() : 0;
     static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
@@ -660,12 +552,12 @@ void gemm_early(GemmArgs p, int group_m)
     const int ntiles = tiles_m * tiles_n;
     const int nk = (p.K + Op::BK - 1) / Op::BK;            // >= 2 (host guarantees)
     const int nwg = gridDim.x, wg = blockIdx.x;
-    const int first = xcd_major(wg, nwg);
+    const int first = wg_slot(wg, nwg, p.xcd_order);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
 
     const int nblk = (p.K * Op::EPU + 31) / 32;            // MX scale blocks per row
 
-    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
+    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r, p.xcd_order) : first; };
 
     // Direct-load addressing.  Each tile gets its own buffer resources (A
     // and B rows of the tile, MX scale rows) whose record count ends at the
@@ -936,22 +828,92 @@ void gemm_early(GemmArgs p, int group_m)
         }
     };
 
+    // One step of the ring (ring_plan.hpp) in iteration g: kt is K tile g's
+    // index inside its tile (-1 in the prologue), stage = g % 2, gg = g with
+    // its low bits known at compile time, cur / nxs the scale-word register
+    // sets of K tiles g and g+1.  Direct loads of K tile g + ktile past the
+    // tile's last K tile take the next tile's resources (past the
+    // workgroup's last tile the zero-record ones).
+    auto step = [&](auto ST, auto U, int kt, int stage, int gg, int set_cur, int set_nxt) {
+        constexpr int st = decltype(ST)::value;
+        constexpr int u = decltype(U)::value;
+        constexpr LoadStep ls = load_step<P>(st);
+        if constexpr (ls.ktile > 0) {
+            const int kl = kt + ls.ktile;
+            const bool lnext = kl >= nk;
+            issue(ls.lo, ls.hi, lnext, lnext ? kl - nk : kl, (stage + ls.ktile) & 1);
+        } else if constexpr (st == RS_READ_TAIL) {
+            read_tail(stage);
+        } else if constexpr (st == RS_READ_HEAD) {
+            read_head(stage ^ 1);
+        } else if constexpr (st == RS_READ_SCALES) {
+            read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, gg + 1, set_nxt);
+        } else if constexpr (st == RS_MFMA_A) {
+            // the first AM instructions, with the K tile's tail reads and the
+            // pending loads spread over them
+            mfmas(0, AM, set_cur);
+            constexpr int R = (TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
+            constexpr int PER = (R + AM - 1) / AM;
+#pragma unroll
+            for (int x = 0; x < AM; ++x) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (x * PER < R)
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
+                if (loads_after(x, AM, LA))
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
+        } else if constexpr (st == RS_MFMA_X) {
+            mfmas(AM, AM + XM, set_cur);
+#pragma unroll
+            for (int x = 0; x < XM; ++x) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (loads_after(x, XM, LX))
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
+        } else if constexpr (st == RS_MFMA_Y) {
+            mfmas(AM + XM, NKS * NM, set_cur);
+            constexpr int R = YK * FRAG_READS + (YA + TJ) * RPF + (Op::MX ? TI + TJ : 0);
+            constexpr int PER = (R + YM - 1) / YM;
+#pragma unroll
+            for (int x = 0; x < YM; ++x) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (x * PER < R)
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
+                if (loads_after(x, YM, LY))
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
+        } else if constexpr (st == RS_WAIT_LGKM) {
+            // the waits and barriers are fences for the scheduler too: no
+            // matrix-core instruction may drift across them
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkm0();
+        } else if constexpr (st == RS_WAIT_VM || st == RS_WAIT_VM_PRO) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<vm_wait<P>(st)>();
+        } else if constexpr (st == RS_BARRIER) {
+            barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (st == RS_ISSUE_GROUP0) {
+            issue_group(false, 0, group_buffer(0));
+        } else if constexpr (st == RS_ISSUE_GROUP) {
+            if constexpr (Op::SG && u == 0) {
+                // at a group's first K tile: the next group's scale words
+                // into the other group buffer (the host model checks that its
+                // last reads precede a barrier before this issue and that the
+                // loads land before their first reader)
+                const bool gnext = kt + GK >= nk;
+                issue_group(gnext, gnext ? 0 : kt + GK, group_buffer(gg / GK + 1));
+            }
+        }
+    };
+
     // ---------------------------------------------------------- prologue
-    // K tile 0 whole, K tile 1 but its last LA loads, which the first phase A
-    // issues (a direct load always writes LDS, so no placeholder load may
-    // target a stage in use)
-    issue_group(false, 0, 0);                      // scale group 0 (GK K tiles)
-    issue(0, G::LOADS, false, 0, 0);
-    issue(0, LX + LY, false, 1, 1);
-    wait_vmcnt<LX + LY>();                         // K tile 0 (and scale group 0) landed
-    barrier();
-    read_head(0);
-    read_scales(0, 0, 0, 0);
+    static_for<kEarlyPrologueSteps>([&](auto S) {
+        step(std::integral_constant<int, kEarlyPrologue[decltype(S)::value]>{},
+             std::integral_constant<int, 0>{}, -1, 1, -1, 0, 0);
+    });
 
     int g = 0;
-    // the last LA loads of the K tile whose loads began last iteration
-    bool pn_next = false;
-    int pn_kt = 1, pn_stage = 1;
     for (int r = 0; r < my_tiles; ++r) {
 #pragma unroll
         for (int i = 0; i < TI; ++i)
@@ -973,76 +935,10 @@ void gemm_early(GemmArgs p, int group_m)
                 // and with them the stage and the scale word, as constants
                 const int gg = (g & ~(UNR - 1)) | u;
                 const int stage = gg & 1;
-                // phase A: the first AM instructions; the K tile's other fragments (its
-                // tail) into registers; the last loads of K tile g+1
-                read_tail(stage);
-                issue(LX + LY, G::LOADS, pn_next, pn_kt, pn_stage);
-                mfmas(0, AM, cur);
-                {
-                    constexpr int R = (TI - YA) * RPF + FRAG_READS * (NKS - 1 - YK);
-                    constexpr int PER = (R + AM - 1) / AM;
-#pragma unroll
-                    for (int x = 0; x < AM; ++x) {
-                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                        if (x * PER < R)
-                            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
-                        if (loads_after(x, AM, LA))
-                            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-                    }
-                }
-                // the waits and barriers are fences for the scheduler too: no
-                // matrix-core instruction may drift across them
-                __builtin_amdgcn_sched_barrier(0);
-                wait_lgkm0();
-                barrier();                             // free: stage `stage` read by every wave
-                __builtin_amdgcn_sched_barrier(0);
-                // phase X: the loads of K tile g+2 into the released stage begin
-                // (past the last K tile `lnext` holds: the zero-record resources)
-                const int kl = kt + 2;
-                const bool lnext = kl >= nk;
-                const int lkt = lnext ? kl - nk : kl;
-                issue(0, LX, lnext, lkt, stage);
-                mfmas(AM, AM + XM, cur);
-#pragma unroll
-                for (int x = 0; x < XM; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                    if (loads_after(x, XM, LX))
-                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<LX>();                      // this wave's loads of K tile g+1 landed
-                barrier();                             // ready: K tile g+1 in the other stage
-                __builtin_amdgcn_sched_barrier(0);
-                // phase Y: the rest of K tile g; K tile g+1's first fragments (its
-                // head)
-                read_head(stage ^ 1);
-                read_scales(stage ^ 1, kt + 1 < nk ? kt + 1 : 0, gg + 1, nxs);
-                issue(LX, LX + LY, lnext, lkt, stage);
-                pn_next = lnext;
-                pn_kt = lkt;
-                pn_stage = stage;
-                mfmas(AM + XM, NKS * NM, cur);
-                {
-                    constexpr int R = YK * FRAG_READS + (YA + TJ) * RPF + (Op::MX ? TI + TJ : 0);
-                    constexpr int PER = (R + YM - 1) / YM;
-#pragma unroll
-                    for (int x = 0; x < YM; ++x) {
-                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                        if (x * PER < R)
-                            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, PER, 0);
-                        if (loads_after(x, YM, LY))
-                            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-                    }
-                }
-                if constexpr (Op::SG && u == 0) {
-                    // at a group's first K tile: the next group's scale words into
-                    // the other group buffer, whose last reads (a group back)
-                    // ended before this iteration's barrier 1; the wait before
-                    // barrier 2 of the next iteration covers them, ahead of
-                    // their first reader, phase Y of iteration g + GK - 1
-                    const bool gnext = kt + GK >= nk;
-                    issue_group(gnext, gnext ? 0 : kt + GK, ((g / GK) + 1) & 1);
-                }
+                static_for<kEarlyLoopSteps>([&](auto S) {
+                    step(std::integral_constant<int, kEarlyLoop[decltype(S)::value]>{}, U, kt, stage,
+                         gg, cur, nxs);
+                });
                 if constexpr (Op::MX && UNR % 2 != 0) {
 #pragma unroll
                     for (int w = 0; w < SW; ++w) {
@@ -1071,8 +967,6 @@ void gemm_early(GemmArgs p, int group_m)
         // the load side moves one tile ahead
         cur = nxt;
         nxt = tile_span(r + 2);
-        // the pending loads belong to the tile that is now current
-        pn_next = false;
     }
     wait_vmcnt<0>();   // no direct load still writing LDS when the waves end
 }
@@ -1138,7 +1032,7 @@ void gemm_pingpong(GemmArgs p, int group_m)
     const int ntiles = tiles_m * tiles_n;
     const int nk = (p.K + Op::BK - 1) / Op::BK;                  // >= S (host guarantees)
     const int nwg = gridDim.x, wg = blockIdx.x;
-    const int first = xcd_major(wg, nwg);
+    const int first = wg_slot(wg, nwg, p.xcd_order);
     const int my_tiles = PERSIST ? (first < ntiles ? (ntiles - 1 - first) / nwg + 1 : 0) : 1;
     const int total = my_tiles * nk;
 
@@ -1158,7 +1052,7 @@ void gemm_pingpong(GemmArgs p, int group_m)
         s_ld = grp == 0 ? p.ld_sa : p.ld_sb;
     }
 
-    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r) : first; };
+    auto tile_of = [&](int r) { return PERSIST ? persistent_tile_id(wg, nwg, r, p.xcd_order) : first; };
 
     // Direct-load geometry: this wave's loads t = 0..N-1 fill LDS rows
     // (wave*N + t)*16 .. +15; lane l writes row +l/4 at physical chunk l%4 and
@@ -1349,28 +1243,10 @@ void gemm_pingpong(GemmArgs p, int group_m)
     wait_vmcnt<0>();
 }
 
-int g_num_cus = 0;
-
-// The branch-free epilogue applies: bf16 C, beta == 0, whole tiles, C rows
-// 8-byte aligned.
 bool whole_bf16(const GemmArgs &p, int bm, int bn)
 {
     return p.c_dtype == OUT_BF16 && p.beta == 0.0f && p.M % bm == 0 && p.N % bn == 0 &&
            p.ldc % 4 == 0 && ((uintptr_t)p.C % 8) == 0;
-}
-
-int num_cus()
-{
-    if (g_num_cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            g_num_cus = n;
-        else
-            g_num_cus = 256;
-    }
-    return g_num_cus;
 }
 
 template <class Op, int BM, int BN, int STAGES, bool PERSIST>
@@ -1378,10 +1254,10 @@ hipError_t launch(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    const int group_m = group_rows(tiles_m, p.group_m);
     int grid = ntiles;
     if (PERSIST)
-        grid = ntiles < num_cus() ? ntiles : num_cus();
+        grid = ntiles < p.ncu ? ntiles : p.ncu;
     if (whole_bf16(p, BM, BN))
         hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, EPI_BF16_WHOLE>), dim3(grid),
                            dim3(256), 0, s, p, group_m);
@@ -1396,14 +1272,14 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int ntiles = tiles_m * tiles_n;
-    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    const int group_m = group_rows(tiles_m, p.group_m);
     // with no more tiles than CUs a persistent grid is the one-tile grid:
     // run the simpler kernel
-    if (PERSIST && ntiles <= num_cus())
+    if (PERSIST && ntiles <= p.ncu)
         return launch_early<Op, BM, BN, false>(p, s);
     int grid = ntiles;
     if (PERSIST)
-        grid = ntiles < num_cus() ? ntiles : num_cus();
+        grid = ntiles < p.ncu ? ntiles : p.ncu;
     if (whole_bf16(p, BM, BN) && p.ldc % 8 == 0 && (uintptr_t)p.C % 16 == 0)
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
                            s, p, group_m);
@@ -1426,10 +1302,10 @@ hipError_t launch_early_bf16(const GemmArgs &p, hipStream_t s)
         return launch_early<Bf16Ring64, 256, 256, PERSIST>(p, s);
     const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     const int ntiles = tiles_m * tiles_n;
-    const int group_m = tiles_m < 8 ? tiles_m : 8;
-    if (PERSIST && ntiles <= num_cus())
+    const int group_m = group_rows(tiles_m, p.group_m);
+    if (PERSIST && ntiles <= p.ncu)
         return launch_early_bf16<false>(p, s);
-    const int grid = PERSIST ? (ntiles < num_cus() ? ntiles : num_cus()) : ntiles;
+    const int grid = PERSIST ? (ntiles < p.ncu ? ntiles : p.ncu) : ntiles;
     hipLaunchKernelGGL((gemm_early<Bf16Ring64S16, 256, 256, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
                        s, p, group_m);
     return hipGetLastError();
@@ -1440,10 +1316,10 @@ hipError_t launch_pingpong(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + PP::BM - 1) / PP::BM, tiles_n = (p.N + PP::BN - 1) / PP::BN;
     const int ntiles = tiles_m * tiles_n;
-    const int group_m = tiles_m < 8 ? tiles_m : 8;
+    const int group_m = group_rows(tiles_m, p.group_m);
     int grid = ntiles;
     if (PERSIST)
-        grid = ntiles < num_cus() ? ntiles : num_cus();
+        grid = ntiles < p.ncu ? ntiles : p.ncu;
     if (whole_bf16(p, PP::BM, PP::BN))
         hipLaunchKernelGGL((gemm_pingpong<Op, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(512), 0, s, p,
                            group_m);
@@ -1455,43 +1331,8 @@ hipError_t launch_pingpong(const GemmArgs &p, hipStream_t s)
 
 bool big_tiles(const GemmArgs &p)
 {
-    return (long)((p.M + 255) / 256) * ((p.N + 255) / 256) >= num_cus();
+    return (long)((p.M + 255) / 256) * ((p.N + 255) / 256) >= p.ncu;
 }
-
-} // namespace
-
-// Ring shapes measured fastest at 8192^3 on MI355X: bf16 in 32-wide K tiles
-// (64-byte rows) with four stages and split loads; MX-fp8 in 128-wide K tiles
-// (128-byte rows, two k-steps per barrier) with two stages.  bf16 with
-// 64-wide tiles and two stages, or without split loads, measured within 2%;
-// MX with 64-wide tiles and four stages measured 20% slower.
-hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
-{
-    // 256x256 tiles when they give every CU work, 128x128 otherwise; the
-    // early-release ring needs two or more whole K tiles
-    const bool big = big_tiles(p);
-    const bool ring_ok = p.K > Bf16Ring64::BK && p.K % Bf16Ring64::BK == 0;
-    switch (level) {
-    case 4:
-        return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
-    case 5:
-        if (big && ring_ok)
-            return launch_early_bf16<false>(p, s);
-        return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
-    case 6:
-        if (big && ring_ok)
-            return launch_early_bf16<true>(p, s);
-        return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
-    case 7:
-        if (p.K > 3 * Bf16Ring::BK)
-            return launch_pingpong<Bf16Ring, true>(p, s);
-        return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
-    default:
-        return hipErrorInvalidValue;
-    }
-}
-
-namespace {
 
 // Levels 5-7 for one 8-bit element format: Op (the older ring), Ring (64-byte
 // rows, level 7), Ring128 / Ring128G (gemm_early without / with scale groups).
@@ -1518,33 +1359,4 @@ hipError_t launch_fast_mx8(int level, const GemmArgs &p, hipStream_t s)
 }
 
 } // namespace
-
-// FP4: gemm_early in byte units, with whole scale groups (K a multiple of
-// 512 elements, 16-byte scale rows) and 16-byte aligned rows.
-hipError_t launch_fast_fp4(int level, const GemmArgs &p, hipStream_t s)
-{
-    if (p.K % 512 != 0 || p.lda % 32 != 0 || p.ldb % 32 != 0 || p.ld_sa % 16 != 0 ||
-        p.ld_sb % 16 != 0 || (uintptr_t)p.SA % 16 != 0 || (uintptr_t)p.SB % 16 != 0)
-        return hipErrorInvalidValue;
-    GemmArgs q = p;
-    q.K = p.K / 2;
-    q.lda = p.lda / 2;
-    q.ldb = p.ldb / 2;
-    switch (level) {
-    case 5: return launch_early<Fp4Ring128G, 256, 256, false>(q, s);
-    case 6: return launch_early<Fp4Ring128G, 256, 256, true>(q, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s)
-{
-    switch (p.mx_fmt) {
-    case MX_E2M1: return launch_fast_fp4(level, p, s);
-    case MX_E4M3: return launch_fast_mx8<Mxfp8Op, Mxfp8Ring, Mxfp8Ring128, Mxfp8Ring128G>(level, p, s);
-    case MX_E5M2: return launch_fast_mx8<E5m2Op, E5m2Ring, E5m2Ring128, E5m2Ring128G>(level, p, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
 } // namespace mce

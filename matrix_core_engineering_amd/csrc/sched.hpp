@@ -29,6 +29,21 @@ MCE_HD int xcd_major(int wg, int nwg)
     return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Position of workgroup `wg` in the tile walk: XCD-major (xcd != 0, the
+// default) or the dispatch order itself (xcd == 0, for the tile-order study).
+MCE_HD int wg_slot(int wg, int nwg, int xcd)
+{
+    return xcd ? xcd_major(wg, nwg) : wg;
+}
+
+// Tile rows per group of the grouped order: `requested` when positive
+// (clamped to the tile rows), else the default of 8.
+MCE_HD int group_rows(int tiles_m, int requested)
+{
+    const int g = requested > 0 ? requested : 8;
+    return tiles_m < g ? tiles_m : g;
+}
+
 // Linear tile id -> (tile row, tile column), grouped by `group_m` tile rows.
 // Bijection from [0, tiles_m * tiles_n) onto the tile grid.
 MCE_HD void grouped_tile(int id, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
@@ -43,10 +58,11 @@ MCE_HD void grouped_tile(int id, int tiles_m, int tiles_n, int group_m, int &tm,
 }
 
 // The r-th tile of workgroup `wg` in a persistent grid of `nwg` workgroups
-// (r = 0, 1, ... while the result is < tiles_m * tiles_n).
-MCE_HD int persistent_tile_id(int wg, int nwg, int r)
+// (r = 0, 1, ... while the result is < tiles_m * tiles_n), XCD-major unless
+// xcd == 0.
+MCE_HD int persistent_tile_id(int wg, int nwg, int r, int xcd = 1)
 {
-    return r * nwg + xcd_major(wg, nwg);
+    return r * nwg + wg_slot(wg, nwg, xcd);
 }
 
 // XOR swizzle of the 16-byte chunk index inside one 128-byte LDS row (8

@@ -26,15 +26,30 @@ def to_dev(arr):
     return torch.from_numpy(a.view(view).copy()).to(DEV)
 
 
+class Offset:
+    """Operand bytes placed `off` bytes into a device buffer (16-byte aligned
+    base), so the pointer handed to the library is misaligned by `off`."""
+
+    def __init__(self, arr, off):
+        a = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        host = np.zeros(a.size + 16 + off, np.uint8)
+        host[off:off + a.size] = a
+        self.buf = torch.from_numpy(host).to(DEV)
+        self.off = off
+
+    def data_ptr(self):
+        return self.buf.data_ptr() + self.off
+
+
 class DeviceProblem:
     """Operands on the device; C inside a buffer with GUARD_ROWS sentinel rows
     above and below, sentinel padding columns, and (when beta == 0) NaN in
     every logical element so that an element left unwritten is caught."""
 
-    def __init__(self, p):
+    def __init__(self, p, a_off=0, b_off=0):
         self.p = p
-        self.A = to_dev(p.A)
-        self.B = to_dev(p.B)
+        self.A = Offset(p.A, a_off) if a_off else to_dev(p.A)
+        self.B = Offset(p.B, b_off) if b_off else to_dev(p.B)
         self.SA = to_dev(p.SA)
         self.SB = to_dev(p.SB)
         outer = p.N if p.c_col_major else p.M

@@ -60,9 +60,27 @@ def bf16(M, N, K, lda, a_cm, ldb, b_cm, ldc, c_cm=0, c_dtype=0, alpha=1.0, beta=
     dict(M=4, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, C=0),      # C NULL
     dict(M=4, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=4, C=FAKE_A + 8),  # C overlaps A
     dict(M=1 << 16, N=4, K=1 << 15, lda=1 << 15, a_cm=0, ldb=1 << 15, b_cm=1, ldc=4),  # A >= 2 GiB
+    dict(M=3, N=4, K=4, lda=1 << 62, a_cm=0, ldb=4, b_cm=1, ldc=4),    # lda overflows a span
+    dict(M=3, N=4, K=4, lda=(1 << 31) + 8, a_cm=0, ldb=4, b_cm=1, ldc=4),  # lda above int32
+    dict(M=3, N=4, K=4, lda=4, a_cm=0, ldb=4, b_cm=1, ldc=1 << 62),    # ldc overflows a span
+    dict(M=3, N=4, K=4, lda=4, a_cm=0, ldb=1 << 40, b_cm=1, ldc=4),    # ldb above int32
 ])
 def test_invalid_arguments_rejected_on_host(args):
     assert bf16(**args) == mce.MCE_EINVAL
+
+
+def test_tile_order_knobs_validated():
+    def order(xcd, gm, level=0):
+        return mce.gemm_bf16_order(level, xcd, gm, 4, 4, 4, FAKE_A, 4, 0, FAKE_B, 4, 1, FAKE_C, 4,
+                                   0, 0, 1.0, 0.0, stream=0, raise_on_error=False)
+    assert order(2, 0) == mce.MCE_EINVAL
+    assert order(-1, 0) == mce.MCE_EINVAL
+    assert order(1, -1) == mce.MCE_EINVAL
+    assert order(1, 0, level=8) == mce.MCE_EUNSUPPORTED
+    st = mce.gemm_mx_order(0, 3, 0, mce.MCE_MX_E4M3, 4, 4, 32, FAKE_A, 32, 0, 0x40000000, 1,
+                           FAKE_B, 32, 1, 0x50000000, 1, FAKE_C, 4, 0, 0, 1.0, 0.0, stream=0,
+                           raise_on_error=False)
+    assert st == mce.MCE_EINVAL
 
 
 def test_level_out_of_range():

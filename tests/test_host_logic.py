@@ -24,6 +24,8 @@ int h_xcd_major(int wg, int nwg) { return mce::xcd_major(wg, nwg); }
 void h_grouped_tile(int id, int tm_, int tn_, int g, int *tm, int *tn)
 { mce::grouped_tile(id, tm_, tn_, g, *tm, *tn); }
 int h_persistent_tile_id(int wg, int nwg, int r) { return mce::persistent_tile_id(wg, nwg, r); }
+int h_persistent_tile_id_x(int wg, int nwg, int r, int x) { return mce::persistent_tile_id(wg, nwg, r, x); }
+int h_group_rows(int tm, int req) { return mce::group_rows(tm, req); }
 int h_swz8(int r) { return mce::swz8(r); }
 int h_swz8h(int r) { return mce::swz8h(r); }
 int h_swz4(int r) { return mce::swz4(r); }
@@ -50,6 +52,29 @@ def grouped(lib, i, tm_, tn_, g):
     a, b = ctypes.c_int(), ctypes.c_int()
     lib.h_grouped_tile(i, tm_, tn_, g, ctypes.byref(a), ctypes.byref(b))
     return a.value, b.value
+
+
+@pytest.mark.parametrize("xcd", [0, 1])
+@pytest.mark.parametrize("ntiles,nwg", [(1024, 256), (1000, 256), (272, 256), (17, 5)])
+def test_both_tile_walks_cover_every_tile_once(lib, xcd, ntiles, nwg):
+    seen = []
+    for wg in range(nwg):
+        r = 0
+        while True:
+            t = lib.h_persistent_tile_id_x(wg, nwg, r, xcd)
+            if t >= ntiles:
+                break
+            seen.append(t)
+            r += 1
+    assert sorted(seen) == list(range(ntiles))
+    if xcd == 0:   # the dispatch order: workgroup w starts at tile w
+        assert all(lib.h_persistent_tile_id_x(w, nwg, 0, 0) == w for w in range(nwg))
+
+
+def test_group_rows_default_and_clamp(lib):
+    assert lib.h_group_rows(32, 0) == 8 and lib.h_group_rows(5, 0) == 5
+    assert lib.h_group_rows(32, 4) == 4 and lib.h_group_rows(3, 16) == 3
+    assert lib.h_group_rows(32, 1) == 1
 
 
 @pytest.mark.parametrize("nwg", [1, 7, 8, 9, 63, 64, 100, 255, 256, 257, 1000, 1024])
