@@ -85,6 +85,9 @@ def parse_args():
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--level", type=int, default=None,
                     help="with --only bf16|mxfp8|cfgN: run that level instead of the default")
+    ap.add_argument("--order", type=str, default=None,
+                    help="with --only bf16|mxfp8: tile walk 'X,G' (X 1 XCD-major or 0 dispatch "
+                         "order, G tile rows per group) through gemm_bf16_order / gemm_mx_order")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,6 +136,20 @@ class Workload:
                                     p.ld_sa, self.B, p.ldb, p.b_col_major, self.SB, p.ld_sb,
                                     self.C, p.ldc, p.c_col_major, p.c_dtype, p.alpha, p.beta,
                                     stream=stream, raise_on_error=False)
+
+    def run_order(self, xcd, group_m, stream):
+        """The default level with a chosen tile walk; returns the status."""
+        import matrix_core_engineering_amd as mce
+        p = self.p
+        if p.SA is None:
+            return mce.gemm_bf16_order(0, xcd, group_m, p.M, p.N, p.K, self.A, p.lda, p.a_col_major,
+                                       self.B, p.ldb, p.b_col_major, self.C, p.ldc, p.c_col_major,
+                                       p.c_dtype, p.alpha, p.beta, stream=stream,
+                                       raise_on_error=False)
+        return mce.gemm_mx_order(0, xcd, group_m, mce.MCE_MX_E4M3, p.M, p.N, p.K, self.A, p.lda,
+                                 p.a_col_major, self.SA, p.ld_sa, self.B, p.ldb, p.b_col_major,
+                                 self.SB, p.ld_sb, self.C, p.ldc, p.c_col_major, p.c_dtype, p.alpha,
+                                 p.beta, stream=stream, raise_on_error=False)
 
     def level(self):
         import matrix_core_engineering_amd as mce
@@ -540,14 +557,8 @@ def tile_orders(args, dev, stream):
         p = w.p
 
         def run(xcd, gm):
-            if p.SA is None:
-                return mce.gemm_bf16_order(0, xcd, gm, p.M, p.N, p.K, w.A, p.lda, p.a_col_major,
-                                           w.B, p.ldb, p.b_col_major, w.C, p.ldc, p.c_col_major,
-                                           p.c_dtype, p.alpha, p.beta, stream=stream)
-            return mce.gemm_mx_order(0, xcd, gm, mce.MCE_MX_E4M3, p.M, p.N, p.K, w.A, p.lda,
-                                     p.a_col_major, w.SA, p.ld_sa, w.B, p.ldb, p.b_col_major,
-                                     w.SB, p.ld_sb, w.C, p.ldc, p.c_col_major, p.c_dtype,
-                                     p.alpha, p.beta, stream=stream)
+            st = w.run_order(xcd, gm, stream)
+            assert st == mce.MCE_OK, mce.gemm_status_string(st)
 
         times = {o: [] for o in orders}
         for _ in range(args.warmup):
@@ -624,7 +635,12 @@ def main():
     if args.only:
         work = Workload({"bf16": 4, "mxfp8": 5, "cfg1": 1, "cfg2": 2, "cfg3": 3}[args.only], dev)
         for _ in range(args.reps + 1):
-            if args.level is None:
+            if args.order is not None:
+                xcd, gm = (int(v) for v in args.order.split(","))
+                if work.run_order(xcd, gm, stream) != mce.MCE_OK:
+                    print(f"order {args.order} declined", file=sys.stderr, flush=True)
+                    sys.exit(2)
+            elif args.level is None:
                 work.run(stream)
             elif work.run_level(args.level, stream) != mce.MCE_OK:
                 print(f"level {args.level} declines {args.only}", file=sys.stderr, flush=True)
@@ -636,16 +652,20 @@ def main():
 
     bf16 = Workload(4, dev)
     mx = Workload(5, dev)
+    # measurements reported beside the headline, taken first: the clock and
+    # power of each kernel over a 2 s window of back-to-back launches, and
+    # the matrix-core loop rates; they also bring the clocks to their
+    # sustained state before the timed steps
+    clocks = {"bf16_8192": sustained_window(bf16, stream),
+              "mxfp8_8192": sustained_window(mx, stream),
+              "matrix_core_loop_bf16_16x16x32": sustained_loop(dev, stream, 1)}
+    ceiling = matrix_core_ceiling(dev, stream)
+    # the headline: W warm-up launches, then K timed launches (HIP events)
     t_bf16, wall = timed_steps(bf16, args.warmup, args.steps, stream)
     t_mx, _ = timed_steps(mx, args.warmup, args.steps, stream)
     ms_per_step = float(np.mean(t_bf16))
     value = bf16.p.flops / (ms_per_step * 1e-3) / 1e12
     tf_mx = mx.p.flops / (float(np.mean(t_mx)) * 1e-3) / 1e12
-
-    ceiling = matrix_core_ceiling(dev, stream)
-    clocks = {"bf16_8192": sustained_window(bf16, stream),
-              "mxfp8_8192": sustained_window(mx, stream),
-              "matrix_core_loop_bf16_16x16x32": sustained_loop(dev, stream, 1)}
     traffic = read_traffic()
     # the default bf16 kernel for whole 256x256 bf16 tiles runs 16x16x32
     loop_bf16 = ceiling["bf16_16x16x32"]["tflops"]
