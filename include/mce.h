@@ -139,6 +139,15 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  *   level 5  + multi-stage LDS ring with ready/free stages (step 6)
  *   level 6  + persistent grid with a tile-order scheduler (step 7)
  *   level 7  + role-specialised waves (step 8)
+ *   level 8  not available: its B200 mechanism (2-CTA clusters sharing
+ *            operand tiles through distributed shared memory and multicast
+ *            loads, step 9) has no gfx950 counterpart; every call with
+ *            level 8 returns MCE_EUNSUPPORTED.  gemm_bf16_order /
+ *            gemm_mx_order expose its nearest lever, the tile walk over the
+ *            XCDs' L2 caches.
+ *   level 9  + several consumer wave groups on one staged ring (step 10):
+ *            eight waves, two per SIMD, in two groups of four sharing every
+ *            stage of level 6's ring, each wave 128x64 of a 256x256 tile
  *
  * bf16 levels 4 and 7 need both operands K-contiguous (A row-major, B
  * column-major), 16-byte aligned base pointers, lda and ldb multiples of 8
@@ -148,6 +157,10 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  * alignment and K).  gemm_mxfp8_level accepts levels 3 and 5-7, 5-7 with the
  * K-contiguity and alignment rules above and scale rows padded to 4 bytes
  * (same meaning; its level 3 also takes any K and either operand layout).
+ * Level 9 needs the level-4 rules and whole K tiles, at least two: bf16 K a
+ * multiple of 64 and above 64; MX (8-bit elements) K a multiple of 512 with
+ * 16-byte aligned scale rows (A, B, SA, SB 16-byte aligned, ld_sa and ld_sb
+ * multiples of 16).  Other problems return MCE_EUNSUPPORTED at level 9.
  */
 int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, int a_col_major,

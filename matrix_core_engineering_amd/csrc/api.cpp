@@ -130,6 +130,19 @@ bool mx_scales_eligible(const Call &c)
            ((uintptr_t)c.SB % 4) == 0;
 }
 
+// Level 9 (eight consumer waves on the early-release ring): whole K tiles,
+// at least two (bf16: K a multiple of 64; MX: 8-bit elements and whole
+// scale groups, K a multiple of 512 with 16-byte aligned scale rows).
+bool level9_eligible(const Call &c)
+{
+    if (!fast_eligible(c))
+        return false;
+    if (c.fmt == FMT_BF16)
+        return c.K > 64 && c.K % 64 == 0;
+    return elem_bits(c) == 8 && c.K % 512 == 0 && c.ld_sa % 16 == 0 && c.ld_sb % 16 == 0 &&
+           ((uintptr_t)c.SA % 16) == 0 && ((uintptr_t)c.SB % 16) == 0;
+}
+
 constexpr int kBestBf16Level = 6;     // the persistent pipelined kernel
 constexpr int kBestMxLevel = 6;
 
@@ -153,13 +166,15 @@ bool level_accepts(const Call &c, int level)
         case 2: return c.M <= 128 && c.N <= 128;
         case 3: case 5: case 6: return true;
         case 4: case 7: return fast_eligible(c);
-        default: return false;
+        case 9: return level9_eligible(c);
+        default: return false;   // level 8: no gfx950 counterpart (include/mce.h)
         }
     }
     switch (level) {
     case 3: return true;
     case 5: case 6: return (fast_eligible(c) && mx_scales_eligible(c)) || fp4_fast_eligible(c);
     case 7: return fast_eligible(c) && mx_scales_eligible(c);   // 8-bit formats
+    case 9: return level9_eligible(c);
     default: return false;
     }
 }
@@ -303,9 +318,10 @@ int run(const Call &in)
     } else {
         int level = in.level != 0 ? in.level : pick_level(c);
         if (c.fmt == FMT_BF16)
-            err = level <= 3                              ? mce::launch_simple_bf16(level, p, c.stream)
-                  : fast_eligible(c) || level == 4 || level == 7 ? mce::launch_fast_bf16(level, p, c.stream)
-                                                         : mce::launch_general_bf16(level, p, c.stream);
+            err = level <= 3 ? mce::launch_simple_bf16(level, p, c.stream)
+                  : fast_eligible(c) || level == 4 || level == 7 || level == 9
+                      ? mce::launch_fast_bf16(level, p, c.stream)
+                      : mce::launch_general_bf16(level, p, c.stream);
         else
             err = level <= 3 ? mce::launch_simple_mx(p, c.stream) : mce::launch_fast_mx(level, p, c.stream);
         if (err == hipErrorInvalidValue && level >= 4)
@@ -377,7 +393,7 @@ int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K, const void *A, i
                     int64_t ldc, int c_col_major, int c_dtype, float alpha, float beta,
                     void *stream)
 {
-    if (level < 1 || level > 7)
+    if (level < 1 || level > 9)
         return MCE_EUNSUPPORTED;
     return run(make_call(level, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
                          b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta,
@@ -389,7 +405,7 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K, const void *A, 
                      int b_col_major, const void *SB, int64_t ld_sb, void *C, int64_t ldc,
                      int c_col_major, int c_dtype, float alpha, float beta, void *stream)
 {
-    if (level < 1 || level > 7)
+    if (level < 1 || level > 9)
         return MCE_EUNSUPPORTED;
     return run(make_call(level, FMT_MX, MCE_MX_E4M3, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
                          b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
@@ -430,7 +446,7 @@ int gemm_mx_level(int level, int elem_format, int64_t M, int64_t N, int64_t K, c
                   int64_t ldb, int b_col_major, const void *SB, int64_t ld_sb, void *C, int64_t ldc,
                   int c_col_major, int c_dtype, float alpha, float beta, void *stream)
 {
-    if (level < 1 || level > 7)
+    if (level < 1 || level > 9)
         return MCE_EUNSUPPORTED;
     return run(make_call(level, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B,
                          ldb, b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta,
@@ -442,7 +458,7 @@ int gemm_bf16_order(int level, int xcd_order, int group_m, int64_t M, int64_t N,
                     int b_col_major, void *C, int64_t ldc, int c_col_major, int c_dtype,
                     float alpha, float beta, void *stream)
 {
-    if (level < 0 || level > 7)
+    if (level < 0 || level > 9)
         return MCE_EUNSUPPORTED;
     Call c = make_call(level, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb,
                        b_col_major, nullptr, 0, C, ldc, c_col_major, c_dtype, alpha, beta, stream);
@@ -457,7 +473,7 @@ int gemm_mx_order(int level, int xcd_order, int group_m, int elem_format, int64_
                   int64_t ld_sb, void *C, int64_t ldc, int c_col_major, int c_dtype, float alpha,
                   float beta, void *stream)
 {
-    if (level < 0 || level > 7)
+    if (level < 0 || level > 9)
         return MCE_EUNSUPPORTED;
     Call c = make_call(level, FMT_MX, elem_format, M, N, K, A, lda, a_col_major, SA, ld_sa, B, ldb,
                        b_col_major, SB, ld_sb, C, ldc, c_col_major, c_dtype, alpha, beta, stream);

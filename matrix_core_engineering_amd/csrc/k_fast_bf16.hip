@@ -6,7 +6,8 @@ namespace mce {
 
 // 256x256 tiles when they give every CU work (the early-release ring when K
 // is a whole number of 64-wide K tiles, at least two), else 128x128 tiles on
-// the older ring; level 7 the role-specialised kernel.
+// the older ring; level 7 the role-specialised kernel; level 9 the
+// early-release ring with eight consumer waves (whole 64-wide K tiles only).
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
     // 256x256 tiles when they give every CU work, 128x128 otherwise; the
@@ -18,12 +19,16 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
         return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
     case 5:
         if (big && ring_ok)
-            return launch_early_bf16<false>(p, s);
+            return launch_early_bf16<Bf16Ring64, Bf16Ring64S16, false>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
     case 6:
         if (big && ring_ok)
-            return launch_early_bf16<true>(p, s);
+            return launch_early_bf16<Bf16Ring64, Bf16Ring64S16, true>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);
+    case 9:
+        if (ring_ok)
+            return launch_early_bf16<Bf16Ring64W8, Bf16Ring64S16W8, true>(p, s);
+        return hipErrorInvalidValue;
     case 7:
         if (p.K > 3 * Bf16Ring::BK)
             return launch_pingpong<Bf16Ring, true>(p, s);

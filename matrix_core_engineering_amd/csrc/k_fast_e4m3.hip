@@ -6,7 +6,7 @@ namespace mce {
 
 hipError_t launch_fast_e4m3(int level, const GemmArgs &p, hipStream_t s)
 {
-    return launch_fast_mx8<Mxfp8Op, Mxfp8Ring, Mxfp8Ring128, Mxfp8Ring128G>(level, p, s);
+    return launch_fast_mx8<Mxfp8Op, Mxfp8Ring, Mxfp8Ring128, Mxfp8Ring128G, Mxfp8Ring128GW8>(level, p, s);
 }
 
 } // namespace mce

@@ -7,7 +7,7 @@ namespace mce {
 
 hipError_t launch_fast_e5m2(int level, const GemmArgs &p, hipStream_t s)
 {
-    return launch_fast_mx8<E5m2Op, E5m2Ring, E5m2Ring128, E5m2Ring128G>(level, p, s);
+    return launch_fast_mx8<E5m2Op, E5m2Ring, E5m2Ring128, E5m2Ring128G, E5m2Ring128GW8>(level, p, s);
 }
 
 } // namespace mce

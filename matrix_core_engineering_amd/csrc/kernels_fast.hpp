@@ -155,7 +155,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
                                                char *buf)
 {
     static_assert(G::TJ % 2 == 0, "blocks staged in pairs");
-    static_assert(RR == 16 || RR == 32, "rows per round");
+    static_assert(RR == 8 || RR == 16 || RR == 32, "rows per round");
     const int h = lane >> 5, l32 = lane & 31;
     const int rrow = lane >> 3, rchunk = lane & 7;       // read-back position
 #pragma unroll
@@ -165,7 +165,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
 #pragma unroll
             for (int half = 0; half < 32 / RR; ++half) {
             // lane (l32, h) holds row l32, columns 8q + 4h .. +3 of each block
-            if (RR == 32 || (l32 >> 4) == half) {
+            if (RR == 32 || l32 / RR == half) {
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -532,7 +532,7 @@ __device__ __forceinline__ void wait_tiles_after(int n)
 // iteration are in ring_plan.hpp, which the host model of the ring protocol
 // (tests/ring_model.cpp) replays.
 template <class Op, int BM, int BN, bool PERSIST, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * Op::WAVES) __attribute__((amdgpu_waves_per_eu(Op::WAVES / 4, Op::WAVES / 4)))
 void gemm_early(GemmArgs p, int group_m)
 {
     using P = EarlyPlan<Op, BM, BN>;
@@ -547,14 +547,16 @@ void gemm_early(GemmArgs p, int group_m)
     // LDS: the two stages, then (scale groups) two buffers of 16 bytes per
     // A and B row, then (staged epilogue) one buffer per wave
     constexpr int SG_BYTES = P::SG_BYTES;
-    constexpr int EPI_RR = Op::SG || S16 ? 16 : 32;
-    constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? 4 * epi_wave_bytes<EPI_RR>() : 0;
+    constexpr int WAVES = P::WAVES;
+    // rows per round of the LDS-staged epilogue: what the LDS left over holds
+    constexpr int EPI_RR = WAVES == 8 ? (Op::SG ? 8 : 16) : (Op::SG || S16 ? 16 : 32);
+    constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? WAVES * epi_wave_bytes<EPI_RR>() : 0;
     static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + SG_BYTES + EPI_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
     const int h = lane >> 5, l32 = lane & 31;
 
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -589,8 +591,11 @@ void gemm_early(GemmArgs p, int group_m)
     for (int t = 0; t < G::NB; ++t)
         vb[t] = (uint32_t)(((wave * G::NB + t) * G::RPL + lrow) * p.ldb + ((t & 1) ? kc_odd : kc_even)) *
                 Op::ELT;
-    const uint32_t vsa = (uint32_t)((wave * 64 + lane) * p.ld_sa);
-    const uint32_t vsb = (uint32_t)((wave * 64 + lane) * p.ld_sb);
+    // scale rows: with eight waves, waves 0-3 load the A rows' scale words
+    // and waves 4-7 the B rows'
+    const int srow = (WAVES == 8 ? (wave & 3) : wave) * 64 + lane;
+    const uint32_t vsa = (uint32_t)(srow * p.ld_sa);
+    const uint32_t vsb = (uint32_t)(srow * p.ld_sb);
 
     // Base and record count of the r-th tile's resources (A rows, B rows,
     // MX scale rows); past the last tile every record count is zero (loads
@@ -772,11 +777,20 @@ void gemm_early(GemmArgs p, int group_m)
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(t.sa, t.nsa);
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(t.sb, t.nsb);
             char *gb = smem + G::LDS_BYTES + buf * (BM + BN) * 16;
-            char *da = gb + wave * 1024, *db = gb + BM * 16 + wave * 1024;
             const int soff = kt * BPK;
-            const uint32_t voa = vsa, vob = vsb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)da, 16, voa, soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)db, 16, vob, soff, 0, 0);
+            if constexpr (WAVES == 4) {
+                char *da = gb + wave * 1024, *db = gb + BM * 16 + wave * 1024;
+                const uint32_t voa = vsa, vob = vsb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)da, 16, voa, soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)db, 16, vob, soff, 0, 0);
+            } else {
+                // one operand per wave: a uniform select, no branch
+                const bool bside = wave >= 4;
+                const __amdgpu_buffer_rsrc_t rs = bside ? rb : ra;
+                char *dst = gb + (bside ? BM * 16 : 0) + (wave & 3) * 1024;
+                const uint32_t vo = bside ? vsb : vsa;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, vo, soff, 0, 0);
+            }
         }
     };
 
@@ -1299,33 +1313,34 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
     if (PERSIST)
         grid = ntiles < p.ncu ? ntiles : p.ncu;
     if (whole_bf16(p, BM, BN) && p.ldc % 8 == 0 && (uintptr_t)p.C % 16 == 0)
-        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
     else if (whole_bf16(p, BM, BN))
-        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
     else
-        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p,
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_ANY>), dim3(grid), dim3(64 * Op::WAVES), 0, s, p,
                            group_m);
     return hipGetLastError();
 }
 
-// bf16 levels 5-6 on 256x256 tiles: whole bf16 tiles that take the
+// bf16 levels 5-6 (and 9) on 256x256 tiles: whole bf16 tiles that take the
 // LDS-staged epilogue run the 16x16x32 format (more flops per clock at the
-// power limit), everything else the 32x32x16 one.
-template <bool PERSIST>
+// power limit), everything else the 32x32x16 one.  Ring / RingS16: the
+// formats of the two instruction shapes (four waves, or eight for level 9).
+template <class Ring, class RingS16, bool PERSIST>
 hipError_t launch_early_bf16(const GemmArgs &p, hipStream_t s)
 {
     if (!whole_bf16(p, 256, 256) || p.ldc % 8 != 0 || (uintptr_t)p.C % 16 != 0)
-        return launch_early<Bf16Ring64, 256, 256, PERSIST>(p, s);
+        return launch_early<Ring, 256, 256, PERSIST>(p, s);
     const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     const int ntiles = tiles_m * tiles_n;
     const int group_m = group_rows(tiles_m, p.group_m);
     if (PERSIST && ntiles <= p.ncu)
-        return launch_early_bf16<false>(p, s);
+        return launch_early_bf16<Ring, RingS16, false>(p, s);
     const int grid = PERSIST ? (ntiles < p.ncu ? ntiles : p.ncu) : ntiles;
-    hipLaunchKernelGGL((gemm_early<Bf16Ring64S16, 256, 256, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
-                       s, p, group_m);
+    hipLaunchKernelGGL((gemm_early<RingS16, 256, 256, PERSIST, EPI_BF16_LDS>), dim3(grid),
+                       dim3(64 * RingS16::WAVES), 0, s, p, group_m);
     return hipGetLastError();
 }
 
@@ -1352,9 +1367,10 @@ bool big_tiles(const GemmArgs &p)
     return (long)((p.M + 255) / 256) * ((p.N + 255) / 256) >= p.ncu;
 }
 
-// Levels 5-7 for one 8-bit element format: Op (the older ring), Ring (64-byte
-// rows, level 7), Ring128 / Ring128G (gemm_early without / with scale groups).
-template <class Op, class Ring, class Ring128, class Ring128G>
+// Levels 5-7 and 9 for one 8-bit element format: Op (the older ring), Ring
+// (64-byte rows, level 7), Ring128 / Ring128G (gemm_early without / with
+// scale groups), Ring128GW8 (level 9: eight consumer waves, scale groups).
+template <class Op, class Ring, class Ring128, class Ring128G, class Ring128GW8>
 hipError_t launch_fast_mx8(int level, const GemmArgs &p, hipStream_t s)
 {
     const bool ring_ok = p.K > Ring128::BK && p.K % Ring128::BK == 0;   // whole K tiles
@@ -1372,6 +1388,10 @@ hipError_t launch_fast_mx8(int level, const GemmArgs &p, hipStream_t s)
         return ring_ok ? launch_early<Ring128, 256, 256, true>(p, s) : launch<Op, 256, 256, 2, true>(p, s);
     case 7:
         return p.K > 3 * Ring::BK ? launch_pingpong<Ring, true>(p, s) : launch<Op, 256, 256, 2, true>(p, s);
+    case 9:
+        if (ring_ok && groups)
+            return launch_early<Ring128GW8, 256, 256, true>(p, s);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }

@@ -29,6 +29,7 @@ namespace mce {
 // rest in the next phase A (the instruction order needs A fragment i only
 // from the (TJ*i)-th instruction on).
 struct Bf16Ring64 {                   // 128-byte rows
+    static constexpr int WAVES = 4;   // one wave per SIMD, 128x128 per wave
     static constexpr bool MX = false, SG = false, FP4 = false;
     static constexpr int EPU = 1;     // elements per K unit (FP4: two per byte)
     static constexpr int ELT = 2;
@@ -51,6 +52,7 @@ struct Bf16Ring64S16 : Bf16Ring64 {
     static constexpr int AM = 32, XM = 88, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 struct Mxfp8Ring128 {                 // 128-byte rows
+    static constexpr int WAVES = 4;
     static constexpr bool MX = true, SG = false, FP4 = false, S16 = false;
     static constexpr int EPU = 1;
     static constexpr int FMT = MX_E4M3;
@@ -84,6 +86,7 @@ struct E5m2Ring128G : Mxfp8Ring128G {
 // two scale words per row and K tile, a scale group (16 bytes per row)
 // covers two K tiles.
 struct Fp4Ring128G {
+    static constexpr int WAVES = 4;
     static constexpr bool MX = true, SG = true, FP4 = true, S16 = false;
     static constexpr int EPU = 2;
     static constexpr int FMT = MX_E2M1;
@@ -93,15 +96,44 @@ struct Fp4Ring128G {
     static constexpr int AM = 16, XM = 40, LX = 16, LY = 0, YA = 2, YK = 0;
 };
 
+// Level 9: several consumers of one staged ring ("B200 GEMM Optimization
+// Ladder", section A1 level 9 and section E step 10: more consumer groups
+// sharing one staged operand so each staged byte feeds more matrix-core
+// work).  Eight waves, two per SIMD, in two groups of four; each wave owns
+// 128x64 of the 256x256 tile (128 accumulator registers, so two waves fit a
+// SIMD's register file), and both groups consume every stage: each A row of
+// a stage feeds four waves, each B row two.  A K tile carries half the
+// matrix-core instructions per wave, so the phases are half as long; the
+// other wave on the SIMD fills the gaps of each one's LDS reads and waits.
+// Eight direct loads per wave and K tile.  MX formats with scale groups only
+// (waves 0-3 load the A rows' scale words, waves 4-7 the B rows').
+struct Bf16Ring64W8 : Bf16Ring64 {
+    static constexpr int WAVES = 8;
+    static constexpr int AM = 8, XM = 20, LX = 8, LY = 0, YA = 2, YK = 0;
+};
+struct Bf16Ring64S16W8 : Bf16Ring64S16 {
+    static constexpr int WAVES = 8;
+    static constexpr int AM = 16, XM = 44, LX = 8, LY = 0, YA = 2, YK = 0;
+};
+struct Mxfp8Ring128GW8 : Mxfp8Ring128G {
+    static constexpr int WAVES = 8;
+    static constexpr int AM = 6, XM = 8, LX = 7, LY = 1, YA = 1, YK = 0;
+};
+struct E5m2Ring128GW8 : Mxfp8Ring128GW8 {
+    static constexpr int FMT = MX_E5M2;
+};
+
 // ---------------------------------------------------------------- geometry
 
 template <class Op, int BM, int BN, int S>
 struct RingGeometry {
+    static constexpr int WAVES = Op::WAVES;                // 4 (2x2) or 8 (2x4)
+    static constexpr int WAVES_N = WAVES / 2;
     static constexpr int ROWB = Op::BK * Op::ELT;          // 64 or 128 bytes per LDS row
     static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
     static constexpr int RPL = 1024 / ROWB;                // rows per direct load
     static constexpr int EPC = 16 / Op::ELT;               // K elements per chunk
-    static constexpr int WM = BM / 2, WN = BN / 2;
+    static constexpr int WM = BM / 2, WN = BN / WAVES_N;
     static constexpr int TI = WM / 32, TJ = WN / 32;
     static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
     // one aligned 4-byte scale word per row (the four blocks containing the K
@@ -111,11 +143,13 @@ struct RingGeometry {
     static constexpr int SB_BYTES = Op::MX && !Op::SG ? BN * 4 : 0;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
     static constexpr int LDS_BYTES = S * STAGE_BYTES;
-    static constexpr int NA = BM / RPL / 4;                // direct loads per wave per K tile
-    static constexpr int NB = BN / RPL / 4;
+    static constexpr int NA = BM / RPL / WAVES;            // direct loads per wave per K tile
+    static constexpr int NB = BN / RPL / WAVES;
     static constexpr int NSA = Op::MX && !Op::SG ? 1 : 0;  // 4-byte scale loads: 64 rows each
     static constexpr int NSB = Op::MX && !Op::SG ? 1 : 0;
     static constexpr int LOADS = NA + NB + NSA + NSB;
+    static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
+    static_assert(WAVES == 4 || !Op::MX || Op::SG, "eight waves: MX with scale groups only");
     static_assert((ROWB == 64 && CH == 4 && RPL == 16) || (ROWB == 128 && CH == 8 && RPL == 8),
                   "64- or 128-byte LDS rows");
     static_assert(NA % 2 == 0 && NB % 2 == 0, "loads split in halves; swizzle parity");
@@ -146,6 +180,10 @@ struct EarlyPlan {
     // LDS: the two stages, then (scale groups) two buffers of 16 bytes per
     // A and B row
     static constexpr int SG_BYTES = Op::SG ? 2 * (BM + BN) * 16 : 0;
+    // direct loads per wave for one scale group: one 16-byte load of 64 rows
+    // per wave and operand with four waves, one of either operand with eight
+    static constexpr int GROUP_LOADS = Op::SG ? 8 / G::WAVES : 0;
+    static constexpr int WAVES = G::WAVES;
     static_assert(G::CH == 8, "128-byte LDS rows");
     static_assert(AM > 0 && XM > 0 && YM > 0 && LX > 0 && LY >= 0 && LA >= 0, "phase split");
     static_assert(YA >= 1 && YA <= TI, "first A fragment read in phase Y");

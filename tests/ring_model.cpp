@@ -1,7 +1,7 @@
 // Host model of the early-release ring protocol of gemm_early, compiled by
 // tests/test_ring_protocol.py with g++ and driven through ctypes.  It replays
 // the kernel's own step tables (ring_plan.hpp: kEarlyPrologue, kEarlyLoop,
-// load_step, vm_wait, read_ktile) for the four waves of a workgroup over a
+// load_step, vm_wait, read_ktile) for the four or eight waves of a workgroup over a
 // persistent run of `tiles` tiles of `nk` K tiles, and checks the ring's
 // hand-offs ("B200 TMA Pipeline Designer", section E step 8: every stage's
 // ready and free have a unique producer and consumer; section B: a consumer
@@ -32,8 +32,6 @@
 namespace {
 
 using namespace mce;
-
-constexpr int kWaves = 4;
 
 enum Area { STAGE0 = 0, STAGE1 = 1, GROUP0 = 2, GROUP1 = 3 };
 
@@ -73,12 +71,14 @@ int run(const int *pro, int npro, const int *loop, int nloop, int tiles, int nk,
         char *msg, int msg_len)
 {
     using P = EarlyPlan<Op, 256, 256>;
+    constexpr int kWaves = P::WAVES;
+    constexpr int kGroupLoads = P::GROUP_LOADS;
     Model m;
     m.loads_per_tile = P::LOADS;
     m.gk = P::GK;
     m.sg = Op::SG ? 1 : 0;
     const int total = tiles * nk;   // K tiles the workgroup consumes
-    Wave waves[kWaves];
+    Wave waves[8];
     int epoch = 0;
 
     auto stage_area = [](int ktile) { return (ktile & 1) ? STAGE1 : STAGE0; };
@@ -142,11 +142,15 @@ int run(const int *pro, int npro, const int *loop, int nloop, int tiles, int nk,
                     read(w, stage_area(t), t);
                 continue;
             }
+            // scale groups: each wave's share, kGroupLoads loads (with
+            // eight waves, waves 0-3 load the A rows, 4-7 the B rows: the
+            // share is numbered by wave so every load of a group is distinct)
+            const int g_lo = kWaves == 8 ? (w >> 2) : 0;
             if (Op::SG && st == RS_ISSUE_GROUP0)
-                issue_loads(w, GROUP0 + group_buffer(0), 0, 0, 2);
+                issue_loads(w, GROUP0 + group_buffer(0), 0, g_lo, g_lo + kGroupLoads);
             if (Op::SG && st == RS_ISSUE_GROUP && g % P::UNR == 0) {
                 const int q = g / P::GK + 1;
-                issue_loads(w, GROUP0 + group_buffer(q), q, 0, 2);
+                issue_loads(w, GROUP0 + group_buffer(q), q, g_lo, g_lo + kGroupLoads);
             }
         }
     };
@@ -173,7 +177,7 @@ int run(const int *pro, int npro, const int *loop, int nloop, int tiles, int nk,
         by_content[{m.loads[id].area, m.loads[id].content}].push_back(id);
     for (const Read &r : m.reads) {
         auto it = by_content.find({r.area, r.content});
-        const int expect = r.area <= STAGE1 ? kWaves * m.loads_per_tile : kWaves * 2;
+        const int expect = r.area <= STAGE1 ? kWaves * m.loads_per_tile : kWaves * kGroupLoads;
         if (it == by_content.end() || (int)it->second.size() != expect) {
             std::snprintf(buf, sizeof buf, "read of area %d content %d: %d loads issued, %d expected",
                           r.area, r.content, it == by_content.end() ? 0 : (int)it->second.size(),
@@ -193,16 +197,21 @@ int run(const int *pro, int npro, const int *loop, int nloop, int tiles, int nk,
             }
         }
     }
-    // each load index of a content issued exactly once per wave
+    // each load index of a content issued exactly once by every wave (stage
+    // loads) or once per wave half (eight waves' group loads)
+    // (four waves: each issues both indices, A and B rows; eight: waves 0-3
+    // index 0, waves 4-7 index 1, so four issues per index either way)
+    const int per_index = kWaves * kGroupLoads / 2;
     for (auto &kv : by_content) {
-        std::vector<int> seen(kv.first.first <= STAGE1 ? m.loads_per_tile : 2, 0);
+        const bool stage = kv.first.first <= STAGE1;
+        std::vector<int> seen(stage ? m.loads_per_tile : 2, 0);
         for (int id : kv.second)
             if (m.loads[id].index < (int)seen.size())
                 ++seen[m.loads[id].index];
         // contents that are read must be whole (checked above); none may be
         // loaded twice
         for (int c : seen)
-            if (c != 0 && c != kWaves) {
+            if (c != 0 && c != (stage ? kWaves : per_index)) {
                 std::snprintf(buf, sizeof buf, "area %d content %d: a load issued %d times", kv.first.first,
                               kv.first.second, c / kWaves);
                 m.error(buf);
@@ -277,6 +286,9 @@ int ring_pending_loads(int op)
     switch (op) {
     case 0: return EarlyPlan<Bf16Ring64, 256, 256>::LA;
     case 1: return EarlyPlan<Bf16Ring64S16, 256, 256>::LA;
+    case 7: return EarlyPlan<Bf16Ring64W8, 256, 256>::LA;
+    case 8: return EarlyPlan<Bf16Ring64S16W8, 256, 256>::LA;
+    case 9: case 10: return EarlyPlan<Mxfp8Ring128GW8, 256, 256>::LA;
     case 2: case 4: return EarlyPlan<Mxfp8Ring128, 256, 256>::LA;
     case 3: case 5: return EarlyPlan<Mxfp8Ring128G, 256, 256>::LA;
     case 6: return EarlyPlan<Fp4Ring128G, 256, 256>::LA;
@@ -288,7 +300,7 @@ int ring_pending_loads(int op)
 int ring_unroll(int op)
 {
     switch (op) {
-    case 3: case 5: return EarlyPlan<Mxfp8Ring128G, 256, 256>::UNR;
+    case 3: case 5: case 9: case 10: return EarlyPlan<Mxfp8Ring128G, 256, 256>::UNR;
     case 6: return EarlyPlan<Fp4Ring128G, 256, 256>::UNR;
     default: return 1;
     }
@@ -305,6 +317,10 @@ int ring_model(int op, const int *pro, int npro, const int *loop, int nloop, int
     case 4: return run<E5m2Ring128>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
     case 5: return run<E5m2Ring128G>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
     case 6: return run<Fp4Ring128G>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
+    case 7: return run<Bf16Ring64W8>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
+    case 8: return run<Bf16Ring64S16W8>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
+    case 9: return run<Mxfp8Ring128GW8>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
+    case 10: return run<E5m2Ring128GW8>(pro, npro, loop, nloop, tiles, nk, wait_delta, msg, msg_len);
     default: return -1;
     }
 }

@@ -29,8 +29,8 @@ from gpu_util import DeviceProblem, expected_bits, run_problem
 
 pytestmark = pytest.mark.gpu
 
-BF16_LEVELS = [1, 2, 3, 4, 5, 6, 7]
-MX_LEVELS = [3, 5, 6, 7]
+BF16_LEVELS = [1, 2, 3, 4, 5, 6, 7, 9]
+MX_LEVELS = [3, 5, 6, 7, 9]
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 
 
@@ -50,7 +50,10 @@ def level_should_accept(level, p):
         return True
     a_kc = (p.b_col_major if p.c_col_major else not p.a_col_major)
     b_kc = (not p.a_col_major if p.c_col_major else p.b_col_major)
-    return a_kc and b_kc and p.lda % 8 == 0 and p.ldb % 8 == 0 and p.K % 8 == 0
+    direct = a_kc and b_kc and p.lda % 8 == 0 and p.ldb % 8 == 0 and p.K % 8 == 0
+    if level == 9:   # whole 64-wide K tiles, at least two
+        return direct and p.K % 64 == 0 and p.K > 64
+    return direct
 
 
 def run_level(p, level):
@@ -471,7 +474,7 @@ LARGE_RAGGED_K = {"ktail": LARGE_RAGGED, "kwhole": {BF16: (4100, 8200, 1024), E4
 SCALE_LD = {"ktail": 36, "kwhole": 36, "kgroups": 48}
 
 
-@pytest.mark.parametrize("level", [5, 6, 7, None])
+@pytest.mark.parametrize("level", [5, 6, 7, 9, None])
 @pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
 @pytest.mark.parametrize("kind", ["ktail", "kwhole", "kgroups"])
 def test_large_ragged_integer_exact(level, fmt, kind):
@@ -544,7 +547,7 @@ def test_large_ragged_alpha_beta_sampled(level, fmt, kind):
     assert ok, f"{bad} sampled entries out of bound (worst {worst})"
 
 
-@pytest.mark.parametrize("level", [5, 6, None])
+@pytest.mark.parametrize("level", [5, 6, 9, None])
 @pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
 def test_whole_tiles_bf16_output_bitwise(level, fmt):
     """Whole 256x256 tiles, K a multiple of every K tile, bf16 output with
@@ -570,7 +573,7 @@ def test_whole_tiles_bf16_output_bitwise(level, fmt):
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
 
 
-@pytest.mark.parametrize("level", [5, 6])
+@pytest.mark.parametrize("level", [5, 6, 9])
 @pytest.mark.parametrize("fmt,shape,alpha", [(BF16, (4096, 4352, 512), 1.0),
                                              (BF16, (8448, 4096, 256), 0.5),
                                              (E4M3FN, (4096, 4352, 1024), 1.0)],

@@ -18,7 +18,9 @@ CSRC = os.path.join(ROOT, "matrix_core_engineering_amd", "csrc")
 SRC = os.path.join(ROOT, "tests", "ring_model.cpp")
 
 OPS = {0: "bf16 32x32x16", 1: "bf16 16x16x32", 2: "MX E4M3", 3: "MX E4M3 scale groups",
-       4: "MX E5M2", 5: "MX E5M2 scale groups", 6: "MX E2M1"}
+       4: "MX E5M2", 5: "MX E5M2 scale groups", 6: "MX E2M1",
+       7: "level 9 bf16 32x32x16", 8: "level 9 bf16 16x16x32", 9: "level 9 MX E4M3",
+       10: "level 9 MX E5M2"}
 
 
 @pytest.fixture(scope="module")
