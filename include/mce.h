@@ -84,7 +84,9 @@ enum {
 
 /*
  * bf16 GEMM.  A: bf16 bits (uint16), B: bf16 bits, fp32 accumulate.
- * Picks the fastest level that accepts the problem.
+ * Picks the fastest level that accepts the problem: level 9 when the
+ * problem has at least two 256x256 tiles but no more than the device has
+ * compute units and level 9 accepts it, else level 6.
  * ("B200 GEMM Optimization Ladder", section E steps 1-8.)
  */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,

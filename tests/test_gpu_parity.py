@@ -358,19 +358,22 @@ def test_mx_mn_major_operands(fmt, layout, level):
 @pytest.mark.parametrize("level", MX_LEVELS)
 def test_mx_scale_semantics(level):
     """All data 1.0; scale bytes chosen per (row, block): the result is the
-    closed form sum_b 32 * 2^(ea(i,b) + eb(j,b)), written out here."""
-    M, N, K = 64, 64, 128
+    closed form sum_b 32 * 2^(ea(i,b) + eb(j,b)), written out here.  (K =
+    128, four blocks; level 9 takes whole scale groups: K = 512, 16 blocks.)"""
+    M, N = 64, 64
+    K = 512 if level == 9 else 128
+    nb = K // 32
     p = make_problem(M, N, K, fmt=E4M3FN, c_dtype=OUT_F32, seed=7)
     p.A[:] = 0x38
     p.B[:] = 0x38
-    ea = (np.arange(M)[:, None] + 3 * np.arange(4)[None, :]) % 9 - 4      # -4..4
-    eb = (2 * np.arange(N)[:, None] + np.arange(4)[None, :]) % 5 - 2      # -2..2
+    ea = (np.arange(M)[:, None] + 3 * np.arange(nb)[None, :]) % 9 - 4      # -4..4
+    eb = (2 * np.arange(N)[:, None] + np.arange(nb)[None, :]) % 5 - 2      # -2..2
     p.SA[:] = (ea + 127).astype(np.uint8)
     p.SB[:] = (eb + 127).astype(np.uint8)
     p.SA[0, 0], p.SB[1, 3] = 127, 127
     ea[0, 0], eb[1, 3] = 0, 0
     want = np.zeros((M, N))
-    for b in range(4):
+    for b in range(nb):
         want += 32.0 * np.exp2(ea[:, b][:, None] + eb[:, b][None, :])
     r = run_level(p, level)
     assert np.array_equal(r[0], want)
@@ -474,9 +477,16 @@ LARGE_RAGGED_K = {"ktail": LARGE_RAGGED, "kwhole": {BF16: (4100, 8200, 1024), E4
 SCALE_LD = {"ktail": 36, "kwhole": 36, "kgroups": 48}
 
 
-@pytest.mark.parametrize("level", [5, 6, 7, 9, None])
-@pytest.mark.parametrize("fmt", [BF16, E4M3FN], ids=["bf16", "mx"])
-@pytest.mark.parametrize("kind", ["ktail", "kwhole", "kgroups"])
+# level 9 takes whole K tiles (bf16: K a multiple of 64) and, for MX, whole
+# scale groups with 16-byte scale rows: of these shapes only "kgroups" and
+# the bf16 "kwhole" (mce.h)
+LARGE_RAGGED_CASES = [(lvl, fmt, kind) for lvl in (5, 6, 7, 9, None) for fmt in (BF16, E4M3FN)
+                      for kind in ("ktail", "kwhole", "kgroups")
+                      if lvl != 9 or kind == "kgroups" or (kind == "kwhole" and fmt == BF16)]
+
+
+@pytest.mark.parametrize("level,fmt,kind", LARGE_RAGGED_CASES,
+                         ids=[f"{k}-{'bf16' if f == BF16 else 'mx'}-{l}" for l, f, k in LARGE_RAGGED_CASES])
 def test_large_ragged_integer_exact(level, fmt, kind):
     """Exact-integer inputs at a ragged large shape: row and column sums of C
     equal A(B 1) and (1^T A) B exactly, and sampled entries match the oracle
