@@ -1,4 +1,4 @@
-"""Plain fp64 CPU reference GEMM -- test infrastructure only.
+"""Plain fp64 CPU references (GEMM, attention) -- test infrastructure only.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It loads ``liboracle.so`` (built by gcc from
@@ -9,7 +9,9 @@ exact fp64 decoding of bf16 / MX (E4M3FN, E5M2, E2M3, E3M2, E2M1 elements,
 E8M0 scales; OCP MX v1.0) inputs and fp64 sums over k in
 order (the baseline contract of "B200 GEMM Optimization Ladder", section E
 step 1; block-scaled operands as in "B200 TMEM Lifecycle Planner", section A1
-case 2).  ``check`` applies the acceptance bound to a GPU result.
+case 2).  ``attention`` is the plain scaled dot-product attention of
+attention.c.  ``check`` and ``check_attention`` apply the acceptance bounds
+to a GPU result.
 """
 import ctypes
 import os
@@ -59,6 +61,9 @@ def _load():
     lib.oracle_e8m0_to_f64.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
+    lib.oracle_attention.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, f32, i32, i64, i64,
+                                     vp, vp, vp]
+    lib.oracle_attention.restype = i32
     _lib = lib
     return lib
 
@@ -170,4 +175,29 @@ def gemm_entries(M, N, K, A, lda, a_col_major, B, ldb, b_col_major, ii, jj,
     return out, tsum
 
 
-from .check import check, tolerance  # noqa: E402,F401
+def attention(batch, heads, seq_q, seq_k, dim, Q, K, V, scale, causal=False, row_begin=0,
+              row_end=None):
+    """Reference attention rows [row_begin, row_end) of the flattened
+    batch x heads x seq_q query rows; Q, K, V hold bf16 bits (uint16, any
+    shape with batch*heads*seq*dim elements in that order).  Returns (O, PV,
+    SMAX): O and PV of shape (rows, dim), SMAX of shape (rows,)."""
+    rows_total = batch * heads * seq_q
+    if row_end is None:
+        row_end = rows_total
+    q, pq = _arr(Q, np.uint16)
+    k, pk = _arr(K, np.uint16)
+    v, pvv = _arr(V, np.uint16)
+    rows = row_end - row_begin
+    o = np.zeros((max(rows, 0), dim), dtype=np.float64)
+    pv = np.zeros((max(rows, 0), dim), dtype=np.float64)
+    smax = np.zeros(max(rows, 0), dtype=np.float64)
+    rc = _load().oracle_attention(batch, heads, seq_q, seq_k, dim, pq, pk, pvv, float(scale),
+                                  int(bool(causal)), row_begin, row_end, o.ctypes.data,
+                                  pv.ctypes.data, smax.ctypes.data)
+    del q, k, v
+    if rc != 0:
+        raise ValueError(f"oracle_attention failed with code {rc}")
+    return o, pv, smax
+
+
+from .check import check, check_attention, tolerance, attention_tolerance  # noqa: E402,F401

@@ -1,4 +1,5 @@
-"""Builds liboracle.so from oracle.c with gcc (test infrastructure only).
+"""Builds liboracle.so from oracle.c (GEMM) and attention.c with gcc (test
+infrastructure only).
 
 -O2 without -ffast-math keeps every fp64 sum in k order; -ffp-contract=off
 keeps products and sums separately rounded.
@@ -8,6 +9,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
+SOURCES = [SRC, os.path.join(HERE, "attention.c")]
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
@@ -16,7 +18,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
 
 def build_oracle(verbose=False):
     tmp = LIB_PATH + ".tmp"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, *SOURCES, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

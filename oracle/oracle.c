@@ -3,8 +3,8 @@
  *
  * This file is the oracle that the GPU kernels are checked against.  Only the
  * test suite, the smoke check and the benchmark's CPU-baseline leg may load it.
- * It shares no code, header, table or helper with the HIP library: it is built
- * by gcc on its own, from this file alone.
+ * It shares no code, header, table or helper with the HIP library: gcc builds
+ * it on its own, from this file and attention.c (the attention reference).
  *
  * What it computes (the plain definition, nothing more):
  *     C <- alpha * op(A) * op(B) + beta * C0
