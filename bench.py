@@ -32,6 +32,11 @@ level of the ladder on every standard workload.
 element format at its default level, with W warm-up and K timed launches.
 --tile-orders prints one JSON line timing the 8192^3 bf16 and MX GEMMs
 under each tile walk (XCD-major or dispatch order, several group sizes).
+--attention prints one JSON line timing the fused attention forward on the
+16k-token workloads (4 x 4096 tokens, 16 heads of 128; causal and full),
+with the oracle timed on a row sample beside it; --only attn-causal|attn-full
+runs one of them R times for profiling.  The default line carries the same
+timings in `attention`.
 """
 import argparse
 import hashlib
@@ -71,7 +76,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop", "cfg1", "cfg2", "cfg3"]
+    ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop", "cfg1", "cfg2", "cfg3",
+                                       "attn-causal", "attn-full"]
                     + list(MX_FORMAT_NAMES),
                     default=None)
     ap.add_argument("--levels", action="store_true",
@@ -80,6 +86,8 @@ def parse_args():
                     help="time every standard workload against its roofline (one JSON line)")
     ap.add_argument("--mx-formats", action="store_true",
                     help="time the 8192^3 MX GEMM in every element format (one JSON line)")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the fused attention workloads (one JSON line)")
     ap.add_argument("--tile-orders", action="store_true",
                     help="time the 8192^3 GEMMs under each tile walk (one JSON line)")
     ap.add_argument("--reps", type=int, default=3)
@@ -389,6 +397,86 @@ def read_traffic():
         return None
 
 
+class AttentionWorkload:
+    """One attention workload (bf16 Q, K, V resident on the device, bf16 O)
+    through attention_bf16."""
+
+    def __init__(self, name, dev):
+        import torch
+        from matrix_core_engineering_amd.inputs import (ATTENTION_WORKLOADS, attention_flops,
+                                                        attention_inputs)
+        self.name = name
+        self.w = w = dict(ATTENTION_WORKLOADS[name])
+        self.shape = (w["batch"], w["heads"], w["seq_q"], w["seq_k"], w["dim"])
+        self.host = attention_inputs(*self.shape, seed=7)
+        self.Q, self.K, self.V = (torch.from_numpy(x.view(np.int16)).to(dev) for x in self.host)
+        self.O = torch.zeros_like(self.Q)
+        self.scale = 1.0 / float(np.sqrt(w["dim"]))
+        self.flops = attention_flops(*self.shape, w["causal"])
+
+    def run(self, stream):
+        import matrix_core_engineering_amd as mce
+        return mce.attention_bf16(*self.shape, self.Q, self.K, self.V, self.O, mce.MCE_OUT_BF16,
+                                  self.scale, self.w["causal"], stream=stream)
+
+    def describe(self):
+        B, H, S, T, D = self.shape
+        return (f"attention forward, {B} x {S} queries and keys, {H} heads of {D}, "
+                f"{'causal' if self.w['causal'] else 'full'}, N(0,1) bf16 Q/K/V, bf16 out")
+
+
+def attention_cpu_baseline(work, target_s):
+    """The oracle on the first query rows of the flattened batch x heads x
+    seq_q order of an attention workload, sized to about target_s seconds,
+    with those rows of the GPU result checked; flops counted as the
+    kernel's (4 dim per visible query-key pair)."""
+    import oracle
+    B, H, S, T, D = work.shape
+    causal = work.w["causal"]
+    q, k, v = work.host
+
+    def pairs(r0, r1):
+        i = np.arange(r0, r1) % S
+        if not causal:
+            return float(len(i) * T)
+        return float(np.clip(i + T - S + 1, 0, T).sum())
+
+    cal = min(B * H * S, 2 * S)      # two whole heads: every row length
+    t0 = time.perf_counter()
+    oracle.attention(B, H, S, T, D, q, k, v, np.float32(work.scale), causal, 0, cal)
+    per_pair = max((time.perf_counter() - t0) / pairs(0, cal), 1e-12)
+    rows = int(min(B * H * S, max(cal, target_s / (per_pair * pairs(0, S)) * S)))
+    t0 = time.perf_counter()
+    oref, pv, smax = oracle.attention(B, H, S, T, D, q, k, v, np.float32(work.scale), causal,
+                                      0, rows)
+    secs = time.perf_counter() - t0
+    got = work.O.reshape(-1, D)[:rows].cpu().numpy().view(np.uint16)
+    got = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ok, worst, _ = oracle.check_attention(got, oref, pv, smax, T, True)
+    return {"value": 4.0 * D * pairs(0, rows) / secs / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the first {rows} of {B * H * S} query rows (batch x head x query order), "
+                      f"fp64, {secs:.1f} s",
+            "seconds": secs, "sample_rows_checked_ok": bool(ok),
+            "sample_worst_err_over_tol": worst}
+
+
+def attention_timings(dev, stream, warmup, steps, cpu_seconds=None):
+    out = {}
+    for name in ("causal", "full"):
+        work = AttentionWorkload(name, dev)
+        t, _ = timed_steps(work, warmup, steps, stream)
+        ms = float(np.mean(t))
+        tf = work.flops / (ms * 1e-3) / 1e12
+        out[name] = {"workload": work.describe(), "flops_per_launch": work.flops,
+                     "us_per_launch": ms * 1e3, "us_median": float(np.median(t)) * 1e3,
+                     "tflops": tf, "peak_tflops": PEAK_BF16, "frac_of_peak": tf / PEAK_BF16}
+        if cpu_seconds:
+            out[name]["cpu_baseline"] = attention_cpu_baseline(work, cpu_seconds)
+        del work
+    return out
+
+
 def cpu_baseline(work, target_s):
     """Times the oracle on rows [0, R) of the bf16 workload (R sized for
     about target_s seconds) and checks those rows of the GPU result."""
@@ -621,6 +709,18 @@ def main():
     if args.tile_orders:
         tile_orders(args, dev, stream)
         return
+    if args.attention:
+        res = attention_timings(dev, stream, args.warmup, args.steps,
+                                None if args.no_cpu_baseline else args.cpu_seconds)
+        print(json.dumps({"attention": res}), flush=True)
+        return
+    if args.only in ("attn-causal", "attn-full"):
+        work = AttentionWorkload(args.only[5:], dev)
+        for _ in range(args.reps + 1):
+            work.run(stream)
+        torch.cuda.synchronize()
+        print(f"ran {args.only} x {args.reps + 1}", flush=True)
+        return
     if args.only == "loop":
         res = matrix_core_ceiling(dev, stream, reps=args.reps)
         print(json.dumps({"matrix_core_loop": res}), flush=True)
@@ -666,6 +766,7 @@ def main():
     ms_per_step = float(np.mean(t_bf16))
     value = bf16.p.flops / (ms_per_step * 1e-3) / 1e12
     tf_mx = mx.p.flops / (float(np.mean(t_mx)) * 1e-3) / 1e12
+    attention = attention_timings(dev, stream, args.warmup, args.steps)
     traffic = read_traffic()
     # the default bf16 kernel for whole 256x256 bf16 tiles runs 16x16x32
     loop_bf16 = ceiling["bf16_16x16x32"]["tflops"]
@@ -695,6 +796,7 @@ def main():
                       "us_per_launch": float(np.mean(t_mx)) * 1e3,
                       "us_median": float(np.median(t_mx)) * 1e3,
                       "sustained_loop_tflops": loop_mx, "frac_of_sustained_loop": tf_mx / loop_mx},
+           "attention": attention,
            "clocks": clocks, "matrix_core_loop": ceiling, "wall_s_timed": wall}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(bf16, args.cpu_seconds)

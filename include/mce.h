@@ -297,6 +297,35 @@ enum { MCE_LOOP_BF16_32X32X16 = 0, MCE_LOOP_BF16_16X16X32 = 1, MCE_LOOP_MXFP8_32
 int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *out,
                          int blocks, int iters, void *stream);
 
+/*
+ * Fused attention forward on the same matrix cores: for every batch b, head h
+ * and query row i,
+ *     o(b,h,i,:) = sum_j softmax_j(scale * q(b,h,i,:) . k(b,h,j,:)) v(b,h,j,:)
+ * over the keys j visible to i: all j < seq_k, or with causal != 0 those
+ * with j <= i + seq_k - seq_q (the last query row sees every key).  A row
+ * with no visible key is written as zeros.  The pages name this workload
+ * only through its score, probability and output tiles (S, P, O) and their
+ * reuse ("B200 TMEM Lifecycle Planner", section A2 trigger 2, section E
+ * steps 1-7); the definition is the standard one.
+ *   Q        batch x heads x seq_q x head_dim bf16 bits, dim contiguous
+ *   K, V     batch x heads x seq_k x head_dim bf16 bits, dim contiguous
+ *   O        batch x heads x seq_q x head_dim, MCE_OUT_BF16 (round to
+ *            nearest even) or MCE_OUT_F32 (o_dtype); written, never read
+ *   scale    the score scale (commonly 1 / sqrt(head_dim))
+ * Scores and P V accumulate in fp32; the probabilities enter the P V
+ * product as bf16.  Device pointers owned by the caller; nothing allocated;
+ * asynchronous on `stream`.
+ * Errors: MCE_EINVAL for negative sizes, head_dim < 1, an unknown o_dtype,
+ * NULL pointers that would be used, O overlapping Q, K or V, one (batch,
+ * head) slice of 2^31 bytes or more; MCE_EUNSUPPORTED on a device other
+ * than gfx950, for head_dim other than 64 or 128, or for Q, K, V not
+ * 16-byte aligned (O: 8 bytes for bf16, 16 for fp32); MCE_ELAUNCH for a
+ * failed launch.  batch * heads * seq_q == 0 launches nothing.
+ */
+int attention_bf16(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                   const void *Q, const void *K, const void *V, void *O, int o_dtype,
+                   float scale, int causal, void *stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char *gemm_status_string(int status);
 

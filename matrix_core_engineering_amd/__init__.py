@@ -13,6 +13,7 @@ import os
 __all__ = ["gemm_bf16", "gemm_mxfp8", "gemm_bf16_level", "gemm_mxfp8_level",
            "gemm_bf16_pick_level", "gemm_mxfp8_pick_level", "gemm_mx",
            "gemm_mx_level", "gemm_mx_pick_level", "gemm_bf16_order", "gemm_mx_order",
+           "attention_bf16",
            "MCE_MX_E4M3", "MCE_MX_E5M2",
            "MCE_MX_E2M3", "MCE_MX_E3M2", "MCE_MX_E2M1",
            "gemm_status_string", "MceError", "lib_path", "load",
@@ -31,7 +32,7 @@ EXPORTED_SYMBOLS = ("gemm_bf16", "gemm_mxfp8", "gemm_bf16_level",
                     "gemm_mxfp8_level", "gemm_bf16_pick_level",
                     "gemm_mxfp8_pick_level", "gemm_mx", "gemm_mx_level",
                     "gemm_mx_pick_level", "gemm_bf16_order", "gemm_mx_order",
-                    "mce_matrix_core_loop", "gemm_status_string")
+                    "attention_bf16", "mce_matrix_core_loop", "gemm_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -76,6 +77,7 @@ def load():
     lib.gemm_mx_pick_level.argtypes = [i32] + mnk + [vp, i64, i32, vp, i64, vp, i64, i32, vp, i64]
     lib.gemm_bf16_order.argtypes = [i32, i32, i32] + bf16_args
     lib.gemm_mx_order.argtypes = [i32, i32, i32, i32] + mx_args
+    lib.attention_bf16.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp, i32, f32, i32, vp]
     lib.mce_matrix_core_loop.argtypes = [i32, vp, i64, vp, i32, i32, vp]
     for name in EXPORTED_SYMBOLS[:-1]:
         getattr(lib, name).restype = i32
@@ -202,6 +204,14 @@ def gemm_mx_order(level, xcd_order, group_m, elem_format, M, N, K, A, lda, a_col
                               int(c_dtype), float(alpha), float(beta), _stream(stream))
     return _check(st, f"gemm_mx_order({level}, {xcd_order}, {group_m}, {elem_format})",
                   raise_on_error)
+
+
+def attention_bf16(batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, o_dtype, scale,
+                   causal=False, stream=None, raise_on_error=True):
+    st = load().attention_bf16(batch, heads, seq_q, seq_k, head_dim, _ptr(Q), _ptr(K), _ptr(V),
+                               _ptr(O), int(o_dtype), float(scale), int(bool(causal)),
+                               _stream(stream))
+    return _check(st, "attention_bf16", raise_on_error)
 
 
 def mce_matrix_core_loop(shape, frags, n_frag, out, blocks, iters, stream=None,

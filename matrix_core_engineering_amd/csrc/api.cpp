@@ -518,6 +518,57 @@ int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *ou
                : MCE_ELAUNCH;
 }
 
+int attention_bf16(int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                   const void *Q, const void *K, const void *V, void *O, int o_dtype, float scale,
+                   int causal, void *stream)
+{
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim < 1)
+        return MCE_EINVAL;
+    if (o_dtype != MCE_OUT_F32 && o_dtype != MCE_OUT_BF16)
+        return MCE_EINVAL;
+    if (batch > INT32_MAX || heads > INT32_MAX || seq_q > INT32_MAX || seq_k > INT32_MAX ||
+        head_dim > INT32_MAX)
+        return MCE_EINVAL;
+    // each (batch, head) slice is addressed with 32-bit buffer offsets (the
+    // fp32 output slice included)
+    if (seq_q > (kMaxBytes - 1) / 4 / head_dim || seq_k > (kMaxBytes - 1) / 2 / head_dim)
+        return MCE_EINVAL;
+    const int64_t bh = batch * heads;   // both below 2^31: no overflow
+    if (bh > INT32_MAX || bh * ((seq_q + 127) / 128) > INT32_MAX)
+        return MCE_EINVAL;
+    if (bh == 0 || seq_q == 0)
+        return gfx950_cus() == 0 ? MCE_EUNSUPPORTED : MCE_OK;
+    if (!Q || !O || (seq_k > 0 && (!K || !V)))
+        return MCE_EINVAL;
+    const int64_t nq = bh * seq_q * head_dim, nk = bh * seq_k * head_dim;
+    const int64_t no = nq * (o_dtype == MCE_OUT_F32 ? 4 : 2);
+    if (overlaps(O, no, Q, nq * 2) || overlaps(O, no, K, nk * 2) || overlaps(O, no, V, nk * 2))
+        return MCE_EINVAL;
+    const int ncu = gfx950_cus();
+    if (ncu == 0)
+        return MCE_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128)
+        return MCE_EUNSUPPORTED;
+    // 16-byte vector loads of every operand row; 8- or 16-byte output stores
+    if ((uintptr_t)Q % 16 || (uintptr_t)K % 16 || (uintptr_t)V % 16 ||
+        (uintptr_t)O % (o_dtype == MCE_OUT_F32 ? 16 : 8))
+        return MCE_EUNSUPPORTED;
+    mce::AttnArgs a;
+    a.batch = (int)batch;
+    a.heads = (int)heads;
+    a.seq_q = (int)seq_q;
+    a.seq_k = (int)seq_k;
+    a.dim = (int)head_dim;
+    a.Q = (const uint16_t *)Q;
+    a.K = (const uint16_t *)K;
+    a.V = (const uint16_t *)V;
+    a.O = O;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    a.causal = causal ? 1 : 0;
+    a.o_dtype = o_dtype;
+    return mce::launch_attention(a, (hipStream_t)stream) == hipSuccess ? MCE_OK : MCE_ELAUNCH;
+}
+
 const char *gemm_status_string(int status)
 {
     switch (status) {

@@ -28,6 +28,18 @@ hipError_t launch_fast_fp4(int level, const GemmArgs &p, hipStream_t s);
 // layout, alignment and K, through registers.
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);
 
+// Fused attention forward (bf16 Q, K, V of batch x heads x seq x dim, dim
+// contiguous; O the same shape as Q).  scale_log2 = scale * log2(e).
+struct AttnArgs {
+    int batch, heads, seq_q, seq_k, dim;
+    const uint16_t *Q, *K, *V;
+    void *O;
+    float scale_log2;
+    int causal, o_dtype;
+};
+// Returns hipErrorInvalidValue for a head dimension other than 64 or 128.
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+
 // The matrix-core ceiling loop (shape: MCE_LOOP_*); returns
 // hipErrorInvalidValue for an unknown shape.
 hipError_t launch_matrix_core_loop(int shape, const void *frags, int n_frag, float *out, int blocks,

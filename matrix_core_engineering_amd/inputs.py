@@ -253,3 +253,32 @@ def integer_problem(M, N, K, *, fmt=BF16, seed=0, **kw):
         kw.setdefault("scale_exp_lo", 0)
         kw.setdefault("scale_exp_hi", 2)
     return make_problem(M, N, K, fmt=fmt, seed=seed, **kw)
+
+
+# Attention inputs: Q, K, V of batch x heads x seq x dim (dim contiguous) as
+# bf16 bits, drawn N(0, std^2) in that order with generators t = 10, 11, 12.
+# The standard workload: 16k tokens (4 sequences of 4096), 16 heads of 128.
+ATTENTION_WORKLOADS = {
+    "causal": dict(batch=4, heads=16, seq_q=4096, seq_k=4096, dim=128, causal=True),
+    "full": dict(batch=4, heads=16, seq_q=4096, seq_k=4096, dim=128, causal=False),
+}
+
+
+def attention_inputs(batch, heads, seq_q, seq_k, dim, *, seed=0, std=1.0):
+    """(Q, K, V) uint16 arrays of bf16 bits, shapes (batch, heads, seq, dim)."""
+    out = []
+    for t, seq in ((10, seq_q), (11, seq_k), (12, seq_k)):
+        x = torch.randn(batch, heads, seq, dim, generator=_gen(seed, t)) * std
+        out.append(to_bf16_bits(x))
+    return tuple(out)
+
+
+def attention_flops(batch, heads, seq_q, seq_k, dim, causal):
+    """Matrix-product flops of attention: 4 * dim per visible (query, key)
+    pair (the S and the P V products)."""
+    pairs = 0
+    for i in range(seq_q) if causal else ():
+        pairs += min(max(i + seq_k - seq_q + 1, 0), seq_k)
+    if not causal:
+        pairs = seq_q * seq_k
+    return 4.0 * dim * pairs * batch * heads

@@ -178,3 +178,35 @@ def test_mx_pick_level_by_format():
 def test_matrix_core_loop_rejects_bad_arguments(shape, frags, n_frag, out, blocks, iters):
     assert mce.mce_matrix_core_loop(shape, frags, n_frag, out, blocks, iters, stream=0,
                                     raise_on_error=False) == mce.MCE_EINVAL
+
+
+def attn(B=1, H=1, S=4, T=4, D=64, Q=FAKE_A, K=FAKE_B, V=0x40000000, O=FAKE_C, o_dtype=1,
+         scale=0.125, causal=0):
+    return mce.attention_bf16(B, H, S, T, D, Q, K, V, O, o_dtype, scale, causal, stream=0,
+                              raise_on_error=False)
+
+
+@pytest.mark.parametrize("args", [
+    dict(B=-1), dict(H=-1), dict(S=-1), dict(T=-1), dict(D=0),
+    dict(o_dtype=5),
+    dict(Q=0), dict(O=0), dict(K=0), dict(V=0),
+    dict(O=FAKE_A + 64),                               # O overlaps Q
+    dict(O=0x40000000 + 16),                           # O overlaps V
+    dict(S=1 << 24, D=128),                            # fp32 output slice of 8 GiB
+    dict(T=1 << 23, D=128),                            # K slice of 2 GiB
+    dict(D=1 << 40),                                   # head_dim beyond 32 bits
+    dict(B=1 << 20, H=1 << 12),                        # batch * heads above 2^31
+])
+def test_attention_invalid_arguments(args):
+    assert attn(**args) == mce.MCE_EINVAL
+
+
+def test_attention_empty_and_unsupported():
+    # nothing to compute: no pointer is used, so NULL is fine
+    for kw in (dict(B=0), dict(H=0), dict(S=0)):
+        st = attn(Q=0, K=0, V=0, O=0, **kw)
+        assert st in (mce.MCE_OK, mce.MCE_EUNSUPPORTED)
+    # no key at all: Q and O are still needed, K and V are not
+    assert attn(T=0, K=0, V=0, Q=0) == mce.MCE_EINVAL
+    assert attn(D=96) == mce.MCE_EUNSUPPORTED
+    assert attn(Q=FAKE_A + 8) == mce.MCE_EUNSUPPORTED

@@ -30,6 +30,8 @@ int h_swz8(int r) { return mce::swz8(r); }
 int h_swz8h(int r) { return mce::swz8h(r); }
 int h_swz4(int r) { return mce::swz4(r); }
 int h_swz4q(int r) { return mce::swz4q(r); }
+int h_attn_key_of_col(int j) { return mce::attn_key_of_col(j); }
+int h_swz_attn_k(int r, int d) { return mce::swz_attn_k(r, d); }
 int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 0; }
 }
 '''
@@ -296,3 +298,78 @@ def test_loads_after_spreads_evenly(lib, n, l):
     if l > 1:
         gaps = np.diff(pos)
         assert gaps.min() >= n // l and gaps.max() <= -(-n // l)
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attn_key_order_feeds_pv_operand(lib):
+    """The score columns' key order is a permutation of the 32 keys, and
+    accumulators 8t + e of lane half h (column 8q + 4h + c with q = 2t +
+    e // 4, c = e % 4) hold key 16t + 8h + e: the P operand of k-step t."""
+    keys = [lib.h_attn_key_of_col(j) for j in range(32)]
+    assert sorted(keys) == list(range(32))
+    for h in range(2):
+        for t in range(2):
+            for e in range(8):
+                col = 8 * (2 * t + e // 4) + 4 * h + e % 4
+                assert keys[col] == 16 * t + 8 * h + e
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+@pytest.mark.parametrize("blk", range(2))
+def test_attn_k_fragment_reads_conflict_free(lib, dim, blk):
+    """Lane l reads K row 32 blk + key(l % 32) at logical chunk 2s + l / 32;
+    rows of 2 * dim bytes."""
+    for s in range(dim // 16):
+        addrs = []
+        for l in range(64):
+            r = 32 * blk + lib.h_attn_key_of_col(l & 31)
+            c = (2 * s + (l >> 5)) ^ lib.h_swz_attn_k(r, dim)
+            addrs.append(r * 2 * dim + c * 16)
+        assert cycles_extra(addrs, 16, "read") == 0
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_attn_k_direct_loads_fill_each_row_once(lib, dim):
+    """The K tile's direct loads: 1 KiB per load, lane l at byte 16 l, row
+    load * rows_per_load + l / chunks, fetching logical chunk
+    (l % chunks) ^ swz(row); every (row, logical chunk) of the 64-row tile
+    exactly once, and the swizzle of rows 32 b + r equal to that of r."""
+    chunks = 2 * dim // 16
+    rpl = 1024 // (2 * dim)
+    seen = set()
+    for ld in range(64 // rpl):
+        for l in range(64):
+            r = ld * rpl + l // chunks
+            seen.add((r, (l % chunks) ^ lib.h_swz_attn_k(r, dim)))
+    assert seen == {(r, c) for r in range(64) for c in range(chunks)}
+    for r in range(32):
+        assert lib.h_swz_attn_k(r + 32, dim) == lib.h_swz_attn_k(r, dim)
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_attn_vt_writes_and_reads(lib, dim):
+    """V^T tile: row d holds 64 keys as 32 key-pair words, pair kp at
+    ((kp >> 2) ^ swz8(d)) * 16 + (kp & 3) * 4.  Each write instruction
+    (wave w, pass, element e; lanes h * 32 + kp write row
+    8 (2w + h + 8 pass) + e) is conflict-free under the 4-byte write rule,
+    every word of the tile is written once, and the P V operand reads (rows
+    32 b + l % 32, logical chunk 2 ts + l / 32) are conflict-free."""
+    written = set()
+    for w in range(4):
+        for ps in range(dim // 64):
+            for e in range(8):
+                addrs = []
+                for l in range(64):
+                    h, kp = l >> 5, l & 31
+                    d = 8 * (2 * w + h + 8 * ps) + e
+                    a = d * 128 + ((kp >> 2) ^ lib.h_swz8(d)) * 16 + (kp & 3) * 4
+                    addrs.append(a)
+                    written.add(a)
+                assert cycles_extra(addrs, 4, "write") == 0
+    assert written == set(range(0, dim * 128, 4))
+    for b in range(dim // 32):
+        for ts in range(4):
+            addrs = [(32 * b + (l & 31)) * 128 + (((2 * ts + (l >> 5)) ^ lib.h_swz8(32 * b + (l & 31))) * 16)
+                     for l in range(64)]
+            assert cycles_extra(addrs, 16, "read") == 0
