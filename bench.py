@@ -24,9 +24,10 @@ Modes for profiling (no JSON): --only bf16|mxfp8|copy|e4m3|e5m2|e2m3|e3m2|e2m1
 L instead of the default one; copy: a 1 GiB
 device-to-device copy, the calibration of the HBM byte counters; the MX
 element-format names: the 8192^3 MX GEMM in that format; cfg1-cfg3: the
-single-tile, 4096^3 and ragged workloads).  --only loop prints the
+single-tile, 4096^3 and ragged workloads; skinny64 / skinny1: the 64 x 8192
+x 8192 and 1 x 8192 x 8192 bf16 GEMMs).  --only loop prints the
 matrix-core loop rates alone.  --configs prints one JSON line timing every
-standard workload against its own roofline; --levels one line timing every
+standard workload and the skinny shapes against their own rooflines; --levels one line timing every
 level of the ladder on every standard workload.
 --mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
 element format at its default level, with W warm-up and K timed launches.
@@ -77,7 +78,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop", "cfg1", "cfg2", "cfg3",
-                                       "attn-causal", "attn-full"]
+                                       "attn-causal", "attn-full", "skinny64", "skinny1"]
                     + list(MX_FORMAT_NAMES),
                     default=None)
     ap.add_argument("--levels", action="store_true",
@@ -107,8 +108,8 @@ class Workload:
 
     def __init__(self, cfg, dev):
         import torch
-        from matrix_core_engineering_amd.inputs import config_problem
-        self.p = p = config_problem(cfg)
+        from matrix_core_engineering_amd.inputs import config_problem, skinny_problem
+        self.p = p = config_problem(cfg) if isinstance(cfg, int) else skinny_problem(cfg)
 
         def up(a):
             v = {1: np.uint8, 2: np.int16, 4: np.int32}[a.dtype.itemsize]
@@ -186,14 +187,16 @@ class MxFormatWorkload:
     per 32 K with exponents -8..8, bf16 out) in one element format: 8-bit
     codes from U[-448, 448], the packed formats every code equally likely."""
 
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, a_col_major=False, b_col_major=True):
         import torch
         from matrix_core_engineering_amd.inputs import E4M3FN, E5M2, OUT_BF16, make_problem
         gfmt, self.code, self.peak = mx_format_table()[name]
         kw = (dict(dist="uniform", lo=-448.0, hi=448.0) if gfmt in (E4M3FN, E5M2)
               else dict(dist="codes"))
-        self.p = p = make_problem(8192, 8192, 8192, fmt=gfmt, a_col_major=False, b_col_major=True,
-                                  c_dtype=OUT_BF16, seed=5, name=f"mx_{name}_8192", **kw)
+        self.a_cm, self.b_cm = int(a_col_major), int(b_col_major)
+        self.p = p = make_problem(8192, 8192, 8192, fmt=gfmt, a_col_major=a_col_major,
+                                  b_col_major=b_col_major, c_dtype=OUT_BF16, seed=5,
+                                  name=f"mx_{name}_8192", **kw)
 
         def up(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -204,24 +207,29 @@ class MxFormatWorkload:
     def run(self, stream):
         import matrix_core_engineering_amd as mce
         p = self.p
-        return mce.gemm_mx(self.code, p.M, p.N, p.K, self.A, p.lda, 0, self.SA, p.ld_sa, self.B,
-                           p.ldb, 1, self.SB, p.ld_sb, self.C, p.ldc, 0, p.c_dtype, p.alpha,
-                           p.beta, stream=stream)
+        return mce.gemm_mx(self.code, p.M, p.N, p.K, self.A, p.lda, self.a_cm, self.SA, p.ld_sa,
+                           self.B, p.ldb, self.b_cm, self.SB, p.ld_sb, self.C, p.ldc, 0, p.c_dtype,
+                           p.alpha, p.beta, stream=stream)
 
     def level(self):
         import matrix_core_engineering_amd as mce
         p = self.p
-        return mce.gemm_mx_pick_level(self.code, p.M, p.N, p.K, self.A, p.lda, 0, self.SA, p.ld_sa,
-                                      self.B, p.ldb, 1, self.SB, p.ld_sb)
+        return mce.gemm_mx_pick_level(self.code, p.M, p.N, p.K, self.A, p.lda, self.a_cm, self.SA,
+                                      p.ld_sa, self.B, p.ldb, self.b_cm, self.SB, p.ld_sb)
 
 
 def mx_formats(args, dev, stream):
-    """One JSON line: each element format's 8192^3 GEMM at its default level,
-    HIP events on the launch stream around each launch."""
+    """One JSON line: each element format's 8192^3 GEMM at its default level
+    (and the 8-bit formats with MN-major operands: A column-major, or A
+    column-major and B row-major), HIP events on the launch stream around
+    each launch."""
     import torch
     res = {}
-    for name in MX_FORMAT_NAMES:
-        w = MxFormatWorkload(name, dev)
+    cases = [(n, n, False, True) for n in MX_FORMAT_NAMES]
+    cases += [(f"{n}_a_col", n, True, True) for n in ("e4m3", "e5m2")]
+    cases += [(f"{n}_a_col_b_row", n, True, False) for n in ("e4m3", "e5m2")]
+    for key, name, a_cm, b_cm in cases:
+        w = MxFormatWorkload(name, dev, a_cm, b_cm)
         for _ in range(args.warmup):
             w.run(stream)
         torch.cuda.synchronize()
@@ -233,8 +241,8 @@ def mx_formats(args, dev, stream):
         torch.cuda.synchronize()
         us = float(np.mean([ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)])) * 1e3
         tf = w.p.flops / (us * 1e-6) / 1e12
-        res[name] = {"level": w.level(), "us_per_launch": us, "tflops": tf, "peak_tflops": w.peak,
-                     "frac_of_peak": tf / w.peak}
+        res[key] = {"level": w.level(), "us_per_launch": us, "tflops": tf, "peak_tflops": w.peak,
+                    "frac_of_peak": tf / w.peak}
         del w
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "MX GEMM TFLOP/s by element format, 8192^3, bf16 out",
@@ -245,7 +253,8 @@ def mx_formats(args, dev, stream):
 CEILING_SHAPES = (("bf16_32x32x16", 0, "bf16", PEAK_BF16),
                   ("bf16_16x16x32", 1, "bf16", PEAK_BF16),
                   ("mxfp8_32x32x64", 2, "e4m3", PEAK_FP8),
-                  ("mxfp4_32x32x64", 3, "e2m1", PEAK_FP4))
+                  ("mxfp4_32x32x64", 3, "e2m1", PEAK_FP4),
+                  ("mxfp6_32x32x64", 4, "e2m3", PEAK_FP4))
 
 
 def matrix_core_ceiling(dev, stream, iters=2000, reps=3):
@@ -263,7 +272,10 @@ def matrix_core_ceiling(dev, stream, iters=2000, reps=3):
             "e4m3": (torch.rand(nfrag * 32, generator=g) * 896.0 - 448.0)
                     .to(torch.float8_e4m3fn).view(torch.uint8).to(dev),
             # every E2M1 code equally likely, two per byte (no NaN or Inf codes)
-            "e2m1": torch.randint(0, 256, (nfrag * 32,), generator=g, dtype=torch.uint8).to(dev)}
+            "e2m1": torch.randint(0, 256, (nfrag * 32,), generator=g, dtype=torch.uint8).to(dev),
+            # every E2M3 code equally likely, four per three bytes (no NaN or
+            # Inf codes in the 6-bit formats)
+            "e2m3": torch.randint(0, 256, (nfrag * 32,), generator=g, dtype=torch.uint8).to(dev)}
     blocks = 256
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     flops = blocks * 4 * iters * float(1 << 21)
@@ -294,22 +306,25 @@ def algorithmic_bytes(p):
 
 
 def configs(args, dev, stream):
-    """One JSON line: every standard workload through its default entry
-    point, each against the roofline that bounds it (matrix cores, or HBM
-    when its flops per algorithmic byte are below the ridge; a problem of
-    fewer 128x128 tiles than CUs occupies part of one CU set and is
-    reported as latency-bound, with no roofline fraction).  The
-    HBM-bound ragged workload is timed cold: a 512 MiB fill before every
-    launch evicts L2 and the Infinity Cache, and only the GEMM is timed."""
+    """One JSON line: every standard workload and the skinny shapes through
+    the default entry point, each against the roofline that bounds it
+    (matrix cores, or HBM when its flops per algorithmic byte are below the
+    ridge; a square-ish problem of fewer 128x128 tiles than CUs occupies
+    part of one CU set and is reported as latency-bound, with no roofline
+    fraction).  HBM-bound workloads are timed cold: a 512 MiB fill before
+    every launch evicts L2 and the Infinity Cache, and only the GEMM is
+    timed."""
     import torch
+    from matrix_core_engineering_amd.inputs import SKINNY
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     res = {}
-    for cfg in (1, 2, 3, 4, 5):
+    for cfg in (1, 2, 3, 4, 5) + tuple(SKINNY):
         w = Workload(cfg, dev)
         p = w.p
         peak = PEAK_FP8 if p.SA is not None else PEAK_BF16
         nbytes = algorithmic_bytes(p)
-        latency = ((p.M + 127) // 128) * ((p.N + 127) // 128) < 256
+        skinny = min(p.M, p.N) <= 256 and max(p.M, p.N) >= 4096
+        latency = not skinny and ((p.M + 127) // 128) * ((p.N + 127) // 128) < 256
         hbm_bound = not latency and p.flops / nbytes < peak * 1e12 / (PEAK_HBM * 1e9)
         for _ in range(args.warmup):
             w.run(stream)
@@ -319,7 +334,7 @@ def configs(args, dev, stream):
         evs = []
         for _ in range(args.steps):
             if hbm_bound:
-                scrub.fill_(cfg)
+                scrub.fill_(len(res) + 1)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -733,7 +748,9 @@ def main():
         print(f"ran {args.only} level {work.level()} x {args.reps + 1}", flush=True)
         return
     if args.only:
-        work = Workload({"bf16": 4, "mxfp8": 5, "cfg1": 1, "cfg2": 2, "cfg3": 3}[args.only], dev)
+        work = Workload({"bf16": 4, "mxfp8": 5, "cfg1": 1, "cfg2": 2, "cfg3": 3,
+                         "skinny64": "skinny_64x8192x8192_bf16",
+                         "skinny1": "skinny_1x8192x8192_bf16"}[args.only], dev)
         for _ in range(args.reps + 1):
             if args.order is not None:
                 xcd, gm = (int(v) for v in args.order.split(","))

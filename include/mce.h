@@ -101,8 +101,11 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
  * a(i,k) = e4m3(A(i,k)) * 2^(SA[i*ld_sa + k/32] - 127).  SB is N x ceil(K/32)
  * bytes, row-major with leading dimension ld_sb, scaling b(k,j) the same way
  * (the scale layout does not follow the operand layout).  Any operand layout;
- * MN-major operands (a_col_major == 1 or b_col_major == 0) run level 3, the
- * pipelined levels need both operands K-contiguous.  The scale byte 0xFF
+ * MN-major operands (a_col_major == 1 or b_col_major == 0) run levels 5-6
+ * through the LDS transpose loads when K is a positive multiple of 128, A
+ * and B are 16-byte aligned with lda, ldb multiples of 16 and the scale rows
+ * 4-byte aligned (ld_sa, ld_sb multiples of 4), else level 3; levels 7 and
+ * 9 need both operands K-contiguous.  The scale byte 0xFF
  * (NaN) and the element NaN codes propagate NaN.
  *
  * Accuracy: the matrix-core instruction sums each group of 8 consecutive K
@@ -158,7 +161,8 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  * run a kernel that stages the operands through registers (any layout,
  * alignment and K).  gemm_mxfp8_level accepts levels 3 and 5-7, 5-7 with the
  * K-contiguity and alignment rules above and scale rows padded to 4 bytes
- * (same meaning; its level 3 also takes any K and either operand layout).
+ * (same meaning; its level 3 also takes any K and either operand layout),
+ * and 5-6 for MN-major operands under the rules given with gemm_mxfp8.
  * Level 9 needs the level-4 rules and whole K tiles, at least two: bf16 K a
  * multiple of 64 and above 64; MX (8-bit elements) K a multiple of 512 with
  * 16-byte aligned scale rows (A, B, SA, SB 16-byte aligned, ld_sa and ld_sb
@@ -193,8 +197,12 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K,
  * Levels: 3 for every format; 5-7 for E4M3 and E5M2 under the rules of
  * gemm_mxfp8_level; 5-6 for E2M1 when lda and ldb are multiples of 32, K a
  * multiple of 512, A, B, SA and SB 16-byte aligned and ld_sa, ld_sb
- * multiples of 16; the 6-bit formats run level 3 only (other levels return
- * MCE_EUNSUPPORTED).
+ * multiples of 16; 5-6 for E2M3 and E3M2 when lda and ldb are multiples of
+ * 64, K a positive multiple of 128, A and B 16-byte aligned, SA and SB
+ * 4-byte aligned and ld_sa, ld_sb multiples of 4 (a three-stage direct-load
+ * pipeline of 96-byte K tiles); other levels, and the levels' cases outside
+ * those rules, return MCE_EUNSUPPORTED.  With no level given, the first
+ * matching rule picks level 6, else level 3.
  */
 int gemm_mx(int elem_format, int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda, int a_col_major,
@@ -279,12 +287,14 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
  * matrix-core rate for that shape and data.
  *   shape   MCE_LOOP_BF16_32X32X16 (the GEMM's 32x32 bf16 instruction),
  *           MCE_LOOP_BF16_16X16X32, MCE_LOOP_MXFP8_32X32X64 (the MX
- *           instruction with E4M3 operands) or MCE_LOOP_MXFP4_32X32X64 (the
- *           same instruction with E2M1 operands); MX scales all 1
+ *           instruction with E4M3 operands), MCE_LOOP_MXFP4_32X32X64 (the
+ *           same instruction with E2M1 operands) or MCE_LOOP_MXFP6_32X32X64
+ *           (with E2M3 operands); MX scales all 1
  *   frags   device pointer to n_frag fragments of 16 bytes (bf16 shapes:
  *           eight bf16) or 32 bytes (MX: 32 E4M3 codes; E2M1: 32 codes
- *           packed two per byte in the first 16 bytes, the rest unread);
- *           fragment
+ *           packed two per byte in the first 16 bytes; E2M3: 32 codes
+ *           packed four per three bytes in the first 24 bytes; the rest
+ *           unread); fragment
  *           (gid * 16 + i) % n_frag is lane gid's i-th operand register set
  *   out     device pointer to blocks * 256 floats, written
  * Errors: MCE_EINVAL for an unknown shape, a NULL pointer, n_frag < 1,
@@ -293,7 +303,7 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K,
  * nothing; asynchronous on `stream`.
  */
 enum { MCE_LOOP_BF16_32X32X16 = 0, MCE_LOOP_BF16_16X16X32 = 1, MCE_LOOP_MXFP8_32X32X64 = 2,
-       MCE_LOOP_MXFP4_32X32X64 = 3 };
+       MCE_LOOP_MXFP4_32X32X64 = 3, MCE_LOOP_MXFP6_32X32X64 = 4 };
 int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *out,
                          int blocks, int iters, void *stream);
 

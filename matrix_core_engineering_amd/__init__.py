@@ -20,13 +20,13 @@ __all__ = ["gemm_bf16", "gemm_mxfp8", "gemm_bf16_level", "gemm_mxfp8_level",
            "EXPORTED_SYMBOLS", "MCE_OK", "MCE_EINVAL", "MCE_EUNSUPPORTED",
            "MCE_ELAUNCH", "MCE_OUT_F32", "MCE_OUT_BF16", "mce_matrix_core_loop",
            "MCE_LOOP_BF16_32X32X16", "MCE_LOOP_BF16_16X16X32", "MCE_LOOP_MXFP8_32X32X64",
-           "MCE_LOOP_MXFP4_32X32X64"]
+           "MCE_LOOP_MXFP4_32X32X64", "MCE_LOOP_MXFP6_32X32X64"]
 
 MCE_OK, MCE_EINVAL, MCE_EUNSUPPORTED, MCE_ELAUNCH = 0, 1, 2, 3
 MCE_OUT_F32, MCE_OUT_BF16 = 0, 1
 MCE_MX_E4M3, MCE_MX_E5M2, MCE_MX_E2M3, MCE_MX_E3M2, MCE_MX_E2M1 = 0, 1, 2, 3, 4
 MCE_LOOP_BF16_32X32X16, MCE_LOOP_BF16_16X16X32, MCE_LOOP_MXFP8_32X32X64 = 0, 1, 2
-MCE_LOOP_MXFP4_32X32X64 = 3
+MCE_LOOP_MXFP4_32X32X64, MCE_LOOP_MXFP6_32X32X64 = 3, 4
 
 EXPORTED_SYMBOLS = ("gemm_bf16", "gemm_mxfp8", "gemm_bf16_level",
                     "gemm_mxfp8_level", "gemm_bf16_pick_level",

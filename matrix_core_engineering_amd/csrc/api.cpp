@@ -123,6 +123,27 @@ bool fp4_fast_eligible(const Call &c)
            ((uintptr_t)c.SA % 16) == 0 && ((uintptr_t)c.SB % 16) == 0;
 }
 
+// FP6 levels 5-6: K-contiguous operands, K a multiple of 128, lda and ldb
+// multiples of 64 elements, 16-byte aligned A and B, 4-byte scale rows.
+bool fp6_fast_eligible(const Call &c)
+{
+    return c.fmt == FMT_MX && (c.mx_fmt == MCE_MX_E2M3 || c.mx_fmt == MCE_MX_E3M2) && c.a_cm == 0 &&
+           c.b_cm == 1 && c.K > 0 && c.K % 128 == 0 && c.lda % 64 == 0 && c.ldb % 64 == 0 &&
+           c.ld_sa % 4 == 0 && c.ld_sb % 4 == 0 && ((uintptr_t)c.A % 16) == 0 &&
+           ((uintptr_t)c.B % 16) == 0 && ((uintptr_t)c.SA % 4) == 0 && ((uintptr_t)c.SB % 4) == 0;
+}
+
+// 8-bit MX levels 5-6 with an MN-major operand: K a positive multiple of
+// 128, 16-byte aligned operands with lda, ldb multiples of 16 bytes, 4-byte
+// scale rows.
+bool mx_mn_eligible(const Call &c)
+{
+    return c.fmt == FMT_MX && elem_bits(c) == 8 && (c.a_cm != 0 || c.b_cm == 0) && c.K > 0 &&
+           c.K % 128 == 0 && c.lda % 16 == 0 && c.ldb % 16 == 0 && c.ld_sa % 4 == 0 &&
+           c.ld_sb % 4 == 0 && ((uintptr_t)c.A % 16) == 0 && ((uintptr_t)c.B % 16) == 0 &&
+           ((uintptr_t)c.SA % 4) == 0 && ((uintptr_t)c.SB % 4) == 0;
+}
+
 bool mx_scales_eligible(const Call &c)
 {
     // the pipelined MX kernels read four scale bytes per 32-bit load
@@ -159,7 +180,7 @@ int pick_level(const Call &c)
         return kBestBf16Level;
     if (kBestMxLevel >= 5 && fast_eligible(c) && mx_scales_eligible(c))
         return kBestMxLevel;
-    if (fp4_fast_eligible(c))
+    if (fp4_fast_eligible(c) || fp6_fast_eligible(c) || mx_mn_eligible(c))
         return kBestMxLevel;
     return 3;
 }
@@ -179,7 +200,9 @@ bool level_accepts(const Call &c, int level)
     }
     switch (level) {
     case 3: return true;
-    case 5: case 6: return (fast_eligible(c) && mx_scales_eligible(c)) || fp4_fast_eligible(c);
+    case 5: case 6:
+        return (fast_eligible(c) && mx_scales_eligible(c)) || fp4_fast_eligible(c) ||
+               fp6_fast_eligible(c) || mx_mn_eligible(c);
     case 7: return fast_eligible(c) && mx_scales_eligible(c);   // 8-bit formats
     case 9: return level9_eligible(c);
     default: return false;
@@ -506,7 +529,7 @@ int gemm_mx_pick_level(int elem_format, int64_t M, int64_t N, int64_t K, const v
 int mce_matrix_core_loop(int shape, const void *frags, int64_t n_frag, float *out, int blocks,
                          int iters, void *stream)
 {
-    if (shape < MCE_LOOP_BF16_32X32X16 || shape > MCE_LOOP_MXFP4_32X32X64 || !frags || !out ||
+    if (shape < MCE_LOOP_BF16_32X32X16 || shape > MCE_LOOP_MXFP6_32X32X64 || !frags || !out ||
         n_frag < 1 || n_frag > INT32_MAX || blocks < 1 || blocks > 65535 || iters < 1 ||
         iters > (1 << 24))
         return MCE_EINVAL;

@@ -34,6 +34,7 @@
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "attn_layout.hpp"
 #include "sched.hpp"
 
 namespace mce {

@@ -20,8 +20,9 @@ namespace {
 // Per iteration and wave 2^21 flops for every shape:
 //   32x32x16 bf16: 4 k-steps x 4x4 blocks = 64 instructions of 32768 flops
 //   16x16x32 bf16: 2 k-steps x 8x8 blocks = 128 instructions of 16384 flops
-//   32x32x64 MX E4M3 or E2M1: 1 k-step x 4x4 blocks = 16 instructions of
-//   131072 flops (E2M1 operands: the first four of the eight registers)
+//   32x32x64 MX E4M3, E2M3 or E2M1: 1 k-step x 4x4 blocks = 16
+//   instructions of 131072 flops (E2M3 operands: the first six of the eight
+//   registers, E2M1 the first four)
 // Sixteen operand fragments per lane (eight A, eight B); consecutive
 // instructions take different fragments, as in the GEMM's inner loop.
 template <int SHAPE>
@@ -30,8 +31,11 @@ void matrix_core_loop(const void *__restrict__ frags, int n_frag, float *__restr
 {
     const int gid = blockIdx.x * 256 + threadIdx.x;
     float s = 0.0f;
-    if constexpr (SHAPE == MCE_LOOP_MXFP8_32X32X64 || SHAPE == MCE_LOOP_MXFP4_32X32X64) {
-        constexpr int FMT = SHAPE == MCE_LOOP_MXFP8_32X32X64 ? MX_E4M3 : MX_E2M1;
+    if constexpr (SHAPE == MCE_LOOP_MXFP8_32X32X64 || SHAPE == MCE_LOOP_MXFP4_32X32X64 ||
+                  SHAPE == MCE_LOOP_MXFP6_32X32X64) {
+        constexpr int FMT = SHAPE == MCE_LOOP_MXFP8_32X32X64   ? MX_E4M3
+                            : SHAPE == MCE_LOOP_MXFP6_32X32X64 ? MX_E2M3
+                                                               : MX_E2M1;
         intx8 f[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
@@ -138,6 +142,10 @@ hipError_t launch_matrix_core_loop(int shape, const void *frags, int n_frag, flo
         break;
     case MCE_LOOP_MXFP4_32X32X64:
         hipLaunchKernelGGL((matrix_core_loop<MCE_LOOP_MXFP4_32X32X64>), dim3(blocks), dim3(256), 0, s,
+                           frags, n_frag, out, iters);
+        break;
+    case MCE_LOOP_MXFP6_32X32X64:
+        hipLaunchKernelGGL((matrix_core_loop<MCE_LOOP_MXFP6_32X32X64>), dim3(blocks), dim3(256), 0, s,
                            frags, n_frag, out, iters);
         break;
     default:

@@ -23,10 +23,13 @@ hipError_t launch_fast_fp4(int level, const GemmArgs &p, hipStream_t s)
 
 hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s)
 {
+    if (mx_bits(p.mx_fmt) == 8 && (p.a_cm != 0 || p.b_cm == 0))
+        return launch_fast_mx_mn(level, p, s);
     switch (p.mx_fmt) {
     case MX_E2M1: return launch_fast_fp4(level, p, s);
     case MX_E4M3: return launch_fast_e4m3(level, p, s);
     case MX_E5M2: return launch_fast_e5m2(level, p, s);
+    case MX_E2M3: case MX_E3M2: return launch_fast_fp6(level, p, s);
     default: return hipErrorInvalidValue;
     }
 }

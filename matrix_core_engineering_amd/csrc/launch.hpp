@@ -18,12 +18,16 @@ hipError_t launch_scale_c(const GemmArgs &p, hipStream_t s);
 // Levels 4-7 (bf16): direct global->LDS loads of K-contiguous operands.
 // Returns hipErrorInvalidValue if the level has no kernel.
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s);
-// Levels 5-7 (MX E4M3 and E5M2; p.mx_fmt) and 5-6 (E2M1): direct loads, as
-// for bf16; dispatches to the per-format launchers below.
+// Levels 5-7 (MX E4M3 and E5M2; p.mx_fmt) and 5-6 (E2M1, E2M3, E3M2):
+// direct loads, as for bf16; dispatches to the per-format launchers below.
 hipError_t launch_fast_mx(int level, const GemmArgs &p, hipStream_t s);
 hipError_t launch_fast_e4m3(int level, const GemmArgs &p, hipStream_t s);
 hipError_t launch_fast_e5m2(int level, const GemmArgs &p, hipStream_t s);
 hipError_t launch_fast_fp4(int level, const GemmArgs &p, hipStream_t s);
+hipError_t launch_fast_fp6(int level, const GemmArgs &p, hipStream_t s);
+// 8-bit MX levels 5-6 with an MN-major operand (A column-major or B
+// row-major), through the LDS transpose loads.
+hipError_t launch_fast_mx_mn(int level, const GemmArgs &p, hipStream_t s);
 // Levels 5-6 (bf16) for operands the direct-load kernels cannot take: any
 // layout, alignment and K, through registers.
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);

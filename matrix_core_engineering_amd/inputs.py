@@ -236,6 +236,26 @@ CONFIGS = {
 }
 
 
+# Skinny shapes (one short side): HBM-bound, measured against the HBM roofline.
+SKINNY = {
+    "skinny_1x8192x8192_bf16": dict(M=1, N=8192, K=8192),
+    "skinny_64x8192x8192_bf16": dict(M=64, N=8192, K=8192),
+    "skinny_8192x64x8192_bf16": dict(M=8192, N=64, K=8192),
+    "skinny_256x8192x8192_bf16": dict(M=256, N=8192, K=8192),
+    "skinny_64x8192x8192_mxfp8": dict(M=64, N=8192, K=8192, fmt=E4M3FN, dist="uniform",
+                                      lo=-448.0, hi=448.0),
+}
+
+
+def skinny_problem(name, seed=11):
+    """A skinny workload: A row-major, B column-major (K-contiguous), bf16
+    out, alpha 1, beta 0; bf16 entries N(0, 0.02^2), MX as workload 5."""
+    kw = dict(a_col_major=False, b_col_major=True, c_dtype=OUT_BF16, alpha=1.0, beta=0.0,
+              dist="normal", std=0.02, name=name)
+    kw.update(SKINNY[name])
+    return make_problem(seed=seed, **kw)
+
+
 def config_problem(idx, seed=None):
     """The standard workload idx (1..5), seeded with idx unless given."""
     kw = dict(CONFIGS[idx])

@@ -89,8 +89,9 @@ def test_level_out_of_range():
 
 
 def test_mx_layouts_and_short_scale_ld():
-    """8-bit MX operands may be MN-major (level 3); packed ones may not; a
-    scale row shorter than ceil(K/32) is invalid."""
+    """8-bit MX operands may be MN-major (level 3 when K is not a multiple of
+    128); packed ones may not; a scale row shorter than ceil(K/32) is
+    invalid."""
     def mx(a_cm, b_cm, ld_sa=1, ld_sb=1, K=32):
         return mce.gemm_mxfp8(4, 4, K, FAKE_A, 4 if a_cm else K, a_cm, 0x40000000, ld_sa,
                               FAKE_B, K if b_cm else 4, b_cm, 0x50000000, ld_sb, FAKE_C, 4, 0,
@@ -147,25 +148,34 @@ def test_mx_packed_formats_need_whole_bytes(fmt, unit):
 
 
 def test_mx_pick_level_by_format():
-    """8-bit formats pick the pipelined level when the operands allow it;
-    the packed formats run level 3."""
+    """Every format picks the pipelined level when the operands allow it,
+    else level 3."""
     def pick(fmt, K=8192, lda=8192, ld_s=256, a_cm=0):
         return mce.gemm_mx_pick_level(fmt, 8192, 8192, K, 0x1000, lda, a_cm, 0x20000, ld_s, 0x9000,
                                       lda, 1, 0x30000, ld_s)
-    for fmt in (mce.MCE_MX_E4M3, mce.MCE_MX_E5M2, mce.MCE_MX_E2M1):
+    for fmt in (mce.MCE_MX_E4M3, mce.MCE_MX_E5M2, mce.MCE_MX_E2M1, mce.MCE_MX_E2M3,
+                mce.MCE_MX_E3M2):
         assert pick(fmt) == 6
+    # the 6-bit formats' pipelined level needs K a multiple of 128 and lda,
+    # ldb multiples of 64
     for fmt in (mce.MCE_MX_E2M3, mce.MCE_MX_E3M2):
-        assert pick(fmt) == 3
+        assert pick(fmt, K=8192 - 64, lda=8192) == 3
+        assert pick(fmt, K=4096, lda=8192 - 32) == 3
+        assert pick(fmt, K=4096, lda=8192 - 64) == 6
     # E2M1's pipelined level needs 16-byte scale rows and K a multiple of 512
     assert pick(mce.MCE_MX_E2M1, ld_s=260) == 3
     assert pick(mce.MCE_MX_E2M1, K=8192 - 256, lda=8192, ld_s=256) == 3
-    assert pick(mce.MCE_MX_E5M2, a_cm=1) == 3
+    # MN-major 8-bit operands: the transpose-load kernel when K is a multiple
+    # of 128 and the leading dimensions of 16 bytes, else level 3
+    assert pick(mce.MCE_MX_E5M2, a_cm=1) == 6
+    assert pick(mce.MCE_MX_E4M3, a_cm=1, K=8192 - 64) == 3
+    assert pick(mce.MCE_MX_E4M3, a_cm=1, lda=8192 - 8) == 3
     assert (mce.gemm_mxfp8_pick_level(8192, 8192, 8192, 0x1000, 8192, 0, 0x9000, 8192, 1) ==
             pick(mce.MCE_MX_E4M3))
 
 
 @pytest.mark.parametrize("shape,frags,n_frag,out,blocks,iters", [
-    (4, FAKE_A, 16, FAKE_C, 1, 1),            # unknown shape
+    (5, FAKE_A, 16, FAKE_C, 1, 1),            # unknown shape
     (-1, FAKE_A, 16, FAKE_C, 1, 1),
     (0, 0, 16, FAKE_C, 1, 1),                 # frags NULL
     (0, FAKE_A, 16, 0, 1, 1),                 # out NULL

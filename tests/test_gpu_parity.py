@@ -242,19 +242,23 @@ OTHER_MX = [E5M2, E2M3, E3M2, E2M1]
 OTHER_MX_IDS = ["e5m2", "e2m3", "e3m2", "e2m1"]
 # K a multiple of 4 (whole bytes for the packed formats); ragged M, N, K
 MXF_SHAPES = [(1, 1, 32), (5, 3, 40), (128, 128, 64), (127, 129, 100), (64, 96, 132),
-              (200, 150, 512), (33, 65, 1000)]
+              (200, 150, 512), (33, 65, 1000), (257, 300, 128), (300, 520, 384)]
 
 
 def mx_format_accepts(fmt, level, p):
     """Levels 5-7 of E5M2 need K-contiguous, 16-byte aligned rows (lda, ldb,
     K multiples of 16) and 4-byte scale rows; levels 5-6 of E2M1 need lda,
-    ldb multiples of 32, K a multiple of 512 and 16-byte scale rows; the
-    6-bit formats run level 3 only."""
+    ldb multiples of 32, K a multiple of 512 and 16-byte scale rows; levels
+    5-6 of the 6-bit formats need K a multiple of 128, lda, ldb multiples of
+    64 and 4-byte scale rows."""
     if level in (None, 3):
         return True
     if fmt == E2M1:
         return (level in (5, 6) and p.K % 512 == 0 and p.lda % 32 == 0 and p.ldb % 32 == 0 and
                 p.ld_sa % 16 == 0 and p.ld_sb % 16 == 0)
+    if fmt in (E2M3, E3M2):
+        return (level in (5, 6) and p.K > 0 and p.K % 128 == 0 and p.lda % 64 == 0 and
+                p.ldb % 64 == 0 and p.ld_sa % 4 == 0 and p.ld_sb % 4 == 0)
     if fmt != E5M2:
         return False
     return p.lda % 16 == 0 and p.ldb % 16 == 0 and p.K % 16 == 0 and p.ld_sa % 4 == 0 and p.ld_sb % 4 == 0
@@ -304,12 +308,27 @@ def test_mx_formats_random_within_bound(fmt, shape, level):
             assert_close(p, r[0])
 
 
+@pytest.mark.parametrize("level", [5, 6])
+@pytest.mark.parametrize("fmt", [E2M3, E3M2], ids=["e2m3", "e3m2"])
+def test_fp6_padded_rows_integer_bitwise(fmt, level):
+    """The 6-bit pipelined kernels with row pitches beyond K (lda = K + 64,
+    ldb = K + 128 elements) and scale rows longer than K / 32: only the
+    first K elements and K / 32 scales of each row take part."""
+    M, N, K = 300, 260, 384
+    p = make_problem(M, N, K, fmt=fmt, a_col_major=False, b_col_major=True, c_dtype=OUT_F32,
+                     dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2, lda=K + 64,
+                     ldb=K + 128, ld_sa=K // 32 + 4, ld_sb=K // 32 + 8, seed=8700 + level + fmt)
+    r = run_mx_format(p, level)
+    assert_bitwise(p, r[1])
+
+
 @pytest.mark.parametrize("fmt,level", [(E5M2, 5), (E5M2, 6), (E5M2, 7), (E5M2, None),
-                                       (E2M1, 5), (E2M1, 6), (E2M1, None)],
+                                       (E2M1, 5), (E2M1, 6), (E2M1, None),
+                                       (E2M3, 5), (E2M3, 6), (E3M2, 6), (E3M2, None)],
                          ids=["e5m2-5", "e5m2-6", "e5m2-7", "e5m2-default", "e2m1-5", "e2m1-6",
-                              "e2m1-default"])
+                              "e2m1-default", "e2m3-5", "e2m3-6", "e3m2-6", "e3m2-default"])
 def test_mx_formats_large_groups_integer_exact(fmt, level):
-    """E5M2 and E2M1 through the pipelined kernels at a ragged large shape
+    """E5M2, E2M1 and the 6-bit formats through the pipelined kernels at a ragged large shape
     with whole scale groups (K a multiple of 512, 16-byte scale rows): row
     and column sums exact, sampled entries bitwise."""
     M, N, K = 4100, 8200, 1536
@@ -330,29 +349,94 @@ def test_mx_formats_large_groups_integer_exact(fmt, level):
     assert np.array_equal(vals[ii, jj], cref)
 
 
-@pytest.mark.parametrize("level", [3, 5, None])
+def mx_mn_accepts(level, p):
+    """MN-major 8-bit MX: level 3 always; levels 5-6 when K is a positive
+    multiple of 128, lda and ldb multiples of 16 and the scale rows 4-byte
+    multiples; levels 7 and 9 never."""
+    if level in (3, None):
+        return True
+    if level not in (5, 6):
+        return False
+    return (p.K > 0 and p.K % 128 == 0 and p.lda % 16 == 0 and p.ldb % 16 == 0 and
+            p.ld_sa % 4 == 0 and p.ld_sb % 4 == 0)
+
+
+def pad16(x):
+    return (x + 15) // 16 * 16
+
+
+# (M, N, K, leading dimensions padded to multiples of 16)
+MN_SHAPES = [(5, 3, 40, False), (127, 129, 100, False), (200, 150, 512, False),
+             (33, 65, 1000, False), (200, 150, 512, True), (300, 520, 384, True),
+             (257, 300, 128, True), (64, 48, 256, True)]
+
+
+@pytest.mark.parametrize("level", [3, 5, 6, 7, None])
 @pytest.mark.parametrize("layout", [(True, True), (False, False), (True, False)],
                          ids=["a_col_b_col", "a_row_b_row", "a_col_b_row"])
 @pytest.mark.parametrize("fmt", [E4M3FN, E5M2], ids=["e4m3", "e5m2"])
 def test_mx_mn_major_operands(fmt, layout, level):
     """8-bit MX operands stored MN-major (scales stay one row per M or N
-    index): level 3 runs them, the pipelined levels decline; integer data
-    bitwise, random data within the bound, ragged shapes."""
+    index): level 3 takes them all, levels 5-6 those with whole 128-wide K
+    tiles and 16-byte leading dimensions (the transpose-load kernel), level
+    7 none; integer data bitwise, random data within the bound, ragged
+    shapes and padded leading dimensions."""
     a_cm, b_cm = layout
-    for t, (M, N, K) in enumerate([(5, 3, 40), (127, 129, 100), (200, 150, 512), (33, 65, 1000)]):
+
+    def last_elements_nonzero(p):
+        # the last element of the last row (A) or column (B) at k = K - 1,
+        # where an MN-major tile's final 16-byte chunk ends: code 2.0
+        if a_cm:
+            p.A[p.K - 1, p.M - 1] = 0x40
+        if not b_cm:
+            p.B[p.K - 1, p.N - 1] = 0x40
+
+    for t, (M, N, K, pad) in enumerate(MN_SHAPES):
+        lds = {}
+        if pad:
+            lds = dict(lda=pad16(M if a_cm else K) + 16, ldb=pad16(K if b_cm else N) + 32)
         p = make_problem(M, N, K, fmt=fmt, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_F32,
-                         dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2, seed=9100 + t)
+                         dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2, seed=9100 + t,
+                         **lds)
+        last_elements_nonzero(p)
         r = run_level(p, level)
-        if level == 5:
-            assert r is None, "the pipelined levels take K-contiguous operands only"
+        if not mx_mn_accepts(level, p):
+            assert r is None, f"level {level} ran a problem it documents as unsupported"
             continue
-        assert r is not None
+        assert r is not None, f"level {level} declined a problem it documents"
         assert_bitwise(p, r[1])
         kw = dict(dist="uniform", lo=-448.0, hi=448.0)
         p = make_problem(M, N, K, fmt=fmt, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_BF16,
-                         alpha=0.5, beta=1.5, seed=9200 + t, **kw)
+                         alpha=0.5, beta=1.5, seed=9200 + t, **kw, **lds)
         r = run_level(p, level)
         assert_close(p, r[0])
+
+
+@pytest.mark.parametrize("level", [5, 6])
+@pytest.mark.parametrize("layout", [(True, True), (True, False)], ids=["a_col_b_col", "a_col_b_row"])
+def test_mx_mn_major_large_integer_exact(layout, level):
+    """The transpose-load kernel at a ragged large shape over many tiles
+    (persistent walk at level 6): row and column sums exact, sampled entries
+    bitwise."""
+    a_cm, b_cm = layout
+    M, N, K = 4100, 8200, 1536
+    p = make_problem(M, N, K, fmt=E4M3FN, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_F32,
+                     dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2,
+                     lda=pad16(M if a_cm else K), ldb=pad16(K if b_cm else N), ld_sa=48, ld_sb=48,
+                     seed=9300 + level, name="large_mx_mn_int")
+    r = run_level(p, level)
+    assert r is not None
+    vals = r[0]
+    from helpers import decode_elements, torch_decode_scales
+    A = decode_elements(p, p.A, p.M, p.K, p.a_col_major, p.lda)
+    B = decode_elements(p, p.B, p.K, p.N, p.b_col_major, p.ldb)
+    A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+    B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    assert np.array_equal(vals.sum(axis=1), A @ B.sum(axis=1))
+    assert np.array_equal(vals.sum(axis=0), A.sum(axis=0) @ B)
+    ii, jj = sample_indices(M, N, 1000, 75)
+    cref, _ = oracle_entries(p, ii, jj)
+    assert np.array_equal(vals[ii, jj], cref)
 
 
 @pytest.mark.parametrize("level", MX_LEVELS)
@@ -617,11 +701,12 @@ def test_whole_tiles_bf16_output_persistent_tail(level, fmt, shape, alpha):
 
 
 @pytest.mark.parametrize("shape", [mce.MCE_LOOP_BF16_32X32X16, mce.MCE_LOOP_BF16_16X16X32,
-                                   mce.MCE_LOOP_MXFP8_32X32X64, mce.MCE_LOOP_MXFP4_32X32X64])
+                                   mce.MCE_LOOP_MXFP8_32X32X64, mce.MCE_LOOP_MXFP4_32X32X64,
+                                   mce.MCE_LOOP_MXFP6_32X32X64])
 def test_matrix_core_loop_closed_form(shape):
     """The ceiling loop on all-ones operands: every instruction adds its K
     depth to each accumulator, 64 per iteration for every shape (4 k-steps of
-    16, 2 of 32, 1 of 64; E2M1 1.0 is code 2), and each lane holds 256
+    16, 2 of 32, 1 of 64; E2M1 1.0 is code 2, E2M3 1.0 code 8), and each lane holds 256
     accumulators, so every
     lane writes 256 * 64 * iters exactly."""
     announce(f"matrix_core_loop shape={shape}")
@@ -631,6 +716,9 @@ def test_matrix_core_loop_closed_form(shape):
         one = torch.ones(n_frag * 32).to(torch.float8_e4m3fn).view(torch.uint8)
     elif shape == mce.MCE_LOOP_MXFP4_32X32X64:
         one = torch.full((n_frag * 32,), 0x22, dtype=torch.uint8)   # two E2M1 1.0 codes per byte
+    elif shape == mce.MCE_LOOP_MXFP6_32X32X64:
+        # four E2M3 1.0 codes (0x08) per three bytes: 0x208208 little-endian
+        one = torch.tensor([0x08, 0x82, 0x20] * 8 + [0] * 8, dtype=torch.uint8).repeat(n_frag)
     else:
         one = torch.ones(n_frag * 8, dtype=torch.bfloat16).view(torch.int16)
     frags = one.to(dev)

@@ -16,8 +16,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SCHED = os.path.join(ROOT, "matrix_core_engineering_amd", "csrc", "sched.hpp")
+ATTN = os.path.join(ROOT, "matrix_core_engineering_amd", "csrc", "attn_layout.hpp")
+MNL = os.path.join(ROOT, "matrix_core_engineering_amd", "csrc", "mn_layout.hpp")
 
 SHIM = r'''
+#include "%s"
+#include "%s"
 #include "%s"
 extern "C" {
 int h_xcd_major(int wg, int nwg) { return mce::xcd_major(wg, nwg); }
@@ -32,6 +36,7 @@ int h_swz4(int r) { return mce::swz4(r); }
 int h_swz4q(int r) { return mce::swz4q(r); }
 int h_attn_key_of_col(int j) { return mce::attn_key_of_col(j); }
 int h_swz_attn_k(int r, int d) { return mce::swz_attn_k(r, d); }
+int h_mn_swz(int r) { return mce::mn_swz(r); }
 int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 0; }
 }
 '''
@@ -41,7 +46,7 @@ int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 
 def lib(tmp_path_factory):
     d = tmp_path_factory.mktemp("hostlogic")
     src = d / "shim.cpp"
-    src.write_text(SHIM % SCHED)
+    src.write_text(SHIM % (SCHED, ATTN, MNL))
     so = d / "libshim.so"
     subprocess.run(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", str(src), "-o", str(so)],
                    check=True)
@@ -373,3 +378,62 @@ def test_attn_vt_writes_and_reads(lib, dim):
             addrs = [(32 * b + (l & 31)) * 128 + (((2 * ts + (l >> 5)) ^ lib.h_swz8(32 * b + (l & 31))) * 16)
                      for l in range(64)]
             assert cycles_extra(addrs, 16, "read") == 0
+
+
+# ------------------------------------------------- MN-major 8-bit MX tiles
+
+def tr8_gather(addr_of_lane, lds):
+    """ds_read_b64_tr_b8 as measured: inside each 16-lane group, output lane
+    i byte b is byte i % 8 of the 8 bytes at input lane 2b + i // 8's
+    address."""
+    out = []
+    for lane in range(64):
+        g, i = lane // 16, lane % 16
+        out.append([lds[addr_of_lane[16 * g + 2 * b + i // 8] + i % 8] for b in range(8)])
+    return out
+
+
+def test_mn_direct_loads_fill_each_chunk_once(lib):
+    """Load t of wave w fills k-rows 4 (8w + t) .. +3: lane l k-row + l / 16
+    at physical chunk l % 16, fetching logical chunk physical ^ swz; every
+    (k-row, logical chunk) of the 128 k-rows exactly once."""
+    seen = set()
+    for g in range(32):
+        for l in range(64):
+            kr = 4 * g + l // 16
+            seen.add((kr, (l % 16) ^ lib.h_mn_swz(kr)))
+    assert seen == {(kr, c) for kr in range(128) for c in range(16)}
+
+
+@pytest.mark.parametrize("rb", range(0, 256, 32))
+def test_mn_transpose_reads_give_the_fragment_conflict_free(lib, rb):
+    """The four transpose reads of a fragment of rows rb .. rb + 31 (k-step
+    ks) give lane l row rb + l % 32 at k = 64ks + 16h .. +15 and 64ks + 32 +
+    16h .. +15 (h = l / 32) in register order, and each read is
+    conflict-free under the 8-byte read rule (32 lanes per cycle)."""
+    # a swizzled tile whose byte at (k-row, row) encodes both
+    lds = [0] * (128 * 256)
+    val = {}
+    for kr in range(128):
+        for c in range(16):
+            pc = c ^ lib.h_mn_swz(kr)
+            for e in range(16):
+                lds[kr * 256 + pc * 16 + e] = (kr, c * 16 + e)
+    for ks in range(2):
+        regs = [[None] * 32 for _ in range(64)]
+        for c in range(4):
+            addrs = []
+            for lane in range(64):
+                tl, tg = lane % 16, lane // 16
+                th, ts = tg >> 1, tg & 1
+                kr = 64 * ks + 16 * th + 8 * (c & 1) + 32 * (c >> 1) + (tl >> 1)
+                pchunk = ((rb >> 4) + ts) ^ lib.h_mn_swz(tl >> 1)
+                addrs.append(kr * 256 + (pchunk << 4) + 8 * (tl & 1))
+            assert cycles_extra(addrs, 8, "read") == 0
+            got = tr8_gather(addrs, lds)
+            for lane in range(64):
+                regs[lane][8 * c:8 * c + 8] = got[lane]
+        for lane in range(64):
+            h, r = lane // 32, lane % 32
+            ks_k = [64 * ks + 16 * h + e for e in range(16)] + [64 * ks + 32 + 16 * h + e for e in range(16)]
+            assert regs[lane] == [(k, rb + r) for k in ks_k], lane
