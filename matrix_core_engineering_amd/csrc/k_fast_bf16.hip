@@ -8,6 +8,8 @@ namespace mce {
 // is a whole number of 64-wide K tiles, at least two), else 128x128 tiles on
 // the older ring; level 7 the role-specialised kernel; level 9 the
 // early-release ring with eight consumer waves (whole 64-wide K tiles only).
+// Levels 5 and 6 hand problems with a side of at most 64 to the skinny
+// kernel (k_skinny.hip), whose 32-wide tiles keep every CU streaming.
 hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
 {
     // 256x256 tiles when they give every CU work, 128x128 otherwise; the
@@ -18,10 +20,14 @@ hipError_t launch_fast_bf16(int level, const GemmArgs &p, hipStream_t s)
     case 4:
         return big ? launch<Bf16Op, 256, 256, 1, false>(p, s) : launch<Bf16Op, 128, 128, 1, false>(p, s);
     case 5:
+        if (skinny_eligible(p))
+            return launch_skinny_bf16(p, s);
         if (big && ring_ok)
             return launch_early_bf16<Bf16Ring64, Bf16Ring64S16, false>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, false>(p, s) : launch<Bf16Op, 128, 128, 3, false>(p, s);
     case 6:
+        if (skinny_eligible(p))
+            return launch_skinny_bf16(p, s);
         if (big && ring_ok)
             return launch_early_bf16<Bf16Ring64, Bf16Ring64S16, true>(p, s);
         return big ? launch<Bf16Op, 256, 256, 2, true>(p, s) : launch<Bf16Op, 128, 128, 3, true>(p, s);

@@ -28,6 +28,11 @@ hipError_t launch_fast_fp6(int level, const GemmArgs &p, hipStream_t s);
 // 8-bit MX levels 5-6 with an MN-major operand (A column-major or B
 // row-major), through the LDS transpose loads.
 hipError_t launch_fast_mx_mn(int level, const GemmArgs &p, hipStream_t s);
+// bf16 levels 5-6 when M or N is at most 64 (K-contiguous operands, K a
+// multiple of 64 and at least 512): 32-wide tiles along the long side, the
+// eight waves of a workgroup splitting K.
+bool skinny_eligible(const GemmArgs &p);
+hipError_t launch_skinny_bf16(const GemmArgs &p, hipStream_t s);
 // Levels 5-6 (bf16) for operands the direct-load kernels cannot take: any
 // layout, alignment and K, through registers.
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);

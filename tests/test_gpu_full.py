@@ -86,6 +86,31 @@ def test_skinny_shapes_every_element(shape, fmt):
     check_every_element(p, vals)
 
 
+# (M, N, K): the split-K skinny kernel's tile shapes (short side 1-32, 33-64),
+# ragged long sides, the shortest K it takes (512, one chunk per wave), an
+# uneven chunk split, and a K below its range (the ordinary kernels)
+SKINNY_SPLIT = [(64, 8192, 8192), (8192, 64, 8192), (33, 4100, 1024), (4100, 47, 1088),
+                (64, 300, 512), (17, 33, 576), (64, 64, 448)]
+
+
+@pytest.mark.parametrize("level", [5, 6, None])
+@pytest.mark.parametrize("shape", SKINNY_SPLIT, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_split_k_every_element(shape, level):
+    """Short side at most 64: four waves split K and reduce through LDS.
+    Integer data bitwise (fp32 out); real data with alpha/beta and bf16 out
+    within the bound; every element."""
+    M, N, K = shape
+    q = integer_problem(M, N, K, c_dtype=OUT_F32, seed=M + 3 * N + K, name=f"skinny_int_{M}x{N}x{K}")
+    announce(f"skinny split-K {q.name} level={level}")
+    _, raw = run(q, level)
+    cref, _ = oracle_full(q)
+    assert np.array_equal(raw, expected_bits(q, cref))
+    p = make_problem(M, N, K, a_col_major=False, b_col_major=True, c_dtype=OUT_BF16, alpha=0.75,
+                     beta=-1.25, dist="normal", seed=M + 5 * N + K, name=f"skinny_{M}x{N}x{K}")
+    vals, _ = run(p, level)
+    check_every_element(p, vals)
+
+
 @pytest.mark.parametrize("shape", [(1, 8192, 8192), (8192, 1, 8192), (257, 300, 1000)])
 @pytest.mark.parametrize("layout", [(False, True), (False, False), (True, True)])
 @pytest.mark.parametrize("offs", [(2, 0), (0, 2), (2, 6)])
