@@ -61,7 +61,8 @@ KERNEL_SOURCES = ["matrix_core_engineering_amd/csrc/kernels_fast.hpp",
                   "matrix_core_engineering_amd/csrc/k_fast_bf16.hip",
                   "matrix_core_engineering_amd/csrc/common.hpp",
                   "matrix_core_engineering_amd/csrc/sched.hpp",
-                  "matrix_core_engineering_amd/csrc/epilogue.hpp"]
+                  "matrix_core_engineering_amd/csrc/epilogue.hpp",
+                  "matrix_core_engineering_amd/csrc/ring_plan.hpp"]
 
 
 def kernel_source_hash():
@@ -395,9 +396,10 @@ def levels(args, dev, stream):
                       "per_config": res}), flush=True)
 
 
-def read_traffic():
+def read_traffic(level):
     """HBM bytes per launch of the bf16 kernel from the committed counter
-    summary, or None if it is missing or was taken on other kernel code."""
+    summary, or None if it is missing, was taken on other kernel code or on
+    another level's kernel."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -406,6 +408,8 @@ def read_traffic():
                     k, v = line.split("=", 1)
                     kv[k.strip()] = v.strip()
         if kv.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        if int(kv.get("kernel_level", -1)) != level:
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -784,7 +788,7 @@ def main():
     value = bf16.p.flops / (ms_per_step * 1e-3) / 1e12
     tf_mx = mx.p.flops / (float(np.mean(t_mx)) * 1e-3) / 1e12
     attention = attention_timings(dev, stream, args.warmup, args.steps)
-    traffic = read_traffic()
+    traffic = read_traffic(bf16.level())
     # the default bf16 kernel for whole 256x256 bf16 tiles runs 16x16x32
     loop_bf16 = ceiling["bf16_16x16x32"]["tflops"]
     loop_mx = ceiling["mxfp8_32x32x64"]["tflops"]

@@ -84,9 +84,10 @@ enum {
 
 /*
  * bf16 GEMM.  A: bf16 bits (uint16), B: bf16 bits, fp32 accumulate.
- * Picks the fastest level that accepts the problem: level 9 when the
- * problem has at least two 256x256 tiles but no more than the device has
- * compute units and level 9 accepts it, else level 6.
+ * Picks the fastest level that accepts the problem: level 9 when level 9
+ * accepts it, M and N exceed 256, and either the problem has no more
+ * 256x256 tiles than the device has compute units or C is whole 256x256
+ * bf16 tiles with beta == 0 and 16-byte aligned rows; else level 6.
  * ("B200 GEMM Optimization Ladder", section E steps 1-8.)
  */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
@@ -257,7 +258,9 @@ int gemm_mx_order(int level, int xcd_order, int group_m, int elem_format,
                   void *C, int64_t ldc, int c_col_major, int c_dtype,
                   float alpha, float beta, void *stream);
 
-/* Level gemm_bf16 / gemm_mxfp8 would run for this problem (0 if none). */
+/* Level gemm_bf16 / gemm_mxfp8 would run for this problem (0 if none);
+   gemm_bf16_pick_level answers for a row-major bf16 C with ldc == N,
+   beta == 0 and a 16-byte aligned base. */
 int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda, int a_col_major,
                          const void *B, int64_t ldb, int b_col_major);

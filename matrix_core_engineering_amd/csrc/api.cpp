@@ -169,12 +169,18 @@ constexpr int kBestMxLevel = 6;
 
 int pick_level(const Call &c)
 {
-    // bf16 with no more 256x256 tiles than compute units (one tile each):
-    // level 9's two waves per SIMD hide the ring's prologue and epilogue
-    // that one tile per workgroup leaves exposed (1-3% faster than level 6
-    // at 4096^3; level 6 is as fast or faster with several tiles per CU)
-    if (c.fmt == FMT_BF16 && level9_eligible(c) && c.ncu > 0 &&
-        ((c.M + 255) / 256) * ((c.N + 255) / 256) <= c.ncu && c.M > 256 && c.N > 256)
+    // bf16, level 9 (eight waves, two per SIMD, on one staged ring) when
+    // it accepts the problem and either the problem has no more 256x256
+    // tiles than compute units (the second wave per SIMD hides the ring's
+    // prologue and epilogue that one tile per workgroup leaves exposed: 4-6%
+    // faster than level 6 at 4096^3) or C is whole 256x256 bf16 tiles with
+    // beta = 0 and 16-byte aligned rows (the 16x16x32 kernel with the staged
+    // epilogue: 1.2-1.4% faster than level 6 at 8192^3 in interleaved
+    // same-run rounds); level 6 otherwise
+    const bool whole16 = c.c_dtype == MCE_OUT_BF16 && c.beta == 0.0f && c.M % 256 == 0 &&
+                         c.N % 256 == 0 && c.ldc % 8 == 0 && ((uintptr_t)c.C % 16) == 0;
+    if (c.fmt == FMT_BF16 && level9_eligible(c) && c.ncu > 0 && c.M > 256 && c.N > 256 &&
+        (whole16 || ((c.M + 255) / 256) * ((c.N + 255) / 256) <= c.ncu))
         return 9;
     if (c.fmt == FMT_BF16)   // levels 5-6 take any bf16 problem
         return kBestBf16Level;
@@ -445,8 +451,10 @@ int gemm_mxfp8_level(int level, int64_t M, int64_t N, int64_t K, const void *A, 
 int gemm_bf16_pick_level(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                          int a_col_major, const void *B, int64_t ldb, int b_col_major)
 {
+    // as for a row-major bf16 C with ldc = N, beta = 0 and a 16-byte
+    // aligned base (the C pointer itself is not needed to pick)
     Call c = make_call(0, FMT_BF16, 0, M, N, K, A, lda, a_col_major, nullptr, 0, B, ldb, b_col_major,
-                       nullptr, 0, nullptr, 1, 0, MCE_OUT_F32, 1.0f, 0.0f, nullptr);
+                       nullptr, 0, nullptr, N > 0 ? N : 1, 0, MCE_OUT_BF16, 1.0f, 0.0f, nullptr);
     if (M < 0 || N < 0 || K < 0)
         return 0;
     c.ncu = gfx950_cus();
