@@ -90,10 +90,6 @@ void attention_fwd(AttnArgs a)
     const size_t kv_base = (size_t)bh * a.seq_k * D;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(a.Q + qo_base, (uint32_t)((size_t)a.seq_q * D * 2));
-    const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc(a.K + kv_base, (uint32_t)((size_t)a.seq_k * D * 2));
-    const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc(a.V + kv_base, (uint32_t)((size_t)a.seq_k * D * 2));
 
     // keys this tile of query rows may see
     const int kv_end_vis = CAUSAL ? q0 + ABM - 1 + a.seq_k - a.seq_q + 1 : a.seq_k;
@@ -113,16 +109,26 @@ void attention_fwd(AttnArgs a)
 
     // K tile loads: this wave's KLOADS direct loads of 1 KiB; lane l writes
     // row (wave*KLOADS + t) * RPL + l / CHK at physical chunk l % CHK and so
-    // fetches logical chunk (l % CHK) ^ swz_attn_k(row)
+    // fetches logical chunk (l % CHK) ^ swz_attn_k(row).  Each tile gets a
+    // buffer resource based at its first key whose record count ends at
+    // seq_k (keys past it read as zeros), so a lane's offsets are constants.
     constexpr int RPL = 1024 / G::ROWK;
-    auto issue_k = [&](int tile, int buf) {
+    uint32_t kvoff[G::KLOADS];
+#pragma unroll
+    for (int t = 0; t < G::KLOADS; ++t) {
+        const int r = (wave * G::KLOADS + t) * RPL + lane / G::CHK;
+        kvoff[t] = (uint32_t)((r * D + ((lane % G::CHK) ^ swz_attn_k(r, D)) * 8) * 2);
+    }
+    auto tile_rsrc = [&](const uint16_t *base, int tile) {
         const int key0 = tile * ABN;
+        const int left = a.seq_k - key0;
+        return make_rsrc(base + kv_base + (size_t)key0 * D, left > 0 ? (uint32_t)left * D * 2 : 0u);
+    };
+    auto issue_k = [&](int tile, int buf) {
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.K, tile);
 #pragma unroll
         for (int t = 0; t < G::KLOADS; ++t) {
-            const int r = (wave * G::KLOADS + t) * RPL + lane / G::CHK;
-            const int lc = (lane % G::CHK) ^ swz_attn_k(r, D);
-            const int key = key0 + r;
-            const uint32_t voff = key < a.seq_k ? (uint32_t)((key * D + lc * 8) * 2) : OOB_OFFSET;
+            const uint32_t voff = kvoff[t];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rk, (lds_ptr_t)(kbuf + buf * G::K_BYTES + (wave * G::KLOADS + t) * 1024), 16, voff, 0, 0,
                 0);
@@ -133,33 +139,34 @@ void attention_fwd(AttnArgs a)
     intx4 vst[G::VPASS][2];
     const int kp = l32;
     auto load_v = [&](int tile) {
-        const int key = tile * ABN + 2 * kp;
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.V, tile);
 #pragma unroll
         for (int ps = 0; ps < G::VPASS; ++ps) {
             const int c = 2 * wave + h + 8 * ps;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const uint32_t off =
-                    key + e < a.seq_k ? (uint32_t)(((key + e) * D + c * 8) * 2) : OOB_OFFSET;
+                const uint32_t off = (uint32_t)(((2 * kp + e) * D + c * 8) * 2);
                 vst[ps][e] = __builtin_bit_cast(intx4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
             }
         }
     };
-    // V^T write: word (V[2kp][d], V[2kp+1][d]) at row d, keys 2kp .. 2kp+1;
-    // 32 consecutive lanes (kp = 0..31) write one row's 32 words, all banks
+    // V^T write: word (V[2kp][d], V[2kp+1][d]) at row d, keys 2kp .. 2kp+1,
+    // i.e. byte d*128 + ((kp >> 2) ^ swz8(d))*16 + (kp & 3)*4.  With d = 8c + e
+    // and c = 2*wave + h + 8*pass, swz8(d) = e ^ h, so the address is a lane
+    // constant plus 8192*pass + 128e + (((kp >> 2) ^ h ^ e) << 4).  32
+    // consecutive lanes (kp = 0..31) write one row's 32 words, all banks.
+    const int vt_lane = (2 * wave + h) * 1024 + (kp & 3) * 4;
+    const int vt_x = (kp >> 2) ^ h;
     auto write_vt = [&](int buf) {
-        char *vb = vbuf + buf * G::VT_BYTES;
+        char *vb = vbuf + buf * G::VT_BYTES + vt_lane;
 #pragma unroll
         for (int ps = 0; ps < G::VPASS; ++ps) {
-            const int c = 2 * wave + h + 8 * ps;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int d = 8 * c + e;
                 const uint32_t lo = (uint32_t)vst[ps][0][e >> 1], hi = (uint32_t)vst[ps][1][e >> 1];
-                const uint32_t word = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
-                                              : ((lo & 0xFFFFu) | (hi << 16));
-                const int pchunk = (kp >> 2) ^ swz8(d);
-                *(uint32_t *)(vb + d * 128 + pchunk * 16 + (kp & 3) * 4) = word;
+                // bytes (lo 0, lo 1, hi 0, hi 1) for even e, (lo 2, lo 3, hi 2, hi 3) for odd e
+                const uint32_t word = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
+                *(uint32_t *)(vb + ps * 8192 + e * 128 + ((vt_x ^ e) << 4)) = word;
             }
         }
     };

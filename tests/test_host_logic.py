@@ -373,6 +373,17 @@ def test_attn_vt_writes_and_reads(lib, dim):
                     written.add(a)
                 assert cycles_extra(addrs, 4, "write") == 0
     assert written == set(range(0, dim * 128, 4))
+    # the kernel's split of that address: a lane constant plus a term in
+    # (pass, e) with swz8(8 (2w + h + 8 pass) + e) = e ^ h
+    for w in range(4):
+        for ps in range(dim // 64):
+            for e in range(8):
+                for l in range(64):
+                    h, kp = l >> 5, l & 31
+                    d = 8 * (2 * w + h + 8 * ps) + e
+                    full = d * 128 + ((kp >> 2) ^ lib.h_swz8(d)) * 16 + (kp & 3) * 4
+                    lane_c = (2 * w + h) * 1024 + (kp & 3) * 4
+                    assert full == lane_c + ps * 8192 + e * 128 + ((((kp >> 2) ^ h) ^ e) << 4)
     for b in range(dim // 32):
         for ts in range(4):
             addrs = [(32 * b + (l & 31)) * 128 + (((2 * ts + (l >> 5)) ^ lib.h_swz8(32 * b + (l & 31))) * 16)
