@@ -209,17 +209,26 @@ void attention_fwd(AttnArgs a)
             issue_k(j + 1, buf ^ 1);
             load_v(j + 1);
         }
-        // ---- S = Q K^T (two 32-key blocks)
+        // ---- S = Q K^T (two 32-key blocks): the two blocks' accumulators
+        // alternate (independent chains), and each k-step's K fragments are
+        // read one k-step ahead of their products
         const char *kb = kbuf + buf * G::K_BYTES;
         floatx16 sacc[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            sacc[blk] = zero16();
-            const char *krp = kb + (32 * blk + krow) * G::ROWK;
+        sacc[0] = zero16();
+        sacc[1] = zero16();
+        {
+            const char *krp0 = kb + krow * G::ROWK, *krp1 = kb + (32 + krow) * G::ROWK;
+            bf16x8 kf[2][2];
+            kf[0][0] = *(const bf16x8 *)(krp0 + (h ^ kswz) * 16);
+            kf[0][1] = *(const bf16x8 *)(krp1 + (h ^ kswz) * 16);
 #pragma unroll
             for (int s = 0; s < G::KS; ++s) {
-                const bf16x8 kf = *(const bf16x8 *)(krp + ((2 * s + h) ^ kswz) * 16);
-                sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[blk], 0, 0, 0);
+                if (s + 1 < G::KS) {
+                    kf[(s + 1) & 1][0] = *(const bf16x8 *)(krp0 + ((2 * (s + 1) + h) ^ kswz) * 16);
+                    kf[(s + 1) & 1][1] = *(const bf16x8 *)(krp1 + ((2 * (s + 1) + h) ^ kswz) * 16);
+                }
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][0], qf[s], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][1], qf[s], sacc[1], 0, 0, 0);
             }
         }
         // ---- online softmax.  Tiles that every row of this wave sees
@@ -279,15 +288,26 @@ void attention_fwd(AttnArgs a)
                 }
             }
         l_run += psum;
-        // ---- O += P V (four k-steps of 16 keys)
-        const char *vb = vbuf + buf * G::VT_BYTES;
+        // ---- O += P V (four k-steps of 16 keys): the DB blocks of O
+        // alternate within each k-step (independent chains), and each
+        // k-step's V fragments are read one k-step ahead
+        {
+            const char *vb = vbuf + buf * G::VT_BYTES + l32 * 128;
+            bf16x8 vf[2][G::DB];
 #pragma unroll
-        for (int b = 0; b < G::DB; ++b) {
-            const char *vrp = vb + (32 * b + l32) * 128;
+            for (int b = 0; b < G::DB; ++b)
+                vf[0][b] = *(const bf16x8 *)(vb + b * 32 * 128 + (h ^ vswz) * 16);
 #pragma unroll
             for (int ts = 0; ts < 4; ++ts) {
-                const bf16x8 vf = *(const bf16x8 *)(vrp + ((2 * ts + h) ^ vswz) * 16);
-                o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ts >> 1][ts & 1], o_acc[b], 0, 0, 0);
+                if (ts + 1 < 4) {
+#pragma unroll
+                    for (int b = 0; b < G::DB; ++b)
+                        vf[(ts + 1) & 1][b] = *(const bf16x8 *)(vb + b * 32 * 128 + ((2 * (ts + 1) + h) ^ vswz) * 16);
+                }
+#pragma unroll
+                for (int b = 0; b < G::DB; ++b)
+                    o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ts & 1][b], pf[ts >> 1][ts & 1], o_acc[b],
+                                                                       0, 0, 0);
             }
         }
         // ---- the next tile's V^T (its buffer was last read before the
