@@ -79,7 +79,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["bf16", "mxfp8", "copy", "loop", "cfg1", "cfg2", "cfg3",
-                                       "attn-causal", "attn-full", "skinny64", "skinny1"]
+                                       "attn-causal", "attn-full", "skinny64", "skinny1", "skinny64mx",
+                                       "skinny1mx"]
                     + list(MX_FORMAT_NAMES),
                     default=None)
     ap.add_argument("--levels", action="store_true",
@@ -754,7 +755,9 @@ def main():
     if args.only:
         work = Workload({"bf16": 4, "mxfp8": 5, "cfg1": 1, "cfg2": 2, "cfg3": 3,
                          "skinny64": "skinny_64x8192x8192_bf16",
-                         "skinny1": "skinny_1x8192x8192_bf16"}[args.only], dev)
+                         "skinny1": "skinny_1x8192x8192_bf16",
+                         "skinny64mx": "skinny_64x8192x8192_mxfp8",
+                         "skinny1mx": "skinny_1x8192x8192_mxfp8"}[args.only], dev)
         for _ in range(args.reps + 1):
             if args.order is not None:
                 xcd, gm = (int(v) for v in args.order.split(","))

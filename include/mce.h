@@ -168,6 +168,12 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  * multiple of 64 and above 64; MX (8-bit elements) K a multiple of 512 with
  * 16-byte aligned scale rows (A, B, SA, SB 16-byte aligned, ld_sa and ld_sb
  * multiples of 16).  Other problems return MCE_EUNSUPPORTED at level 9.
+ * At levels 5 and 6 a problem with M or N at most 64 and K-contiguous,
+ * 16-byte aligned operands runs a kernel whose workgroups hold the whole
+ * short side and split K (bf16: K a multiple of 64, at least 512; E4M3 and
+ * E5M2: K a multiple of 128, at least 1024, scale rows 4-byte aligned); the
+ * long operand is then read from memory once ("B200 GEMM Optimization
+ * Ladder", section B: skinny shapes are bound by bandwidth).
  */
 int gemm_bf16_level(int level, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, int a_col_major,

@@ -1379,10 +1379,14 @@ hipError_t launch_fast_mx8(int level, const GemmArgs &p, hipStream_t s)
                         (uintptr_t)p.SA % 16 == 0 && (uintptr_t)p.SB % 16 == 0;
     switch (level) {
     case 5:
+        if (skinny_mx_eligible(p))
+            return launch_skinny_mx(p, s);
         if (ring_ok && groups)
             return launch_early<Ring128G, 256, 256, false>(p, s);
         return ring_ok ? launch_early<Ring128, 256, 256, false>(p, s) : launch<Op, 256, 256, 2, false>(p, s);
     case 6:
+        if (skinny_mx_eligible(p))
+            return launch_skinny_mx(p, s);
         if (ring_ok && groups)
             return launch_early<Ring128G, 256, 256, true>(p, s);
         return ring_ok ? launch_early<Ring128, 256, 256, true>(p, s) : launch<Op, 256, 256, 2, true>(p, s);

@@ -33,6 +33,9 @@ hipError_t launch_fast_mx_mn(int level, const GemmArgs &p, hipStream_t s);
 // eight waves of a workgroup splitting K.
 bool skinny_eligible(const GemmArgs &p);
 hipError_t launch_skinny_bf16(const GemmArgs &p, hipStream_t s);
+// 8-bit MX (E4M3 / E5M2) operands, K-contiguous, with a short side
+bool skinny_mx_eligible(const GemmArgs &p);
+hipError_t launch_skinny_mx(const GemmArgs &p, hipStream_t s);
 // Levels 5-6 (bf16) for operands the direct-load kernels cannot take: any
 // layout, alignment and K, through registers.
 hipError_t launch_general_bf16(int level, const GemmArgs &p, hipStream_t s);

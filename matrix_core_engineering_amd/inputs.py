@@ -244,6 +244,8 @@ SKINNY = {
     "skinny_256x8192x8192_bf16": dict(M=256, N=8192, K=8192),
     "skinny_64x8192x8192_mxfp8": dict(M=64, N=8192, K=8192, fmt=E4M3FN, dist="uniform",
                                       lo=-448.0, hi=448.0),
+    "skinny_1x8192x8192_mxfp8": dict(M=1, N=8192, K=8192, fmt=E4M3FN, dist="uniform",
+                                     lo=-448.0, hi=448.0),
 }
 
 

@@ -15,7 +15,7 @@ import pytest
 
 import matrix_core_engineering_amd as mce
 import oracle
-from matrix_core_engineering_amd.inputs import (BF16, E4M3FN, OUT_BF16, OUT_F32, config_problem,
+from matrix_core_engineering_amd.inputs import (BF16, E4M3FN, E5M2, OUT_BF16, OUT_F32, config_problem,
                                                 integer_problem, make_problem)
 from helpers import oracle_full
 from gpu_util import DeviceProblem, expected_bits
@@ -107,6 +107,38 @@ def test_skinny_split_k_every_element(shape, level):
     assert np.array_equal(raw, expected_bits(q, cref))
     p = make_problem(M, N, K, a_col_major=False, b_col_major=True, c_dtype=OUT_BF16, alpha=0.75,
                      beta=-1.25, dist="normal", seed=M + 5 * N + K, name=f"skinny_{M}x{N}x{K}")
+    vals, _ = run(p, level)
+    check_every_element(p, vals)
+
+
+# 8-bit MX with a short side: the same two kernels with E4M3 / E5M2 operands,
+# 128-wide K chunks and one scale word per row and chunk.  Shapes: both
+# tile kernels (short side 1-32 and 33-64, M or N short), ragged long sides,
+# the shortest K they take (1024: one chunk per wave of the register
+# kernel), uneven chunk splits (1152 = 9 chunks, 1280 = 10), and a K below
+# the range (896: the ordinary MX kernels).
+SKINNY_MX = [(64, 8192, 8192), (8192, 64, 4096), (1, 4100, 2048), (33, 4100, 1024), (4100, 47, 1152),
+             (17, 33, 1024), (64, 64, 1280), (32, 300, 896)]
+
+
+@pytest.mark.parametrize("level", [5, None])
+@pytest.mark.parametrize("fmt", [E4M3FN, E5M2], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", SKINNY_MX, ids=lambda s: "x".join(map(str, s)))
+def test_skinny_mx_every_element(shape, fmt, level):
+    """MX with a short side at most 64: integer data (scale exponents 0..2)
+    bitwise with fp32 out; U[-448, 448] data with alpha/beta and bf16 out
+    within the bound; every element."""
+    M, N, K = shape
+    q = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_F32, scale_exp_lo=0, scale_exp_hi=2,
+                        seed=M + 3 * N + K + fmt, name=f"skinny_mx_int_{M}x{N}x{K}")
+    announce(f"skinny MX {q.name} fmt={fmt} level={level}")
+    _, raw = run(q, level)
+    cref, _ = oracle_full(q)
+    want = expected_bits(q, cref)
+    assert np.array_equal(raw, want), f"{np.count_nonzero(raw != want)} entries differ"
+    p = make_problem(M, N, K, fmt=fmt, a_col_major=False, b_col_major=True, c_dtype=OUT_BF16,
+                     alpha=0.75, beta=-1.25, dist="uniform", lo=-448.0, hi=448.0,
+                     seed=M + 5 * N + K + fmt, name=f"skinny_mx_{M}x{N}x{K}")
     vals, _ = run(p, level)
     check_every_element(p, vals)
 
