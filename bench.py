@@ -25,10 +25,13 @@ L instead of the default one; copy: a 1 GiB
 device-to-device copy, the calibration of the HBM byte counters; the MX
 element-format names: the 8192^3 MX GEMM in that format; cfg1-cfg3: the
 single-tile, 4096^3 and ragged workloads; skinny64 / skinny1: the 64 x 8192
-x 8192 and 1 x 8192 x 8192 bf16 GEMMs).  --only loop prints the
-matrix-core loop rates alone.  --configs prints one JSON line timing every
-standard workload and the skinny shapes against their own rooflines; --levels one line timing every
-level of the ladder on every standard workload.
+x 8192 and 1 x 8192 x 8192 bf16 GEMMs; skinny64mx / skinny1mx: the same in
+MX E4M3).  --only loop prints the matrix-core loop rates alone.  --configs
+prints one JSON line timing every standard workload and the skinny shapes
+against their own rooflines; --levels one line timing every level of the
+ladder on every standard workload.  Both run each case back to back for a
+quarter of a second before its W warm-up and K timed launches, so that it
+is timed at sustained clocks rather than on the way up from idle.
 --mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
 element format at its default level, with W warm-up and K timed launches.
 --tile-orders prints one JSON line timing the 8192^3 bf16 and MX GEMMs
@@ -307,6 +310,20 @@ def algorithmic_bytes(p):
     return p.M * p.K * elt + p.K * p.N * elt + scales + c_bytes * (2 if p.beta != 0 else 1)
 
 
+def prewarm(run, seconds=0.25):
+    """Runs `run` back to back for about `seconds` of wall time.  From idle
+    (input generation on the host leaves the GPU idle for a second or more)
+    the GPU takes tens of milliseconds of work to reach its sustained
+    clocks; a 4096^3 GEMM measured 118 us after 20 warm-up launches (2 ms)
+    and 102-106 us after 300 (30 ms) on the same boxes."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            run()
+        torch.cuda.synchronize()
+
+
 def configs(args, dev, stream):
     """One JSON line: every standard workload and the skinny shapes through
     the default entry point, each against the roofline that bounds it
@@ -328,6 +345,7 @@ def configs(args, dev, stream):
         skinny = min(p.M, p.N) <= 256 and max(p.M, p.N) >= 4096
         latency = not skinny and ((p.M + 127) // 128) * ((p.N + 127) // 128) < 256
         hbm_bound = not latency and p.flops / nbytes < peak * 1e12 / (PEAK_HBM * 1e9)
+        prewarm(lambda: w.run(stream))
         for _ in range(args.warmup):
             w.run(stream)
         torch.cuda.synchronize()
@@ -376,6 +394,7 @@ def levels(args, dev, stream):
             if w.run_level(level, stream) != mce.MCE_OK:
                 row[str(level)] = None
                 continue
+            prewarm(lambda: w.run_level(level, stream))
             for _ in range(args.warmup):
                 w.run_level(level, stream)
             evs = []

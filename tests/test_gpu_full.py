@@ -111,6 +111,29 @@ def test_skinny_split_k_every_element(shape, level):
     check_every_element(p, vals)
 
 
+# Short side 65-256 (fewer 128x128 tiles than CUs): 128x64 or 64x128 tiles
+# across the short side, ragged edges, whole and partial K tiles.
+MEDIUM = [(256, 8192, 1024), (8192, 200, 768), (100, 4100, 640), (300, 3000, 520), (65, 1000, 72)]
+
+
+@pytest.mark.parametrize("level", [5, None])
+@pytest.mark.parametrize("shape", MEDIUM, ids=lambda s: "x".join(map(str, s)))
+def test_medium_short_side_every_element(shape, level):
+    """Integer data bitwise (fp32 out); real data with alpha/beta and bf16
+    out within the bound; every element."""
+    M, N, K = shape
+    q = integer_problem(M, N, K, c_dtype=OUT_F32, seed=M + 7 * N + K, name=f"medium_int_{M}x{N}x{K}")
+    announce(f"medium {q.name} level={level}")
+    _, raw = run(q, level)
+    cref, _ = oracle_full(q)
+    want = expected_bits(q, cref)
+    assert np.array_equal(raw, want), f"{np.count_nonzero(raw != want)} entries differ"
+    p = make_problem(M, N, K, a_col_major=False, b_col_major=True, c_dtype=OUT_BF16, alpha=0.75,
+                     beta=-1.25, dist="normal", seed=M + 9 * N + K, name=f"medium_{M}x{N}x{K}")
+    vals, _ = run(p, level)
+    check_every_element(p, vals)
+
+
 # 8-bit MX with a short side: the same two kernels with E4M3 / E5M2 operands,
 # 128-wide K chunks and one scale word per row and chunk.  Shapes: both
 # tile kernels (short side 1-32 and 33-64, M or N short), ragged long sides,
