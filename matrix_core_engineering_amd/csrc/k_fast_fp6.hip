@@ -24,9 +24,15 @@
 // two-way is the floor.
 //
 // Scales: one aligned 4-byte word per row and K tile (its four 32-element
-// blocks), staged per stage by 4-byte direct loads, read at a 4-byte pitch
-// (conflict-free); the upper half-wave takes the word shifted one byte down
-// so op_sel 2 ks selects block 2 ks + h.
+// blocks); the upper half-wave takes the word shifted one byte down so
+// op_sel 2 ks selects block 2 ks + h.  With K a multiple of 512 and 16-byte
+// aligned scale rows they arrive in groups: the 16 bytes of each row for
+// four K tiles, one 16-byte direct load per lane and 64 rows, double-buffered
+// beside the three stages (a 4-byte load per lane and row for every K tile
+// spends as many cache-line requests on 256 bytes as a 1 KiB operand load;
+// measured, those loads alone took a fifth of the kernel's time).
+// Otherwise each stage carries its K tile's words, staged by 4-byte direct
+// loads and read at a 4-byte pitch (conflict-free).
 //
 // Pipeline: three stages, one barrier per K tile, placed between the K
 // tile's two k-steps (see the main loop): fragment reads overlap matrix-core
@@ -48,25 +54,38 @@ constexpr int FP6_BK = 128;                    // K elements per K tile
 constexpr int FP6_ROWB = FP6_BK * 6 / 8;       // 96 bytes per LDS operand row
 constexpr int FP6_S = 3;                       // stages
 constexpr int FP6_A_BYTES = FP6_BM * FP6_ROWB, FP6_B_BYTES = FP6_BN * FP6_ROWB;
-constexpr int FP6_STAGE = FP6_A_BYTES + FP6_B_BYTES + (FP6_BM + FP6_BN) * 4;
 constexpr int FP6_NL = FP6_A_BYTES / 1024 / 4;   // 6 operand loads per wave, operand and K tile
-constexpr int FP6_LOADS = 2 * FP6_NL + 2;        // + one scale-word load per operand
 static_assert(FP6_A_BYTES % 4096 == 0, "whole 1 KiB loads per wave");
-static_assert(FP6_S * FP6_STAGE <= 160 * 1024, "LDS budget");
-static_assert(2 * FP6_LOADS < 64, "vmcnt range");
+
+// Stage layout: operands, then (without scale groups) the K tile's scale
+// words; with scale groups two group buffers of 16 bytes per row follow the
+// stages.
+template <bool SG>
+struct Fp6Ring {
+    static constexpr int STAGE = FP6_A_BYTES + FP6_B_BYTES + (SG ? 0 : (FP6_BM + FP6_BN) * 4);
+    static constexpr int GROUP = (FP6_BM + FP6_BN) * 16;
+    static constexpr int LDS = FP6_S * STAGE + (SG ? 2 * GROUP : 0);
+    static constexpr int LOADS = 2 * FP6_NL + (SG ? 0 : 2);   // loads per wave and K tile
+    static constexpr int GLOADS = SG ? 2 : 0;                 // loads per wave and scale group
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(2 * LOADS + 2 * GLOADS < 64, "vmcnt range");
+};
 
 typedef int intx2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int fp6_swz(int row) { return (row >> 3) & 1; }
 
-template <int FMT, bool PERSIST, int EPI>
+template <int FMT, bool SG, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp6(GemmArgs p, int group_m)
 {
     using G = Fp6Geom;
+    using R = Fp6Ring<SG>;
     constexpr int BM = FP6_BM, BN = FP6_BN, ROWB = FP6_ROWB, NL = FP6_NL;
     constexpr int TI = G::TI, TJ = G::TJ;
-    __shared__ __attribute__((aligned(1024))) char smem[FP6_S * FP6_STAGE];
+    constexpr int FP6_STAGE = R::STAGE, FP6_LOADS = R::LOADS;
+    __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+    char *const groups = smem + FP6_S * FP6_STAGE;   // scale groups: 2 x R::GROUP
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -150,13 +169,31 @@ void gemm_fp6(GemmArgs p, int group_m)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_ptr_t)(base + FP6_A_BYTES + (wave * NL + u) * 1024), 16, voff, soff, 0, 0);
         }
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.sa, live ? t.nsa : 0u),
-                                     rsb = make_rsrc(t.sb, live ? t.nsb : 0u);
-        char *sbase = base + FP6_A_BYTES + FP6_B_BYTES;
-        const uint32_t voa = vs_a, vob = vs_b;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sbase + wave * 256), 4, voa, kt * 4, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sbase + BM * 4 + wave * 256), 4, vob, kt * 4,
-                                                 0, 0);
+        if constexpr (!SG) {
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.sa, live ? t.nsa : 0u),
+                                         rsb = make_rsrc(t.sb, live ? t.nsb : 0u);
+            char *sbase = base + FP6_A_BYTES + FP6_B_BYTES;
+            const uint32_t voa = vs_a, vob = vs_b;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sbase + wave * 256), 4, voa, kt * 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sbase + BM * 4 + wave * 256), 4, vob,
+                                                     kt * 4, 0, 0);
+        }
+    };
+    // Scale group gi (K tiles 4 gi .. 4 gi + 3) of tile span t into group
+    // buffer gi % 2: lane l brings the 16 bytes of row 64 wave + l.  Past the
+    // last group the record counts are zero (zeros land in a buffer nothing
+    // reads again).
+    auto issue_group = [&](const Span &t, int gi) {
+        if constexpr (SG) {
+            char *gb = groups + (gi & 1) * R::GROUP;
+            const bool live = 4 * gi < nk;
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.sa, live ? t.nsa : 0u),
+                                         rsb = make_rsrc(t.sb, live ? t.nsb : 0u);
+            const uint32_t voa = vs_a, vob = vs_b;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(gb + wave * 1024), 16, voa, gi * 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(gb + BM * 16 + wave * 1024), 16, vob,
+                                                     gi * 16, 0, 0);
+        }
     };
 
     // fragment of k-step ks from the row at `rowp`: bytes 48 ks + 24 h ..
@@ -184,14 +221,18 @@ void gemm_fp6(GemmArgs p, int group_m)
         for (int j = 0; j < TJ; ++j)
             fb[j] = frag(base + FP6_A_BYTES + (wn * G::WN + j * 32 + l32) * ROWB, ks);
     };
-    auto read_sc = [&](int stage, int (&sa)[TI], int (&sb)[TJ]) {
-        const uint32_t *sw = (const uint32_t *)(smem + stage * FP6_STAGE + FP6_A_BYTES + FP6_B_BYTES);
+    // the scale words of K tile kt (in `stage`, or word kt % 4 of the rows'
+    // 16 bytes in group buffer (kt / 4) % 2)
+    auto read_sc = [&](int stage, int kt, int (&sa)[TI], int (&sb)[TJ]) {
+        constexpr int PITCH = SG ? 4 : 1;          // words per row
+        const uint32_t *sw = SG ? (const uint32_t *)(groups + ((kt >> 2) & 1) * R::GROUP) + (kt & 3)
+                                : (const uint32_t *)(smem + stage * FP6_STAGE + FP6_A_BYTES + FP6_B_BYTES);
 #pragma unroll
         for (int i = 0; i < TI; ++i)
-            sa[i] = (int)(sw[wm * G::WM + i * 32 + l32] >> (8 * h));
+            sa[i] = (int)(sw[(wm * G::WM + i * 32 + l32) * PITCH] >> (8 * h));
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-            sb[j] = (int)(sw[BM + wn * G::WN + j * 32 + l32] >> (8 * h));
+            sb[j] = (int)(sw[(BM + wn * G::WN + j * 32 + l32) * PITCH] >> (8 * h));
     };
     // k-step ks of the K tile; B first, so lane l holds row l % 32 of each
     // C block and columns 8q + 4h .. +3 (the layout the epilogue stores)
@@ -208,18 +249,68 @@ void gemm_fp6(GemmArgs p, int group_m)
     // Per K tile kt (stage s = kt % 3): k-step 1's fragments are read while
     // k-step 0 runs; then the wait for tile kt + 1's loads and the barrier,
     // after which no wave reads stage s (its reads are done) and tile kt + 3
-    // goes into it; then tile kt + 1's k-step 0 fragments are read while
-    // k-step 1 of tile kt runs.  Three K tiles of loads are in flight ahead
-    // of the one consumed.
+    // goes into it (and, with scale groups, at the first K tile of group gi
+    // group gi + 1 into the other group buffer, whose last reads, of K tile
+    // 4 gi - 1, came before the previous barrier); then tile kt + 1's k-step
+    // 0 fragments are read while k-step 1 of tile kt runs.  Three K tiles of
+    // loads are in flight ahead of the one consumed.  The scheduling groups
+    // interleave the fragment reads and loads with the matrix-core
+    // instructions.
     intx8 f0a[TI], f0b[TJ], f1a[TI], f1b[TJ];
     int sa_c[TI], sb_c[TJ], sa_n[TI], sb_n[TJ];
+    // loads issued after tile kt + 1's (the wait before K tile kt's
+    // barrier): tile kt + 2's, and a group after tile kt + 3's (at kt - 1)
+    // or tile kt + 2's (at kt - 2) when either of those K tiles began one
+    auto k_tile = [&](const Span &t, const int kt, int &stage, auto q_c) {
+        constexpr int Q = decltype(q_c)::value;    // kt % 4 (scale groups), else 0
+        read_ks(stage, 1, f1a, f1b);
+        mma(std::integral_constant<int, 0>{}, f0a, f0b, sa_c, sb_c);
+#pragma unroll
+        for (int u = 0; u < 12; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // an LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // a matrix-core instruction
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        // (matrix-core instructions touch no memory, so the barrier alone
+        // would not keep them on their side of it)
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int AFTER = FP6_LOADS + ((SG && (Q == 1 || Q == 2)) ? R::GLOADS : 0);
+        wait_vmcnt<AFTER>();
+        wait_lgkm0();
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t, kt + 3, stage);
+        if constexpr (SG && Q == 0)
+            issue_group(t, kt / 4 + 1);
+        const int nstage = stage == 2 ? 0 : stage + 1;
+        read_ks(nstage, 0, f0a, f0b);        // past the last K tile: unused
+        read_sc(nstage, kt + 1, sa_n, sb_n);
+        mma(std::integral_constant<int, 1>{}, f1a, f1b, sa_c, sb_c);
+#pragma unroll
+        for (int u = 0; u < 14; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // a direct load
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+            sa_c[i] = sa_n[i];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+            sb_c[j] = sb_n[j];
+        stage = nstage;
+    };
+
     Span cur = span(0);
     for (int r = 0; r < my_tiles; ++r) {
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
-        // every wave is done reading the previous tile's stages
+        // every wave is done reading the previous tile's stages and groups
         if (r > 0)
             barrier();
+        issue_group(cur, 0);
         issue(cur, 0, 0);
         issue(cur, 1, 1);
         issue(cur, 2, 2);
@@ -231,32 +322,19 @@ void gemm_fp6(GemmArgs p, int group_m)
         wait_vmcnt<2 * FP6_LOADS>();
         barrier();
         read_ks(0, 0, f0a, f0b);
-        read_sc(0, sa_c, sb_c);
+        read_sc(0, 0, sa_c, sb_c);
         int stage = 0;
-        for (int kt = 0; kt < nk; ++kt) {
-            read_ks(stage, 1, f1a, f1b);
-            mma(std::integral_constant<int, 0>{}, f0a, f0b, sa_c, sb_c);
-            // (matrix-core instructions touch no memory, so the barrier alone
-            // would not keep them on their side of it)
-            __builtin_amdgcn_sched_barrier(0);
-            // this wave's loads of tile kt + 1 have landed (tile kt + 2's
-            // may still be in flight; loads complete in issue order)
-            wait_vmcnt<FP6_LOADS>();
-            wait_lgkm0();
-            barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            issue(cur, kt + 3, stage);
-            const int nstage = stage == 2 ? 0 : stage + 1;
-            read_ks(nstage, 0, f0a, f0b);        // past the last K tile: unused
-            read_sc(nstage, sa_n, sb_n);
-            mma(std::integral_constant<int, 1>{}, f1a, f1b, sa_c, sb_c);
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-                sa_c[i] = sa_n[i];
-#pragma unroll
-            for (int j = 0; j < TJ; ++j)
-                sb_c[j] = sb_n[j];
-            stage = nstage;
+        if constexpr (SG) {
+            // nk is a multiple of 4
+            for (int kt = 0; kt < nk; kt += 4) {
+                k_tile(cur, kt, stage, std::integral_constant<int, 0>{});
+                k_tile(cur, kt + 1, stage, std::integral_constant<int, 1>{});
+                k_tile(cur, kt + 2, stage, std::integral_constant<int, 2>{});
+                k_tile(cur, kt + 3, stage, std::integral_constant<int, 3>{});
+            }
+        } else {
+            for (int kt = 0; kt < nk; ++kt)
+                k_tile(cur, kt, stage, std::integral_constant<int, 0>{});
         }
         store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         cur = span(r + 1);
@@ -264,20 +342,32 @@ void gemm_fp6(GemmArgs p, int group_m)
     wait_vmcnt<0>();
 }
 
-template <int FMT, bool PERSIST>
+template <int FMT, bool SG, bool PERSIST>
 hipError_t launch_fp6(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + FP6_BM - 1) / FP6_BM, tiles_n = (p.N + FP6_BN - 1) / FP6_BN;
     const int ntiles = tiles_m * tiles_n;
     const int group_m = group_rows(tiles_m, p.group_m);
     if (PERSIST && ntiles <= p.ncu)
-        return launch_fp6<FMT, false>(p, s);
+        return launch_fp6<FMT, SG, false>(p, s);
     const int grid = PERSIST ? (ntiles < p.ncu ? ntiles : p.ncu) : ntiles;
     if (whole_bf16(p, FP6_BM, FP6_BN))
-        hipLaunchKernelGGL((gemm_fp6<FMT, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0, s, p, group_m);
+        hipLaunchKernelGGL((gemm_fp6<FMT, SG, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0, s, p, group_m);
     else
-        hipLaunchKernelGGL((gemm_fp6<FMT, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p, group_m);
+        hipLaunchKernelGGL((gemm_fp6<FMT, SG, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p, group_m);
     return hipGetLastError();
+}
+
+// scale groups when K is a multiple of 512 and the scale rows are 16-byte
+// aligned
+template <int FMT>
+hipError_t launch_fp6_fmt(bool persist, const GemmArgs &p, hipStream_t s)
+{
+    const bool sg = p.K % 512 == 0 && p.ld_sa % 16 == 0 && p.ld_sb % 16 == 0 && (uintptr_t)p.SA % 16 == 0 &&
+                    (uintptr_t)p.SB % 16 == 0;
+    if (sg)
+        return persist ? launch_fp6<FMT, true, true>(p, s) : launch_fp6<FMT, true, false>(p, s);
+    return persist ? launch_fp6<FMT, false, true>(p, s) : launch_fp6<FMT, false, false>(p, s);
 }
 
 } // namespace
@@ -295,9 +385,9 @@ hipError_t launch_fast_fp6(int level, const GemmArgs &p, hipStream_t s)
         return hipErrorInvalidValue;
     const bool persist = level == 6;
     if (p.mx_fmt == MX_E2M3)
-        return persist ? launch_fp6<MX_E2M3, true>(p, s) : launch_fp6<MX_E2M3, false>(p, s);
+        return launch_fp6_fmt<MX_E2M3>(persist, p, s);
     if (p.mx_fmt == MX_E3M2)
-        return persist ? launch_fp6<MX_E3M2, true>(p, s) : launch_fp6<MX_E3M2, false>(p, s);
+        return launch_fp6_fmt<MX_E3M2>(persist, p, s);
     return hipErrorInvalidValue;
 }
 

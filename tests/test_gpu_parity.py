@@ -310,14 +310,19 @@ def test_mx_formats_random_within_bound(fmt, shape, level):
 
 @pytest.mark.parametrize("level", [5, 6])
 @pytest.mark.parametrize("fmt", [E2M3, E3M2], ids=["e2m3", "e3m2"])
-def test_fp6_padded_rows_integer_bitwise(fmt, level):
+@pytest.mark.parametrize("k,pad_a,pad_b", [(384, 4, 8), (1024, 16, 32), (1024, 4, 8)],
+                         ids=["per-tile-scales", "scale-groups", "groups-misaligned"])
+def test_fp6_padded_rows_integer_bitwise(fmt, level, k, pad_a, pad_b):
     """The 6-bit pipelined kernels with row pitches beyond K (lda = K + 64,
     ldb = K + 128 elements) and scale rows longer than K / 32: only the
-    first K elements and K / 32 scales of each row take part."""
-    M, N, K = 300, 260, 384
+    first K elements and K / 32 scales of each row take part.  K = 1024 with
+    16-byte scale rows takes the scale groups; with 4-byte ones the per-K-tile
+    scale words."""
+    M, N, K = 300, 260, k
     p = make_problem(M, N, K, fmt=fmt, a_col_major=False, b_col_major=True, c_dtype=OUT_F32,
                      dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2, lda=K + 64,
-                     ldb=K + 128, ld_sa=K // 32 + 4, ld_sb=K // 32 + 8, seed=8700 + level + fmt)
+                     ldb=K + 128, ld_sa=K // 32 + pad_a, ld_sb=K // 32 + pad_b,
+                     seed=8700 + level + fmt + k + pad_a)
     r = run_mx_format(p, level)
     assert_bitwise(p, r[1])
 
