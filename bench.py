@@ -29,7 +29,8 @@ x 8192 and 1 x 8192 x 8192 bf16 GEMMs; skinny64mx / skinny1mx: the same in
 MX E4M3).  --only loop prints the matrix-core loop rates alone.  --configs
 prints one JSON line timing every standard workload and the skinny shapes
 against their own rooflines; --levels one line timing every level of the
-ladder on every standard workload.  Both run each case back to back for a
+ladder on every standard workload.  These modes (and --mx-formats,
+--tile-orders and the attention timings) run each case back to back for a
 quarter of a second before its W warm-up and K timed launches, so that it
 is timed at sustained clocks rather than on the way up from idle.
 --mx-formats prints one JSON line instead: the 8192^3 MX GEMM in every
@@ -235,6 +236,7 @@ def mx_formats(args, dev, stream):
     cases += [(f"{n}_a_col_b_row", n, True, False) for n in ("e4m3", "e5m2")]
     for key, name, a_cm, b_cm in cases:
         w = MxFormatWorkload(name, dev, a_cm, b_cm)
+        prewarm(lambda: w.run(stream))
         for _ in range(args.warmup):
             w.run(stream)
         torch.cuda.synchronize()
@@ -504,6 +506,7 @@ def attention_timings(dev, stream, warmup, steps, cpu_seconds=None):
     out = {}
     for name in ("causal", "full"):
         work = AttentionWorkload(name, dev)
+        prewarm(lambda: work.run(stream))
         t, _ = timed_steps(work, warmup, steps, stream)
         ms = float(np.mean(t))
         tf = work.flops / (ms * 1e-3) / 1e12
@@ -688,6 +691,7 @@ def tile_orders(args, dev, stream):
             assert st == mce.MCE_OK, mce.gemm_status_string(st)
 
         times = {o: [] for o in orders}
+        prewarm(lambda: run(1, 8))
         for _ in range(args.warmup):
             run(1, 8)
         for rnd in range(5):
