@@ -26,4 +26,18 @@ MCE_HD int swz_attn_k(int row, int dim)
     return dim == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
+// XOR swizzle of the attention V tile's 16-byte chunks (key rows of 2 * dim
+// bytes, stored as in memory).  A P V operand fragment is two transposing
+// reads (ds_read_b64_tr_b16); each 16-lane group of one reads four
+// consecutive key rows k .. k + 3 (k a multiple of 4) at 32 consecutive
+// bytes of d, and the two groups of a half-wave the next 32 bytes.  With
+// 256-byte rows (one bank row each) the four rows' 64-byte windows go to
+// four different windows (chunk XOR 4 (r & 3)); with 128-byte rows (two per
+// bank row) to distinct 32-byte pairs within each (chunk XOR 2 (r & 3)):
+// conflict-free either way.
+MCE_HD int swz_attn_v(int row, int dim)
+{
+    return dim == 128 ? 4 * (row & 3) : 2 * (row & 3);
+}
+
 } // namespace mce

@@ -24,13 +24,14 @@
 // product: P goes from the S accumulators to that product with no exchange
 // between lanes.
 //
-// Data movement per key tile: the K tile (64 rows of D bf16) by direct loads
-// (buffer_load ... lds, bounds-checked: keys past seq_k read as zero) into a
-// double-buffered, XOR-swizzled LDS tile; the V tile through registers,
-// written transposed (V^T: D rows of 64 keys, key pairs as 4-byte words) so
-// that a P V operand fragment (eight consecutive keys of one d) is one
-// 16-byte LDS read.  One barrier per key tile: the loads of tile j+1 are in
-// flight while tile j is consumed.
+// Data movement per key tile: the K and V tiles (64 rows of D bf16 each) by
+// direct loads (buffer_load ... lds, bounds-checked: keys past seq_k read as
+// zero) into double-buffered, XOR-swizzled LDS tiles stored as in memory.  A
+// P V operand fragment (eight consecutive keys of one d) is two transposing
+// LDS reads (ds_read_b64_tr_b16: each lane addresses 4 d of one key row and
+// receives one d of four key rows), so V needs no pass through registers.
+// One barrier per key tile: the loads of tile j+1 are in flight while tile
+// j is consumed.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -41,6 +42,8 @@ namespace mce {
 namespace {
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 *lds_v4i16_t;
 
 constexpr int ABM = 128;   // query rows per workgroup
 constexpr int ABN = 64;    // keys per key tile
@@ -50,12 +53,11 @@ struct AttnGeom {
     static constexpr int ROWK = D * 2;                 // bytes per K row in LDS
     static constexpr int CHK = ROWK / 16;              // 16-byte chunks per K row
     static constexpr int K_BYTES = ABN * ROWK;         // one K tile
-    static constexpr int VT_BYTES = D * ABN * 2;       // one V^T tile: D rows of 128 bytes
-    static constexpr int LDS = 2 * (K_BYTES + VT_BYTES);
+    static constexpr int V_BYTES = K_BYTES;            // one V tile, the same layout
+    static constexpr int LDS = 2 * (K_BYTES + V_BYTES);
     static constexpr int KS = D / 16;                  // k-steps of S
     static constexpr int DB = D / 32;                  // 32-column blocks of O
-    static constexpr int KLOADS = K_BYTES / 1024 / 4;  // K direct loads per wave and tile
-    static constexpr int VPASS = D / 64;               // V staging passes per tile
+    static constexpr int KLOADS = K_BYTES / 1024 / 4;  // K (and V) direct loads per wave and tile
     static_assert(D == 64 || D == 128, "head dimension 64 or 128");
 };
 
@@ -70,7 +72,7 @@ void attention_fwd(AttnArgs a)
     using G = AttnGeom<D>;
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS];
     char *kbuf = smem;                          // [2][K_BYTES]
-    char *vbuf = smem + 2 * G::K_BYTES;         // [2][VT_BYTES]
+    char *vbuf = smem + 2 * G::K_BYTES;         // [2][V_BYTES]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -113,11 +115,12 @@ void attention_fwd(AttnArgs a)
     // buffer resource based at its first key whose record count ends at
     // seq_k (keys past it read as zeros), so a lane's offsets are constants.
     constexpr int RPL = 1024 / G::ROWK;
-    uint32_t kvoff[G::KLOADS];
+    uint32_t kvoff[G::KLOADS], vvoff[G::KLOADS];
 #pragma unroll
     for (int t = 0; t < G::KLOADS; ++t) {
         const int r = (wave * G::KLOADS + t) * RPL + lane / G::CHK;
         kvoff[t] = (uint32_t)((r * D + ((lane % G::CHK) ^ swz_attn_k(r, D)) * 8) * 2);
+        vvoff[t] = (uint32_t)((r * D + ((lane % G::CHK) ^ swz_attn_v(r, D)) * 8) * 2);
     }
     auto tile_rsrc = [&](const uint16_t *base, int tile) {
         const int key0 = tile * ABN;
@@ -134,41 +137,39 @@ void attention_fwd(AttnArgs a)
                 0);
         }
     };
-    // V tile staging: lane (wave, l) takes key pair kp = l % 32 and, per pass,
-    // the d-chunk c = 2*wave + l/32 + 8*pass of both keys
-    intx4 vst[G::VPASS][2];
-    const int kp = l32;
-    auto load_v = [&](int tile) {
+    // The V tile likewise (its own swizzle)
+    auto issue_v = [&](int tile, int buf) {
         const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.V, tile);
 #pragma unroll
-        for (int ps = 0; ps < G::VPASS; ++ps) {
-            const int c = 2 * wave + h + 8 * ps;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const uint32_t off = (uint32_t)(((2 * kp + e) * D + c * 8) * 2);
-                vst[ps][e] = __builtin_bit_cast(intx4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-            }
+        for (int t = 0; t < G::KLOADS; ++t) {
+            const uint32_t voff = vvoff[t];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (lds_ptr_t)(vbuf + buf * G::V_BYTES + (wave * G::KLOADS + t) * 1024), 16, voff, 0, 0,
+                0);
         }
     };
-    // V^T write: word (V[2kp][d], V[2kp+1][d]) at row d, keys 2kp .. 2kp+1,
-    // i.e. byte d*128 + ((kp >> 2) ^ swz8(d))*16 + (kp & 3)*4.  With d = 8c + e
-    // and c = 2*wave + h + 8*pass, swz8(d) = e ^ h, so the address is a lane
-    // constant plus 8192*pass + 128e + (((kp >> 2) ^ h ^ e) << 4).  32
-    // consecutive lanes (kp = 0..31) write one row's 32 words, all banks.
-    const int vt_lane = (2 * wave + h) * 1024 + (kp & 3) * 4;
-    const int vt_x = (kp >> 2) ^ h;
-    auto write_vt = [&](int buf) {
-        char *vb = vbuf + buf * G::VT_BYTES + vt_lane;
+    // P V operand of block b (d = 32b + l % 32), keys 8h .. 8h + 7 of k-step
+    // ts, from two transposing reads q = 0, 1: in 16-lane group g = (l % 32)
+    // / 16, lane L = l % 16 addresses key row 16 ts + 8h + 4q + L / 4 at
+    // d = 32b + 16g + 4 (L % 4) (8 bytes), and receives d = 32b + 16g + L of
+    // the four key rows 16 ts + 8h + 4q .. +3.  The key rows' swizzle
+    // depends only on L / 4 (the rest is a multiple of 4), so each block's
+    // address is a lane constant plus (16 ts + 4q) rows.
+    int vaddr[G::DB];
+    {
+        const int L = lane & 15, g = l32 >> 4;
+        const int r = 8 * h + (L >> 2);
 #pragma unroll
-        for (int ps = 0; ps < G::VPASS; ++ps) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (uint32_t)vst[ps][0][e >> 1], hi = (uint32_t)vst[ps][1][e >> 1];
-                // bytes (lo 0, lo 1, hi 0, hi 1) for even e, (lo 2, lo 3, hi 2, hi 3) for odd e
-                const uint32_t word = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
-                *(uint32_t *)(vb + ps * 8192 + e * 128 + ((vt_x ^ e) << 4)) = word;
-            }
+        for (int b = 0; b < G::DB; ++b) {
+            const int d = 32 * b + 16 * g + 4 * (L & 3);
+            vaddr[b] = r * G::ROWK + (((2 * d) >> 4) ^ swz_attn_v(r, D)) * 16 + ((2 * d) & 15);
         }
+    }
+    auto read_vf = [&](int buf, int b, int ts) -> bf16x8 {
+        const char *p0 = vbuf + buf * G::V_BYTES + vaddr[b] + 16 * ts * G::ROWK;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)p0);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(p0 + 4 * G::ROWK));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     floatx16 o_acc[G::DB];
@@ -192,14 +193,11 @@ void attention_fwd(AttnArgs a)
     // K row read by this lane for the S products, and its swizzle
     const int krow = attn_key_of_col(l32);
     const int kswz = swz_attn_k(krow, D);   // rows 32b + krow share it (b adds no low bits)
-    const int vswz = swz8(l32);        // V^T rows 32db + l32
 
     if (ntiles > 0) {
         issue_k(0, 0);
-        load_v(0);
+        issue_v(0, 0);
         wait_vm0();
-        write_vt(0);
-        wait_lgkm_0();
         sync_wg();
     }
     for (int j = 0; j < ntiles; ++j) {
@@ -207,7 +205,7 @@ void attention_fwd(AttnArgs a)
         const bool more = j + 1 < ntiles;
         if (more) {
             issue_k(j + 1, buf ^ 1);
-            load_v(j + 1);
+            issue_v(j + 1, buf ^ 1);
         }
         // ---- S = Q K^T (two 32-key blocks): the two blocks' accumulators
         // alternate (independent chains), and each k-step's K fragments are
@@ -292,17 +290,16 @@ void attention_fwd(AttnArgs a)
         // alternate within each k-step (independent chains), and each
         // k-step's V fragments are read one k-step ahead
         {
-            const char *vb = vbuf + buf * G::VT_BYTES + l32 * 128;
             bf16x8 vf[2][G::DB];
 #pragma unroll
             for (int b = 0; b < G::DB; ++b)
-                vf[0][b] = *(const bf16x8 *)(vb + b * 32 * 128 + (h ^ vswz) * 16);
+                vf[0][b] = read_vf(buf, b, 0);
 #pragma unroll
             for (int ts = 0; ts < 4; ++ts) {
                 if (ts + 1 < 4) {
 #pragma unroll
                     for (int b = 0; b < G::DB; ++b)
-                        vf[(ts + 1) & 1][b] = *(const bf16x8 *)(vb + b * 32 * 128 + ((2 * (ts + 1) + h) ^ vswz) * 16);
+                        vf[(ts + 1) & 1][b] = read_vf(buf, b, ts + 1);
                 }
 #pragma unroll
                 for (int b = 0; b < G::DB; ++b)
@@ -310,13 +307,9 @@ void attention_fwd(AttnArgs a)
                                                                        0, 0, 0);
             }
         }
-        // ---- the next tile's V^T (its buffer was last read before the
-        // previous barrier), then the barrier: every wave's reads of this
-        // tile are done and the next tile's K and V^T are in LDS
-        if (more) {
-            wait_vm0();
-            write_vt(buf ^ 1);
-        }
+        // ---- the barrier: every wave's reads of this tile are done and
+        // the next tile's K and V are in LDS
+        wait_vm0();
         wait_lgkm_0();
         sync_wg();
     }

@@ -36,6 +36,7 @@ int h_swz4(int r) { return mce::swz4(r); }
 int h_swz4q(int r) { return mce::swz4q(r); }
 int h_attn_key_of_col(int j) { return mce::attn_key_of_col(j); }
 int h_swz_attn_k(int r, int d) { return mce::swz_attn_k(r, d); }
+int h_swz_attn_v(int r, int d) { return mce::swz_attn_v(r, d); }
 int h_mn_swz(int r) { return mce::mn_swz(r); }
 int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 0; }
 }
@@ -352,43 +353,59 @@ def test_attn_k_direct_loads_fill_each_row_once(lib, dim):
         assert lib.h_swz_attn_k(r + 32, dim) == lib.h_swz_attn_k(r, dim)
 
 
+def tr16_gather(addr_of_lane, lds16):
+    """ds_read_b64_tr_b16 as measured: inside each 16-lane group, output lane
+    i element e is 16-bit word i % 4 of the 8 bytes at input lane
+    4e + i // 4's address (lds16: byte address -> 16-bit value)."""
+    out = []
+    for lane in range(64):
+        g, i = lane // 16, lane % 16
+        out.append([lds16[addr_of_lane[16 * g + 4 * e + i // 4] + 2 * (i % 4)] for e in range(4)])
+    return out
+
+
 @pytest.mark.parametrize("dim", [64, 128])
-def test_attn_vt_writes_and_reads(lib, dim):
-    """V^T tile: row d holds 64 keys as 32 key-pair words, pair kp at
-    ((kp >> 2) ^ swz8(d)) * 16 + (kp & 3) * 4.  Each write instruction
-    (wave w, pass, element e; lanes h * 32 + kp write row
-    8 (2w + h + 8 pass) + e) is conflict-free under the 4-byte write rule,
-    every word of the tile is written once, and the P V operand reads (rows
-    32 b + l % 32, logical chunk 2 ts + l / 32) are conflict-free."""
-    written = set()
-    for w in range(4):
-        for ps in range(dim // 64):
-            for e in range(8):
-                addrs = []
-                for l in range(64):
-                    h, kp = l >> 5, l & 31
-                    d = 8 * (2 * w + h + 8 * ps) + e
-                    a = d * 128 + ((kp >> 2) ^ lib.h_swz8(d)) * 16 + (kp & 3) * 4
-                    addrs.append(a)
-                    written.add(a)
-                assert cycles_extra(addrs, 4, "write") == 0
-    assert written == set(range(0, dim * 128, 4))
-    # the kernel's split of that address: a lane constant plus a term in
-    # (pass, e) with swz8(8 (2w + h + 8 pass) + e) = e ^ h
-    for w in range(4):
-        for ps in range(dim // 64):
-            for e in range(8):
-                for l in range(64):
-                    h, kp = l >> 5, l & 31
-                    d = 8 * (2 * w + h + 8 * ps) + e
-                    full = d * 128 + ((kp >> 2) ^ lib.h_swz8(d)) * 16 + (kp & 3) * 4
-                    lane_c = (2 * w + h) * 1024 + (kp & 3) * 4
-                    assert full == lane_c + ps * 8192 + e * 128 + ((((kp >> 2) ^ h) ^ e) << 4)
+def test_attn_v_loads_and_transpose_reads(lib, dim):
+    """V tile stored as in memory (64 key rows of 2 dim bytes), chunk c of key
+    row r at c ^ swz_attn_v(r): the direct loads fill every (row, chunk)
+    once; the two transposing reads of each P V operand fragment (block b,
+    k-step ts) give lane l d = 32 b + l % 32 at keys 16 ts + 8 h .. +7 in
+    register order, each read conflict-free under the 8-byte read rule; and
+    the kernel's address split (a lane constant per block plus 16 ts + 4 q
+    rows) is the same address."""
+    rowb, chunks, rpl = 2 * dim, 2 * dim // 16, 1024 // (2 * dim)
+    seen = set()
+    for ld in range(64 // rpl):
+        for l in range(64):
+            r = ld * rpl + l // chunks
+            seen.add((r, (l % chunks) ^ lib.h_swz_attn_v(r, dim)))
+    assert seen == {(r, c) for r in range(64) for c in range(chunks)}
+    lds16 = {}
+    for r in range(64):
+        for c in range(chunks):
+            pc = c ^ lib.h_swz_attn_v(r, dim)
+            for w in range(8):
+                lds16[r * rowb + pc * 16 + 2 * w] = (r, c * 8 + w)
     for b in range(dim // 32):
         for ts in range(4):
-            addrs = [(32 * b + (l & 31)) * 128 + (((2 * ts + (l >> 5)) ^ lib.h_swz8(32 * b + (l & 31))) * 16)
-                     for l in range(64)]
-            assert cycles_extra(addrs, 16, "read") == 0
+            regs = [[None] * 8 for _ in range(64)]
+            for q in range(2):
+                addrs = []
+                for l in range(64):
+                    g, L, h = (l % 32) // 16, l % 16, l // 32
+                    r = 16 * ts + 8 * h + 4 * q + L // 4
+                    d = 32 * b + 16 * g + 4 * (L % 4)
+                    a = r * rowb + (((2 * d) >> 4) ^ lib.h_swz_attn_v(r, dim)) * 16 + ((2 * d) & 15)
+                    r0 = 8 * h + (L >> 2)
+                    lane_c = r0 * rowb + (((2 * d) >> 4) ^ lib.h_swz_attn_v(r0, dim)) * 16 + ((2 * d) & 15)
+                    assert a == lane_c + (16 * ts + 4 * q) * rowb
+                    addrs.append(a)
+                assert cycles_extra(addrs, 8, "read") == 0
+                for l, v in enumerate(tr16_gather(addrs, lds16)):
+                    regs[l][4 * q:4 * q + 4] = v
+            for l in range(64):
+                h = l // 32
+                assert regs[l] == [(16 * ts + 8 * h + k, 32 * b + l % 32) for k in range(8)], (b, ts, l)
 
 
 # ------------------------------------------------- MN-major 8-bit MX tiles
