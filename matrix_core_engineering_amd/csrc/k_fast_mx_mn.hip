@@ -47,22 +47,35 @@ constexpr int MN_BM = 256, MN_BN = 256;
 constexpr int MN_BK = 128;                          // K elements (bytes) per K tile
 constexpr int MN_OP_BYTES = 256 * MN_BK;            // one operand's K tile: 32 KiB either way
 constexpr int MN_S = 2;
-constexpr int MN_STAGE = 2 * MN_OP_BYTES + (MN_BM + MN_BN) * 4;
 constexpr int MN_NL = MN_OP_BYTES / 1024 / 4;       // 8 direct loads per wave, operand and K tile
-constexpr int MN_LOADS = 2 * MN_NL + 2;             // + one scale-word load per operand
-static_assert(MN_S * MN_STAGE <= 160 * 1024, "LDS budget");
-static_assert(2 * MN_LOADS < 64, "vmcnt range");
+
+// Stage layout: the two operands' K tiles, then (without scale groups) the
+// K tile's scale words; with scale groups (16 bytes per row for four K
+// tiles, K a multiple of 512 and 16-byte aligned scale rows) two group
+// buffers follow the stages.
+template <bool SG>
+struct MnRing {
+    static constexpr int STAGE = 2 * MN_OP_BYTES + (SG ? 0 : (MN_BM + MN_BN) * 4);
+    static constexpr int GROUP = (MN_BM + MN_BN) * 16;
+    static constexpr int LDS = MN_S * STAGE + (SG ? 2 * GROUP : 0);
+    static constexpr int LOADS = 2 * MN_NL + (SG ? 0 : 2);   // loads per wave and K tile
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(LOADS + 2 < 64, "vmcnt range");
+};
 
 typedef int intx2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) intx2 *lds_v2_t;
 
-template <int FMT, bool A_MN, bool B_MN, bool PERSIST, int EPI>
+template <int FMT, bool A_MN, bool B_MN, bool SG, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mx_mn(GemmArgs p, int group_m)
 {
     using G = MnGeom;
+    using R = MnRing<SG>;
     constexpr int BM = MN_BM, BN = MN_BN, NL = MN_NL, TI = G::TI, TJ = G::TJ;
-    __shared__ __attribute__((aligned(1024))) char smem[MN_S * MN_STAGE];
+    constexpr int MN_STAGE = R::STAGE, MN_LOADS = R::LOADS;
+    __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+    char *const groups = smem + MN_S * MN_STAGE;   // scale groups: 2 x R::GROUP
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -170,13 +183,29 @@ void gemm_mx_mn(GemmArgs p, int group_m)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_ptr_t)(base + MN_OP_BYTES + (wave * NL + u) * 1024), 16, voff, soff_b, 0, 0);
         }
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.sa, live ? t.nsa : 0u),
-                                     rsb = make_rsrc(t.sb, live ? t.nsb : 0u);
-        char *sbase = base + 2 * MN_OP_BYTES;
-        const uint32_t voa = vs_a, vob = vs_b;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sbase + wave * 256), 4, voa, kt * 4, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sbase + BM * 4 + wave * 256), 4, vob, kt * 4,
-                                                 0, 0);
+        if constexpr (!SG) {
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.sa, live ? t.nsa : 0u),
+                                         rsb = make_rsrc(t.sb, live ? t.nsb : 0u);
+            char *sbase = base + 2 * MN_OP_BYTES;
+            const uint32_t voa = vs_a, vob = vs_b;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sbase + wave * 256), 4, voa, kt * 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(sbase + BM * 4 + wave * 256), 4, vob,
+                                                     kt * 4, 0, 0);
+        }
+    };
+    // Scale group gi (K tiles 4 gi .. 4 gi + 3) of span t into group buffer
+    // gi % 2: lane l brings the 16 bytes of row 64 wave + l.
+    auto issue_group = [&](const Span &t, int gi) {
+        if constexpr (SG) {
+            char *gb = groups + (gi & 1) * R::GROUP;
+            const bool live = 4 * gi < nk;
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(t.sa, live ? t.nsa : 0u),
+                                         rsb = make_rsrc(t.sb, live ? t.nsb : 0u);
+            const uint32_t voa = vs_a, vob = vs_b;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(gb + wave * 1024), 16, voa, gi * 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(gb + BM * 16 + wave * 1024), 16, vob,
+                                                     gi * 16, 0, 0);
+        }
     };
 
     // Fragment of k-step ks for the 32-row block starting at row `rb` of
@@ -214,14 +243,18 @@ void gemm_mx_mn(GemmArgs p, int group_m)
         for (int j = 0; j < TJ; ++j)
             fb[j] = frag(B_MN, base + MN_OP_BYTES, wn * G::WN + j * 32, ks);
     };
-    auto read_sc = [&](int stage, int (&sa)[TI], int (&sb)[TJ]) {
-        const uint32_t *sw = (const uint32_t *)(smem + stage * MN_STAGE + 2 * MN_OP_BYTES);
+    // the scale words of K tile kt (in `stage`, or word kt % 4 of the rows'
+    // 16 bytes in group buffer (kt / 4) % 2)
+    auto read_sc = [&](int stage, int kt, int (&sa)[TI], int (&sb)[TJ]) {
+        constexpr int PITCH = SG ? 4 : 1;          // words per row
+        const uint32_t *sw = SG ? (const uint32_t *)(groups + ((kt >> 2) & 1) * R::GROUP) + (kt & 3)
+                                : (const uint32_t *)(smem + stage * MN_STAGE + 2 * MN_OP_BYTES);
 #pragma unroll
         for (int i = 0; i < TI; ++i)
-            sa[i] = (int)(sw[wm * G::WM + i * 32 + l32] >> (8 * h));
+            sa[i] = (int)(sw[(wm * G::WM + i * 32 + l32) * PITCH] >> (8 * h));
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-            sb[j] = (int)(sw[BM + wn * G::WN + j * 32 + l32] >> (8 * h));
+            sb[j] = (int)(sw[(BM + wn * G::WN + j * 32 + l32) * PITCH] >> (8 * h));
     };
     // k-step ks: blocks 2ks (lanes 0-31) and 2ks + 1 (lanes 32-63) of the
     // K tile's scale word, byte 2ks after the upper half's one-byte shift;
@@ -244,7 +277,8 @@ void gemm_mx_mn(GemmArgs p, int group_m)
         int tm, tn;
         grouped_tile(tile_of(r), tiles_m, tiles_n, group_m, tm, tn);
         if (r > 0)
-            barrier();                               // the previous tile's stages are free
+            barrier();                               // the previous tile's stages and groups are free
+        issue_group(cur, 0);
         issue(cur, 0, 0);
         issue(cur, 1, 1);
 #pragma unroll
@@ -255,7 +289,7 @@ void gemm_mx_mn(GemmArgs p, int group_m)
         wait_vmcnt<MN_LOADS>();
         barrier();
         read_ks(0, 0, f0a, f0b);
-        read_sc(0, sa_c, sb_c);
+        read_sc(0, 0, sa_c, sb_c);
         int stage = 0;
         for (int kt = 0; kt < nk; ++kt) {
             read_ks(stage, 1, f1a, f1b);
@@ -270,9 +304,14 @@ void gemm_mx_mn(GemmArgs p, int group_m)
             barrier();
             __builtin_amdgcn_sched_barrier(0);
             issue(cur, kt + 2, stage);
+            // at a group's first K tile the next group into the other group
+            // buffer, whose last reads (of K tile kt - 1) came before the
+            // previous barrier; the next K tile's wait covers it
+            if (SG && (kt & 3) == 0)
+                issue_group(cur, kt / 4 + 1);
             const int nstage = stage ^ 1;
             read_ks(nstage, 0, f0a, f0b);            // past the last K tile: unused
-            read_sc(nstage, sa_n, sb_n);
+            read_sc(nstage, kt + 1, sa_n, sb_n);
             mma(std::integral_constant<int, 1>{}, f1a, f1b, sa_c, sb_c);
 #pragma unroll
             for (int i = 0; i < TI; ++i)
@@ -288,22 +327,32 @@ void gemm_mx_mn(GemmArgs p, int group_m)
     wait_vmcnt<0>();
 }
 
-template <int FMT, bool A_MN, bool B_MN, bool PERSIST>
+template <int FMT, bool A_MN, bool B_MN, bool SG, bool PERSIST>
 hipError_t launch_mn(const GemmArgs &p, hipStream_t s)
 {
     const int tiles_m = (p.M + MN_BM - 1) / MN_BM, tiles_n = (p.N + MN_BN - 1) / MN_BN;
     const int ntiles = tiles_m * tiles_n;
     const int group_m = group_rows(tiles_m, p.group_m);
     if (PERSIST && ntiles <= p.ncu)
-        return launch_mn<FMT, A_MN, B_MN, false>(p, s);
+        return launch_mn<FMT, A_MN, B_MN, SG, false>(p, s);
     const int grid = PERSIST ? (ntiles < p.ncu ? ntiles : p.ncu) : ntiles;
     if (whole_bf16(p, MN_BM, MN_BN))
-        hipLaunchKernelGGL((gemm_mx_mn<FMT, A_MN, B_MN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0, s,
-                           p, group_m);
+        hipLaunchKernelGGL((gemm_mx_mn<FMT, A_MN, B_MN, SG, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
+                           s, p, group_m);
     else
-        hipLaunchKernelGGL((gemm_mx_mn<FMT, A_MN, B_MN, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p,
+        hipLaunchKernelGGL((gemm_mx_mn<FMT, A_MN, B_MN, SG, PERSIST, EPI_ANY>), dim3(grid), dim3(256), 0, s, p,
                            group_m);
     return hipGetLastError();
+}
+
+// scale groups when K is a multiple of 512 and the scale rows are 16-byte
+// aligned
+template <int FMT, bool A_MN, bool B_MN, bool PERSIST>
+hipError_t launch_mn_sg(const GemmArgs &p, hipStream_t s)
+{
+    const bool sg = p.K % 512 == 0 && p.ld_sa % 16 == 0 && p.ld_sb % 16 == 0 && (uintptr_t)p.SA % 16 == 0 &&
+                    (uintptr_t)p.SB % 16 == 0;
+    return sg ? launch_mn<FMT, A_MN, B_MN, true, PERSIST>(p, s) : launch_mn<FMT, A_MN, B_MN, false, PERSIST>(p, s);
 }
 
 template <int FMT, bool PERSIST>
@@ -311,11 +360,11 @@ hipError_t launch_mn_layouts(const GemmArgs &p, hipStream_t s)
 {
     const bool a_mn = p.a_cm != 0, b_mn = p.b_cm == 0;
     if (a_mn && b_mn)
-        return launch_mn<FMT, true, true, PERSIST>(p, s);
+        return launch_mn_sg<FMT, true, true, PERSIST>(p, s);
     if (a_mn)
-        return launch_mn<FMT, true, false, PERSIST>(p, s);
+        return launch_mn_sg<FMT, true, false, PERSIST>(p, s);
     if (b_mn)
-        return launch_mn<FMT, false, true, PERSIST>(p, s);
+        return launch_mn_sg<FMT, false, true, PERSIST>(p, s);
     return hipErrorInvalidValue;                     // both K-contiguous: the early-release ring
 }
 

@@ -419,6 +419,24 @@ def test_mx_mn_major_operands(fmt, layout, level):
 
 @pytest.mark.parametrize("level", [5, 6])
 @pytest.mark.parametrize("layout", [(True, True), (True, False)], ids=["a_col_b_col", "a_col_b_row"])
+@pytest.mark.parametrize("pad_a,pad_b", [(16, 32), (4, 8)], ids=["scale-groups", "groups-misaligned"])
+def test_mx_mn_major_scale_rows(layout, level, pad_a, pad_b):
+    """The transpose-load kernel with K = 1024 and scale rows longer than
+    K / 32: 16-byte multiples take the scale groups (16 bytes per row for four
+    K tiles), 4-byte ones the per-K-tile scale words; integer data bitwise."""
+    a_cm, b_cm = layout
+    M, N, K = 300, 260, 1024
+    p = make_problem(M, N, K, fmt=E4M3FN, a_col_major=a_cm, b_col_major=b_cm, c_dtype=OUT_F32,
+                     dist="int", lo=-4, hi=4, scale_exp_lo=0, scale_exp_hi=2,
+                     lda=pad16(M if a_cm else K) + 16, ldb=pad16(K if b_cm else N) + 32,
+                     ld_sa=K // 32 + pad_a, ld_sb=K // 32 + pad_b, seed=9200 + level + pad_a)
+    r = run_level(p, level)
+    assert r is not None
+    assert_bitwise(p, r[1])
+
+
+@pytest.mark.parametrize("level", [5, 6])
+@pytest.mark.parametrize("layout", [(True, True), (True, False)], ids=["a_col_b_col", "a_col_b_row"])
 def test_mx_mn_major_large_integer_exact(layout, level):
     """The transpose-load kernel at a ragged large shape over many tiles
     (persistent walk at level 6): row and column sums exact, sampled entries
