@@ -207,104 +207,110 @@ void attention_fwd(AttnArgs a)
             issue_k(j + 1, buf ^ 1);
             issue_v(j + 1, buf ^ 1);
         }
-        // ---- S = Q K^T (two 32-key blocks): the two blocks' accumulators
-        // alternate (independent chains), and each k-step's K fragments are
-        // read one k-step ahead of their products
-        const char *kb = kbuf + buf * G::K_BYTES;
-        floatx16 sacc[2];
-        sacc[0] = zero16();
-        sacc[1] = zero16();
-        {
-            const char *krp0 = kb + krow * G::ROWK, *krp1 = kb + (32 + krow) * G::ROWK;
-            bf16x8 kf[2][2];
-            kf[0][0] = *(const bf16x8 *)(krp0 + (h ^ kswz) * 16);
-            kf[0][1] = *(const bf16x8 *)(krp1 + (h ^ kswz) * 16);
-#pragma unroll
-            for (int s = 0; s < G::KS; ++s) {
-                if (s + 1 < G::KS) {
-                    kf[(s + 1) & 1][0] = *(const bf16x8 *)(krp0 + ((2 * (s + 1) + h) ^ kswz) * 16);
-                    kf[(s + 1) & 1][1] = *(const bf16x8 *)(krp1 + ((2 * (s + 1) + h) ^ kswz) * 16);
-                }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][0], qf[s], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][1], qf[s], sacc[1], 0, 0, 0);
-            }
-        }
-        // ---- online softmax.  Tiles that every row of this wave sees
-        // whole skip the mask.
+        // Causal: a key tile wholly past the diagonal of this wave's last row
+        // is masked for every row of the wave (its probabilities are zero
+        // and its maximum -inf), so the wave skips its products and softmax
+        // and only takes part in the loads and the barrier.
         const int key0 = j * ABN;
-        const bool whole = key0 + ABN <= a.seq_k &&
-                           (!CAUSAL || key0 + ABN - 1 <= q0 + 32 * wave + a.seq_k - a.seq_q);
-        // this tile's maximum logit of the row (-inf: nothing visible); on
-        // masked tiles the scores are scaled here and masked keys set to
-        // -inf, so the exponent below multiplies by 1 instead of c
-        float tm;
-        if (whole) {
-            float ext = sacc[0][0];
+        if (!CAUSAL || key0 <= q0 + 32 * wave + 31 + a.seq_k - a.seq_q) {
+            // ---- S = Q K^T (two 32-key blocks): the two blocks' accumulators
+            // alternate (independent chains), and each k-step's K fragments are
+            // read one k-step ahead of their products
+            const char *kb = kbuf + buf * G::K_BYTES;
+            floatx16 sacc[2];
+            sacc[0] = zero16();
+            sacc[1] = zero16();
+            {
+                const char *krp0 = kb + krow * G::ROWK, *krp1 = kb + (32 + krow) * G::ROWK;
+                bf16x8 kf[2][2];
+                kf[0][0] = *(const bf16x8 *)(krp0 + (h ^ kswz) * 16);
+                kf[0][1] = *(const bf16x8 *)(krp1 + (h ^ kswz) * 16);
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    ext = better(ext, sacc[blk][r]);
-            tm = ext * c;
-        } else {
-            tm = ninf;
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * blk + attn_key_of_col(8 * (r >> 2) + 4 * h + (r & 3));
-                    const bool vis = key < a.seq_k && (!CAUSAL || key <= diag);
-                    sacc[blk][r] = vis ? sacc[blk][r] * c : ninf;
-                    tm = __builtin_fmaxf(tm, sacc[blk][r]);
-                }
-        }
-        const float c_eff = whole ? c : 1.0f;
-        tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32));
-        if (__builtin_amdgcn_ballot_w64(tm > m_ref + TAU)) {
-            const float m_new = __builtin_fmaxf(m_ref, tm);
-            const float alpha = m_new == ninf ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int b = 0; b < G::DB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    o_acc[b][r] *= alpha;
-        }
-        const float mu = m_ref == ninf ? 0.0f : m_ref;
-        float psum = 0.0f;
-        bf16x8 pf[2][2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + e], c_eff, -mu));
-                    psum += pr;
-                    pf[blk][t][e] = (__bf16)pr;
+                for (int s = 0; s < G::KS; ++s) {
+                    if (s + 1 < G::KS) {
+                        kf[(s + 1) & 1][0] = *(const bf16x8 *)(krp0 + ((2 * (s + 1) + h) ^ kswz) * 16);
+                        kf[(s + 1) & 1][1] = *(const bf16x8 *)(krp1 + ((2 * (s + 1) + h) ^ kswz) * 16);
+                    }
+                    sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][0], qf[s], sacc[0], 0, 0, 0);
+                    sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 1][1], qf[s], sacc[1], 0, 0, 0);
                 }
             }
-        l_run += psum;
-        // ---- O += P V (four k-steps of 16 keys): the DB blocks of O
-        // alternate within each k-step (independent chains), and each
-        // k-step's V fragments are read one k-step ahead
-        {
-            bf16x8 vf[2][G::DB];
+            // ---- online softmax.  Tiles that every row of this wave sees
+            // whole skip the mask.
+            const bool whole = key0 + ABN <= a.seq_k &&
+                               (!CAUSAL || key0 + ABN - 1 <= q0 + 32 * wave + a.seq_k - a.seq_q);
+            // this tile's maximum logit of the row (-inf: nothing visible); on
+            // masked tiles the scores are scaled here and masked keys set to
+            // -inf, so the exponent below multiplies by 1 instead of c
+            float tm;
+            if (whole) {
+                float ext = sacc[0][0];
 #pragma unroll
-            for (int b = 0; b < G::DB; ++b)
-                vf[0][b] = read_vf(buf, b, 0);
+                for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int ts = 0; ts < 4; ++ts) {
-                if (ts + 1 < 4) {
+                    for (int r = 0; r < 16; ++r)
+                        ext = better(ext, sacc[blk][r]);
+                tm = ext * c;
+            } else {
+                tm = ninf;
 #pragma unroll
-                    for (int b = 0; b < G::DB; ++b)
-                        vf[(ts + 1) & 1][b] = read_vf(buf, b, ts + 1);
-                }
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = key0 + 32 * blk + attn_key_of_col(8 * (r >> 2) + 4 * h + (r & 3));
+                        const bool vis = key < a.seq_k && (!CAUSAL || key <= diag);
+                        sacc[blk][r] = vis ? sacc[blk][r] * c : ninf;
+                        tm = __builtin_fmaxf(tm, sacc[blk][r]);
+                    }
+            }
+            const float c_eff = whole ? c : 1.0f;
+            tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32));
+            if (__builtin_amdgcn_ballot_w64(tm > m_ref + TAU)) {
+                const float m_new = __builtin_fmaxf(m_ref, tm);
+                const float alpha = m_new == ninf ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                m_ref = m_new;
+                l_run *= alpha;
 #pragma unroll
                 for (int b = 0; b < G::DB; ++b)
-                    o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ts & 1][b], pf[ts >> 1][ts & 1], o_acc[b],
-                                                                       0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o_acc[b][r] *= alpha;
+            }
+            const float mu = m_ref == ninf ? 0.0f : m_ref;
+            float psum = 0.0f;
+            bf16x8 pf[2][2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + e], c_eff, -mu));
+                        psum += pr;
+                        pf[blk][t][e] = (__bf16)pr;
+                    }
+                }
+            l_run += psum;
+            // ---- O += P V (four k-steps of 16 keys): the DB blocks of O
+            // alternate within each k-step (independent chains), and each
+            // k-step's V fragments are read one k-step ahead
+            {
+                bf16x8 vf[2][G::DB];
+#pragma unroll
+                for (int b = 0; b < G::DB; ++b)
+                    vf[0][b] = read_vf(buf, b, 0);
+#pragma unroll
+                for (int ts = 0; ts < 4; ++ts) {
+                    if (ts + 1 < 4) {
+#pragma unroll
+                        for (int b = 0; b < G::DB; ++b)
+                            vf[(ts + 1) & 1][b] = read_vf(buf, b, ts + 1);
+                    }
+#pragma unroll
+                    for (int b = 0; b < G::DB; ++b)
+                        o_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ts & 1][b], pf[ts >> 1][ts & 1], o_acc[b],
+                                                                           0, 0, 0);
+                }
             }
         }
         // ---- the barrier: every wave's reads of this tile are done and
