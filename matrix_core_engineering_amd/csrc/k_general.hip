@@ -6,12 +6,13 @@
 // The operands travel through registers: each lane loads 16-byte chunks of
 // a 128-row operand tile per K tile (gfx950 global loads accept any
 // alignment, so a 2-byte-aligned row costs no extra instructions), then
-// writes them to LDS in the K-major, XOR-swizzled rows that the
-// matrix-core fragment reads expect.  A K-contiguous chunk is eight
-// consecutive K of one row (one 16-byte LDS write); for an MN-major operand
-// a lane loads the same eight rows at adjacent K and writes them transposed
-// as 4-byte (k, k+1) pairs ("B200 TMA Pipeline Designer", section B: the
-// layout the reader expects is produced by the writer).
+// writes them to LDS with 16-byte writes.  A K-contiguous chunk is eight
+// consecutive K of one row, kept in K-major, XOR-swizzled rows that the
+// matrix-core fragment reads expect; an MN-major chunk is eight consecutive
+// rows at one K, kept as loaded (256-byte K rows), and the fragment reads
+// transpose it with ds_read_b64_tr_b16 ("B200 TMA Pipeline Designer",
+// section B: the layout the reader expects is produced by the writer; on
+// gfx950 the transposing side is the LDS read).
 //
 // Ring: two LDS stages of 64-byte rows (K tile 32).  K tile kt+1 is loaded
 // into registers before K tile kt's matrix-core work and written to the
@@ -24,14 +25,31 @@
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "mn_layout.hpp"
 #include "sched.hpp"
 
 namespace mce {
 namespace {
 
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 *lds_v4i16_t;
 
 constexpr int GBM = 128, GBN = 128;
+
+// Element e of the result is v[e + s] for e + s < 8, else zero (s >= 0);
+// selects, not branches, since s varies across lanes.
+__device__ __forceinline__ u16x8 shift_down(const u16x8 &v, int s)
+{
+    const uint64_t lo = __builtin_bit_cast(uint64_t, u16x4{v[0], v[1], v[2], v[3]});
+    const uint64_t hi = __builtin_bit_cast(uint64_t, u16x4{v[4], v[5], v[6], v[7]});
+    const int b = min(16 * s, 128);
+    const uint64_t lo_hi = b == 0 ? lo : b >= 64 ? 0 : lo >> b;
+    const uint64_t hi_lo = b == 0 ? 0 : b >= 64 ? (b >= 128 ? 0 : hi >> (b - 64)) : hi << (64 - b);
+    const uint64_t nhi = b >= 64 ? 0 : hi >> b;
+    const u16x4 l4 = __builtin_bit_cast(u16x4, lo_hi | hi_lo), h4 = __builtin_bit_cast(u16x4, nhi);
+    return u16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+}
 
 template <int BK>
 struct GenTile {
@@ -57,15 +75,14 @@ struct GenGeom {
 // KC chunk j of lane tid: row idx / CPR, K (idx % CPR) * 8 with
 // idx = j * 256 + tid.  MN chunk j: rows 8 mn_c(tid) .. +7 at K
 // mn_k(tid) + j: eight consecutive lanes read 128 contiguous bytes of one K
-// row, and the 32 lanes that write LDS in one cycle (measured: 32 lanes per
-// cycle for 4-byte writes) cover four K pairs, so the transposed writes
-// meet at most two to a bank.
+// row and write eight chunks of one 256-byte LDS K row.
 template <bool KC, int BK>
 struct Stager {
     using T = GenTile<BK>;
     typedef u16x8 Regs[T::CH];             // one K tile's chunks of this lane
     const uint16_t *ptr[KC ? T::CH : 1];   // this tile's chunk addresses at K = 0
-    int roff;                              // MN-major: first LDS row of this lane's chunks
+    int roff;                              // MN-major: first row of this lane's chunks in the tile
+    int shift;                             // MN-major: rows that start was moved back by
 
     static __device__ __forceinline__ int mn_c(int tid) { return (tid & 7) | ((tid >> 7) << 3); }
     static __device__ __forceinline__ int mn_k(int tid) { return 2 * ((tid >> 3) & 15); }
@@ -73,10 +90,11 @@ struct Stager {
     // Per tile.  Rows past the edge are never read: a KC row there is
     // clamped to the last row (its products only reach C rows or columns
     // that are never stored), and an MN-major chunk that would cross the
-    // edge starts at rows - 8 instead and fills those eight LDS rows (with
-    // the values another lane may also write there); LDS rows past the edge
-    // then keep stale values, which also reach only C entries that are
-    // never stored.  The MN-major clamp needs eight valid rows in the tile.
+    // edge is fetched ending at it and shifted back into place when it is
+    // written; LDS rows past the edge keep whatever they hold, which also
+    // reaches only C entries that are never stored.  The MN-major clamp
+    // needs eight valid rows in the tile (else every chunk that crosses the
+    // edge is loaded per element).
     __device__ __forceinline__ void prep(const uint16_t *base, int ld, int rows, int r0, int tid)
     {
         if (KC) {
@@ -86,12 +104,13 @@ struct Stager {
                 ptr[KC ? j : 0] = base + (size_t)min(r0 + idx / T::CPR, rows - 1) * ld + (idx % T::CPR) * 8;
             }
             roff = 0;
+            shift = 0;
         } else {
-            // clamp only while the tile holds eight valid rows, so that the
-            // chunk's LDS rows stay inside the tile
+            // clamp only while the tile holds eight valid rows
             const int r = rows - r0 >= 8 ? min(r0 + mn_c(tid) * 8, rows - 8) : r0 + mn_c(tid) * 8;
             ptr[0] = base + (size_t)mn_k(tid) * ld + r;
             roff = r - r0;
+            shift = r0 + mn_c(tid) * 8 - r;
         }
     }
 
@@ -132,7 +151,8 @@ struct Stager {
         }
     }
 
-    __device__ __forceinline__ void store(const Regs &v, char *lds, int tid) const
+    // edge: the tile crosses the M or N edge (MN chunks may need shifting)
+    __device__ __forceinline__ void store(const Regs &v, char *lds, bool edge, int tid) const
     {
         if (KC) {
 #pragma unroll
@@ -142,16 +162,11 @@ struct Stager {
                 *(u16x8 *)(lds + row * T::ROWB + ((c ^ T::swz(row)) * 16)) = v[j];
             }
         } else {
+            const int c = mn_c(tid);
 #pragma unroll
-            for (int jp = 0; jp < T::CH / 2; ++jp) {
-                const int kk = mn_k(tid) + 2 * jp;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = roff + e;
-                    const uint32_t pair = (uint32_t)v[2 * jp][e] | ((uint32_t)v[2 * jp + 1][e] << 16);
-                    *(uint32_t *)(lds + row * T::ROWB + (((kk >> 3) ^ T::swz(row)) * 16) + (kk & 7) * 2) =
-                        pair;
-                }
+            for (int j = 0; j < T::CH; ++j) {
+                const int k = mn_k(tid) + j;
+                *(u16x8 *)(lds + k * 256 + ((c ^ mn_swz16(k)) * 16)) = edge ? shift_down(v[j], shift) : v[j];
             }
         }
     }
@@ -167,13 +182,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
-    // each fragment row's swizzle (rows wm*64 + i*32 + l32, wn*64 + j*32 + l32)
-    int swz_a[2], swz_b[2];
+    // per fragment row block (wm*64 + i*32, wn*64 + j*32): a K-contiguous
+    // operand's 16-byte read offset at k-step 0 (logical chunk h; k-step
+    // ks is the offset ^ 32 ks), or an MN-major operand's transposing-read
+    // offset (this lane supplies K row 8h + (lane % 16) / 4 and rows
+    // 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3 of the block; the second
+    // read is 4 K rows on and k-step 1 16 on, at the same swizzle)
+    auto frag_off = [&](bool kc, int rb) {
+        if (kc) {
+            const int row = rb + l32;
+            return row * T::ROWB + ((h ^ T::swz(row)) * 16);
+        }
+        const int kr = 8 * h + ((lane & 15) >> 2);
+        const int n = rb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        return kr * 256 + (((n >> 3) ^ mn_swz16(kr)) * 16) + (n & 7) * 2;
+    };
+    int off_a[2], off_b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        swz_a[i] = T::swz(wm * 64 + i * 32 + l32);
-        swz_b[i] = T::swz(wn * 64 + i * 32 + l32);
+        off_a[i] = frag_off(A_KC, wm * 64 + i * 32);
+        off_b[i] = T::OP_BYTES + frag_off(B_KC, wn * 64 + i * 32);
     }
+    auto frag = [&](bool kc, const char *S, int o, int ks) -> bf16x8 {
+        if (kc)
+            return *(const bf16x8 *)(S + (o ^ (32 * ks)));
+        const char *p0 = S + o + 4096 * ks;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)p0);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(p0 + 1024));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
     const int tiles_m = (p.M + GBM - 1) / GBM, tiles_n = (p.N + GBN - 1) / GBN;
     const int ntiles = tiles_m * tiles_n;
@@ -191,18 +228,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
     floatx16 acc[2][2];
 
     auto compute = [&](int stage) {
-        const char *As = smem + stage * T::STAGE_BYTES, *Bs = As + T::OP_BYTES;
+        const char *S = smem + stage * T::STAGE_BYTES;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 fa[2], fb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                fa[i] = *(const bf16x8 *)(As + (wm * 64 + i * 32 + l32) * T::ROWB +
-                                          ((2 * ks + h) ^ swz_a[i]) * 16);
+                fa[i] = frag(A_KC, S, off_a[i], ks);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                fb[j] = *(const bf16x8 *)(Bs + (wn * 64 + j * 32 + l32) * T::ROWB +
-                                          ((2 * ks + h) ^ swz_b[j]) * 16);
+                fb[j] = frag(B_KC, S, off_b[j], ks);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -245,9 +280,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void g
             sa.load_fast(va, p.lda, kt * BK);
             sb.load_fast(vb, p.ldb, kt * BK);
         };
+        const bool a_edge = m0 + GBM > p.M, b_edge = n0 + GBN > p.N;
         auto store = [&](int stage) {
-            sa.store(va, smem + stage * T::STAGE_BYTES, tid);
-            sb.store(vb, smem + stage * T::STAGE_BYTES + T::OP_BYTES, tid);
+            sa.store(va, smem + stage * T::STAGE_BYTES, a_edge, tid);
+            sb.store(vb, smem + stage * T::STAGE_BYTES + T::OP_BYTES, b_edge, tid);
         };
 
         // K tile kt+1 travels in registers under K tile kt's work and is

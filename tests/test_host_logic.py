@@ -38,6 +38,7 @@ int h_attn_key_of_col(int j) { return mce::attn_key_of_col(j); }
 int h_swz_attn_k(int r, int d) { return mce::swz_attn_k(r, d); }
 int h_swz_attn_v(int r, int d) { return mce::swz_attn_v(r, d); }
 int h_mn_swz(int r) { return mce::mn_swz(r); }
+int h_mn_swz16(int r) { return mce::mn_swz16(r); }
 int h_loads_after(int x, int n, int l) { return mce::loads_after(x, n, l) ? 1 : 0; }
 }
 '''
@@ -237,7 +238,7 @@ def test_swizzles_are_permutations_per_row(lib):
 
 def mn_lane(t):
     """Register-staged kernel, MN-major operand: lane t of the workgroup
-    holds rows 8c .. 8c+7 at K pair kp, kp + 1 (the kernel's mn_c, mn_k)."""
+    holds rows 8c .. 8c+7 at K rows kp, kp + 1 (the kernel's mn_c, mn_k)."""
     return (t & 7) | ((t >> 7) << 3), 2 * ((t >> 3) & 15)
 
 
@@ -247,18 +248,51 @@ def test_mn_lane_map_covers_tile_once():
     assert {k for _, k in map(mn_lane, range(256))} == set(range(0, 32, 2))
 
 
-@pytest.mark.parametrize("e", range(8))
-def test_mn_transposed_writes_at_most_two_way(lib, e):
-    """4-byte writes of rows 8c + e at each lane's K pair: 32 lanes per cycle
-    over 128 bytes, and all 32 lanes write the same row parity, so two lanes
-    per bank is the floor; the lane map and swz4q reach it."""
+def mn16_addr(lib, krow, n):
+    """Byte offset of element (K row krow, operand row n) in the bf16 MN-major
+    tile kept as loaded: 256-byte K rows, 16-byte chunk n / 8 at
+    (n / 8) ^ mn_swz16(krow)."""
+    return krow * 256 + (((n >> 3) ^ lib.h_mn_swz16(krow)) * 16) + (n & 7) * 2
+
+
+@pytest.mark.parametrize("j", range(2))
+def test_mn16_chunk_writes_conflict_free(lib, j):
+    """16-byte writes of the chunk (rows 8c .. 8c+7, K row kp + j) of every
+    lane, 8 consecutive lanes per cycle: eight chunks of one K row."""
     for w in range(4):
         addrs = []
         for l in range(64):
-            c, kk = mn_lane(64 * w + l)
-            row = 8 * c + e
-            addrs.append(row * 64 + (((kk >> 3) ^ lib.h_swz4q(row)) * 16) + (kk & 7) * 2)
-        assert cycles_extra(addrs, 4, "write") <= 2    # one extra cycle per 32-lane half
+            c, kp = mn_lane(64 * w + l)
+            addrs.append(mn16_addr(lib, kp + j, 8 * c))
+        assert cycles_extra(addrs, 16, "write") == 0
+
+
+def test_mn16_tile_written_once_and_fragments_read(lib):
+    """Every (K row, chunk) of the tile is written by exactly one lane; the
+    two transposing reads of each fragment (row block rb, k-step ks) give
+    lane l operand row rb + l % 32 at K 16 ks + 8 (l / 32) .. +7 in
+    register order, each read conflict-free under the 8-byte read rule."""
+    seen = [(kp + j, mn16_addr(lib, kp + j, 8 * c)) for c, kp in map(mn_lane, range(256)) for j in range(2)]
+    assert len({a for _, a in seen}) == 512 and {k for k, _ in seen} == set(range(32))
+    lds16 = {}
+    for k in range(32):
+        for n in range(128):
+            lds16[mn16_addr(lib, k, n)] = (k, n)
+    for rb in range(0, 128, 32):
+        for ks in range(2):
+            regs = [[] for _ in range(64)]
+            for rd in range(2):
+                addrs = []
+                for l in range(64):
+                    kr = 16 * ks + 4 * rd + 8 * (l >> 5) + ((l & 15) >> 2)
+                    n = rb + 16 * ((l >> 4) & 1) + 4 * (l & 3)
+                    addrs.append(mn16_addr(lib, kr, n))
+                assert cycles_extra(addrs, 8, "read") == 0
+                for l, vals in enumerate(tr16_gather(addrs, lds16)):
+                    regs[l] += vals
+            for l in range(64):
+                k0 = 16 * ks + 8 * (l >> 5)
+                assert regs[l] == [(k0 + e, rb + (l & 31)) for e in range(8)]
 
 
 @pytest.mark.parametrize("j", range(2))
