@@ -109,16 +109,53 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G:
             }
         }
     } else {
+        // edge tile: each lane's groups of four columns that lie inside C
+        // take the vector path, the one that crosses the N edge goes per
+        // element; either way with store_c's operations, so an element's
+        // value does not depend on which path stored it
 #pragma unroll
         for (int i = 0; i < G::TI; ++i)
 #pragma unroll
             for (int j = 0; j < G::TJ; ++j) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int q = 0; q < 4; ++q) {
                     const int m = mbase + i * 32;
-                    const int n = nbase + j * 32 + (r >> 2) * 8 + (r & 3);
-                    if (m < p.M && n < p.N)
-                        store_c(p, m, n, acc[i][j][r]);
+                    const int n = nbase + j * 32 + q * 8;
+                    const floatx16 &a = acc[i][j];
+                    if (m < p.M && n + 4 <= p.N) {
+                        const size_t idx = (size_t)m * p.ldc + n;
+                        if (p.c_dtype == OUT_F32) {
+                            float *dst = (float *)p.C + idx;
+                            floatx4 v = {p.alpha * a[4 * q], p.alpha * a[4 * q + 1], p.alpha * a[4 * q + 2],
+                                         p.alpha * a[4 * q + 3]};
+                            if (p.beta != 0.0f) {
+                                floatx4 c0;
+                                __builtin_memcpy(&c0, dst, 16);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    v[e] = __builtin_fmaf(p.beta, c0[e], v[e]);
+                            }
+                            __builtin_memcpy(dst, &v, 16);
+                        } else {
+                            uint16_t *dst = (uint16_t *)p.C + idx;
+                            u16x4 c0, o;
+                            if (p.beta != 0.0f)
+                                __builtin_memcpy(&c0, dst, 8);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float v = p.alpha * a[4 * q + e];
+                                if (p.beta != 0.0f)
+                                    v = __builtin_fmaf(p.beta, bf16_to_f32(c0[e]), v);
+                                o[e] = f32_to_bf16_rne(v);
+                            }
+                            __builtin_memcpy(dst, &o, 8);
+                        }
+                    } else if (m < p.M) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N)
+                                store_c(p, m, n + e, a[4 * q + e]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
