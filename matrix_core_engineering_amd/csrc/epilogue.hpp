@@ -16,10 +16,12 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 // Epilogue variants, chosen on the host per call: EPI_BF16_WHOLE when C is
 // bf16, beta == 0, M and N are whole tiles and C rows are 8-byte aligned
 // (one branch-free path); EPI_BF16_LDS (gemm_early) the same with 16-byte
-// aligned rows, staged through LDS for whole-line stores; EPI_ANY
-// otherwise.  Keeping the choice out of the kernel's run-time branches lets
-// the compiler move accumulators to stores one block at a time.
-enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1, EPI_BF16_LDS = 2 };
+// aligned rows, staged through LDS for whole-line stores; EPI_F32_LDS
+// (gemm_early) fp32 C of whole tiles with 16-byte aligned rows, any beta,
+// staged likewise; EPI_ANY otherwise.  Keeping the choice out of the
+// kernel's run-time branches lets the compiler move accumulators to stores
+// one block at a time.
+enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1, EPI_BF16_LDS = 2, EPI_F32_LDS = 3 };
 
 template <int EPI, class G, int BM, int BN>
 __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],

@@ -192,6 +192,57 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
         }
 }
 
+// Whole fp32 tiles through the same buffers: a block (32 rows x 32 columns
+// = 32 rows of 128 bytes) per round, RR rows at a time.  Lane (l32, h)
+// writes its four 16-byte pieces of row l32 (columns 8q + 4h .. +3) at the
+// 144-byte pitch (eight consecutive rows fall in eight distinct 16-byte
+// slots, so the writes are conflict-free); the read-back and the stores are
+// those above, with C read at the same 16-byte pieces when beta != 0.  The
+// arithmetic is the register path's (alpha * acc, then + beta * C0), so the
+// results are bitwise those of EPI_ANY.
+template <class G, int BM, int BN, int RR>
+__device__ __forceinline__ void store_tile_lds_f32(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
+                                                   int m_tile, int n_tile, int wm, int wn, int lane,
+                                                   char *buf)
+{
+    static_assert(RR == 8 || RR == 16 || RR == 32, "rows per round");
+    const int h = lane >> 5, l32 = lane & 31;
+    const int rrow = lane >> 3, rchunk = lane & 7;       // read-back position
+#pragma unroll
+    for (int i = 0; i < G::TI; ++i)
+#pragma unroll
+        for (int j = 0; j < G::TJ; ++j)
+#pragma unroll
+            for (int half = 0; half < 32 / RR; ++half) {
+            if (RR == 32 || l32 / RR == half) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx16 &a = acc[i][j];
+                    floatx4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    v *= p.alpha;
+                    *(floatx4 *)(buf + (l32 % RR) * EPI_PITCH + q * 32 + h * 16) = v;
+                }
+            }
+            wait_lgkm0();
+            float *c0 = (float *)p.C + (size_t)(m_tile + wm * G::WM + i * 32 + half * RR) * p.ldc + n_tile +
+                        wn * G::WN + j * 32 + rchunk * 4;
+#pragma unroll
+            for (int s = 0; s < RR / 8; ++s) {
+                const int row = s * 8 + rrow;
+                floatx4 v = *(const floatx4 *)(buf + row * EPI_PITCH + rchunk * 16);
+                floatx4 *dst = (floatx4 *)(c0 + (size_t)row * p.ldc);
+                if (p.beta != 0.0f) {
+                    const floatx4 c = *dst;
+                    v += p.beta * c;
+                }
+                *dst = v;
+            }
+            // the next round's writes may not overtake these reads
+            wait_lgkm0();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
 // The same for 16x16 blocks (the 16x16x32 format): with the B operand fed
 // first, lane l holds row l % 16 and columns 4(l/16) .. +3 of each block.
 // Per block row and group of four blocks (16 rows x 64 columns), every lane
@@ -550,7 +601,7 @@ void gemm_early(GemmArgs p, int group_m)
     constexpr int WAVES = P::WAVES;
     // rows per round of the LDS-staged epilogue: what the LDS left over holds
     constexpr int EPI_RR = WAVES == 8 ? (Op::SG ? 8 : 16) : (Op::SG || S16 ? 16 : 32);
-    constexpr int EPI_BYTES = EPI == EPI_BF16_LDS ? WAVES * epi_wave_bytes<EPI_RR>() : 0;
+    constexpr int EPI_BYTES = EPI == EPI_BF16_LDS || EPI == EPI_F32_LDS ? WAVES * epi_wave_bytes<EPI_RR>() : 0;
     static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + SG_BYTES + EPI_BYTES];
 
@@ -994,6 +1045,10 @@ void gemm_early(GemmArgs p, int group_m)
             store_tile_lds<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane_e,
                                               smem + G::LDS_BYTES + SG_BYTES +
                                                   wave * epi_wave_bytes<EPI_RR>());
+        else if constexpr (EPI == EPI_F32_LDS)
+            store_tile_lds_f32<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane_e,
+                                                  smem + G::LDS_BYTES + SG_BYTES +
+                                                      wave * epi_wave_bytes<EPI_RR>());
         else
             store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         // the load side moves one tile ahead
@@ -1281,6 +1336,13 @@ bool whole_bf16(const GemmArgs &p, int bm, int bn)
            p.ldc % 4 == 0 && ((uintptr_t)p.C % 8) == 0;
 }
 
+// fp32 C of whole tiles with 16-byte aligned rows (any beta)
+bool whole_f32(const GemmArgs &p, int bm, int bn)
+{
+    return p.c_dtype == OUT_F32 && p.M % bm == 0 && p.N % bn == 0 && p.ldc % 4 == 0 &&
+           ((uintptr_t)p.C % 16) == 0;
+}
+
 template <class Op, int BM, int BN, int STAGES, bool PERSIST>
 hipError_t launch(const GemmArgs &p, hipStream_t s)
 {
@@ -1317,6 +1379,9 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
                            s, p, group_m);
     else if (whole_bf16(p, BM, BN))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(64 * Op::WAVES), 0,
+                           s, p, group_m);
+    else if (whole_f32(p, BM, BN))
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_F32_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
     else
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_ANY>), dim3(grid), dim3(64 * Op::WAVES), 0, s, p,

@@ -723,6 +723,37 @@ def test_whole_tiles_bf16_output_persistent_tail(level, fmt, shape, alpha):
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
 
 
+@pytest.mark.parametrize("level", [5, 6, 9, None])
+@pytest.mark.parametrize("fmt,shape,alpha,beta",
+                         [(BF16, (2048, 1536, 512), 1.0, 0.0), (BF16, (4096, 4352, 256), 0.5, 1.0),
+                          (E4M3FN, (2048, 1536, 1024), 1.0, 1.0)],
+                         ids=["bf16-beta0", "bf16-272tiles-beta1", "mx-beta1"])
+def test_whole_tiles_f32_output_bitwise(level, fmt, shape, alpha, beta):
+    """Whole 256x256 tiles with fp32 output and 16-byte aligned rows (the
+    early-release ring stages them through LDS for whole-line stores, any
+    beta; 272 tiles also run a ragged persistent tail at level 6).
+    Exact-integer inputs and C0 in -1..1 make every fp32 value exact, so
+    the whole result must equal the float64 alpha * A B + beta * C0."""
+    M, N, K = shape
+    announce(f"whole tiles fp32 out level {level} {fmt} {shape} alpha {alpha} beta {beta}")
+    p = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_F32, seed=7500 + (level or 0) + M, alpha=alpha,
+                        beta=beta, c_dist="int", name="whole_tiles_f32_out")
+    r = run_level(p, level)
+    assert r is not None
+    vals = r[0]
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if fmt == E4M3FN:
+        from helpers import torch_decode_scales
+        A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+        B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    expect = alpha * (A @ B)
+    if beta != 0.0:
+        expect = expect + beta * p.C0[:M, :N].astype(np.float64)
+    bad = np.argwhere(vals != expect)
+    assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
+
+
 @pytest.mark.parametrize("shape", [mce.MCE_LOOP_BF16_32X32X16, mce.MCE_LOOP_BF16_16X16X32,
                                    mce.MCE_LOOP_MXFP8_32X32X64, mce.MCE_LOOP_MXFP4_32X32X64,
                                    mce.MCE_LOOP_MXFP6_32X32X64])
