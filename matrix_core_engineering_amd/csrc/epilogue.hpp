@@ -18,10 +18,11 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 // (one branch-free path); EPI_BF16_LDS (gemm_early) the same with 16-byte
 // aligned rows, staged through LDS for whole-line stores; EPI_F32_LDS
 // (gemm_early) fp32 C of whole tiles with 16-byte aligned rows, any beta,
-// staged likewise; EPI_ANY otherwise.  Keeping the choice out of the
+// staged likewise, and EPI_BF16B_LDS the same for bf16 C with beta != 0
+// (8-byte aligned rows); EPI_ANY otherwise.  Keeping the choice out of the
 // kernel's run-time branches lets the compiler move accumulators to stores
 // one block at a time.
-enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1, EPI_BF16_LDS = 2, EPI_F32_LDS = 3 };
+enum { EPI_ANY = 0, EPI_BF16_WHOLE = 1, EPI_BF16_LDS = 2, EPI_F32_LDS = 3, EPI_BF16B_LDS = 4 };
 
 template <int EPI, class G, int BM, int BN>
 __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],

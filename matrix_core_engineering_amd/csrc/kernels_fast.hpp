@@ -199,8 +199,10 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
 // slots, so the writes are conflict-free); the read-back and the stores are
 // those above, with C read at the same 16-byte pieces when beta != 0.  The
 // arithmetic is the register path's (alpha * acc, then + beta * C0), so the
-// results are bitwise those of EPI_ANY.
-template <class G, int BM, int BN, int RR>
+// results are bitwise those of EPI_ANY.  BF16B: bf16 C with beta != 0, the
+// fp32 alpha * acc staged the same way, then each lane's four elements
+// combined with C0 and rounded as the register path does, 8-byte pieces.
+template <class G, int BM, int BN, int RR, bool BF16B = false>
 __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
                                                    int m_tile, int n_tile, int wm, int wn, int lane,
                                                    char *buf)
@@ -224,18 +226,28 @@ __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs &p, floatx16 (
                 }
             }
             wait_lgkm0();
-            float *c0 = (float *)p.C + (size_t)(m_tile + wm * G::WM + i * 32 + half * RR) * p.ldc + n_tile +
-                        wn * G::WN + j * 32 + rchunk * 4;
+            const size_t e0 = (size_t)(m_tile + wm * G::WM + i * 32 + half * RR) * p.ldc + n_tile + wn * G::WN +
+                              j * 32 + rchunk * 4;
 #pragma unroll
             for (int s = 0; s < RR / 8; ++s) {
                 const int row = s * 8 + rrow;
                 floatx4 v = *(const floatx4 *)(buf + row * EPI_PITCH + rchunk * 16);
-                floatx4 *dst = (floatx4 *)(c0 + (size_t)row * p.ldc);
-                if (p.beta != 0.0f) {
-                    const floatx4 c = *dst;
-                    v += p.beta * c;
+                if constexpr (BF16B) {
+                    u16x4 *dst = (u16x4 *)((uint16_t *)p.C + e0 + (size_t)row * p.ldc);
+                    const u16x4 c = *dst;
+                    u16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c[e]), v[e]));
+                    *dst = o;
+                } else {
+                    floatx4 *dst = (floatx4 *)((float *)p.C + e0 + (size_t)row * p.ldc);
+                    if (p.beta != 0.0f) {
+                        const floatx4 c = *dst;
+                        v += p.beta * c;
+                    }
+                    *dst = v;
                 }
-                *dst = v;
             }
             // the next round's writes may not overtake these reads
             wait_lgkm0();
@@ -601,7 +613,8 @@ void gemm_early(GemmArgs p, int group_m)
     constexpr int WAVES = P::WAVES;
     // rows per round of the LDS-staged epilogue: what the LDS left over holds
     constexpr int EPI_RR = WAVES == 8 ? (Op::SG ? 8 : 16) : (Op::SG || S16 ? 16 : 32);
-    constexpr int EPI_BYTES = EPI == EPI_BF16_LDS || EPI == EPI_F32_LDS ? WAVES * epi_wave_bytes<EPI_RR>() : 0;
+    constexpr int EPI_BYTES =
+        EPI == EPI_BF16_LDS || EPI == EPI_F32_LDS || EPI == EPI_BF16B_LDS ? WAVES * epi_wave_bytes<EPI_RR>() : 0;
     static_assert(G::LDS_BYTES + SG_BYTES + EPI_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + SG_BYTES + EPI_BYTES];
 
@@ -1045,10 +1058,10 @@ void gemm_early(GemmArgs p, int group_m)
             store_tile_lds<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane_e,
                                               smem + G::LDS_BYTES + SG_BYTES +
                                                   wave * epi_wave_bytes<EPI_RR>());
-        else if constexpr (EPI == EPI_F32_LDS)
-            store_tile_lds_f32<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane_e,
-                                                  smem + G::LDS_BYTES + SG_BYTES +
-                                                      wave * epi_wave_bytes<EPI_RR>());
+        else if constexpr (EPI == EPI_F32_LDS || EPI == EPI_BF16B_LDS)
+            store_tile_lds_f32<G, BM, BN, EPI_RR, EPI == EPI_BF16B_LDS>(
+                p, acc, tm * BM, tn * BN, wm, wn, lane_e,
+                smem + G::LDS_BYTES + SG_BYTES + wave * epi_wave_bytes<EPI_RR>());
         else
             store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         // the load side moves one tile ahead
@@ -1343,6 +1356,13 @@ bool whole_f32(const GemmArgs &p, int bm, int bn)
            ((uintptr_t)p.C % 16) == 0;
 }
 
+// bf16 C of whole tiles with beta != 0 and 8-byte aligned rows
+bool whole_bf16_beta(const GemmArgs &p, int bm, int bn)
+{
+    return p.c_dtype == OUT_BF16 && p.beta != 0.0f && p.M % bm == 0 && p.N % bn == 0 && p.ldc % 4 == 0 &&
+           ((uintptr_t)p.C % 8) == 0;
+}
+
 template <class Op, int BM, int BN, int STAGES, bool PERSIST>
 hipError_t launch(const GemmArgs &p, hipStream_t s)
 {
@@ -1382,6 +1402,9 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
                            s, p, group_m);
     else if (whole_f32(p, BM, BN))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_F32_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
+                           s, p, group_m);
+    else if (whole_bf16_beta(p, BM, BN))
+        hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16B_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
     else
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_ANY>), dim3(grid), dim3(64 * Op::WAVES), 0, s, p,

@@ -754,6 +754,35 @@ def test_whole_tiles_f32_output_bitwise(level, fmt, shape, alpha, beta):
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
 
 
+@pytest.mark.parametrize("level", [5, 6, 9, None])
+@pytest.mark.parametrize("fmt,shape,alpha", [(BF16, (2048, 1536, 512), 1.0), (BF16, (4096, 4352, 256), 0.5),
+                                             (E4M3FN, (2048, 1536, 1024), 1.0)],
+                         ids=["bf16", "bf16-272tiles", "mx"])
+def test_whole_tiles_bf16_output_beta_bitwise(level, fmt, shape, alpha):
+    """Whole 256x256 tiles with bf16 output and beta = 1 (staged through LDS
+    by the early-release ring): exact-integer inputs and C0 in -1..1, so the
+    fp32 value alpha * A B + C0 is exact and the bf16 result must be its
+    correctly rounded value."""
+    M, N, K = shape
+    announce(f"whole tiles bf16 out beta 1 level {level} {fmt} {shape} alpha {alpha}")
+    p = integer_problem(M, N, K, fmt=fmt, c_dtype=OUT_BF16, seed=7600 + (level or 0) + M, alpha=alpha,
+                        beta=1.0, c_dist="int", name="whole_tiles_bf16_beta")
+    r = run_level(p, level)
+    assert r is not None
+    raw = r[1]
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if fmt == E4M3FN:
+        from helpers import torch_decode_scales
+        A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+        B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    from helpers import f64_to_bf16_bits
+    c0 = (p.C0[:M, :N].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    expect = f64_to_bf16_bits(alpha * (A @ B) + c0)
+    bad = np.argwhere(raw != expect)
+    assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
+
+
 @pytest.mark.parametrize("shape", [mce.MCE_LOOP_BF16_32X32X16, mce.MCE_LOOP_BF16_16X16X32,
                                    mce.MCE_LOOP_MXFP8_32X32X64, mce.MCE_LOOP_MXFP4_32X32X64,
                                    mce.MCE_LOOP_MXFP6_32X32X64])
