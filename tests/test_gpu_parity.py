@@ -754,6 +754,31 @@ def test_whole_tiles_f32_output_bitwise(level, fmt, shape, alpha, beta):
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
 
 
+@pytest.mark.parametrize("level", [6, 9])
+@pytest.mark.parametrize("out", [OUT_F32, OUT_BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("pad", [4, 1], ids=["aligned-pad", "unaligned-pad"])
+def test_whole_tiles_padded_c_rows_bitwise(level, out, pad):
+    """Whole tiles with beta = 1 and padded C rows: a pad of 4 elements keeps
+    the rows aligned (the LDS-staged stores, now with a row pitch other than
+    N), a pad of 1 does not (the register path).  The guard columns past N
+    must keep their C0 values; the result is exact as above."""
+    M, N, K = 1024, 768, 256
+    p = integer_problem(M, N, K, c_dtype=out, seed=7700 + level + pad, beta=1.0, c_dist="int",
+                        ldc=N + pad, name="whole_tiles_padded_c")
+    r = run_level(p, level)
+    assert r is not None
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if out == OUT_F32:
+        expect = A @ B + p.C0[:M, :N].astype(np.float64)
+        bad = np.argwhere(r[0] != expect)
+    else:
+        from helpers import f64_to_bf16_bits
+        c0 = (p.C0[:M, :N].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bad = np.argwhere(r[1] != f64_to_bf16_bits(A @ B + c0))
+    assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
+
+
 @pytest.mark.parametrize("level", [5, 6, 9, None])
 @pytest.mark.parametrize("fmt,shape,alpha", [(BF16, (2048, 1536, 512), 1.0), (BF16, (4096, 4352, 256), 0.5),
                                              (E4M3FN, (2048, 1536, 1024), 1.0)],
