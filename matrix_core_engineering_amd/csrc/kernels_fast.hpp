@@ -152,7 +152,7 @@ template <int RR> constexpr int epi_wave_bytes() { return RR * EPI_PITCH; }
 template <class G, int BM, int BN, int RR>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
                                                int m_tile, int n_tile, int wm, int wn, int lane,
-                                               char *buf)
+                                               char *buf, bool full)
 {
     static_assert(G::TJ % 2 == 0, "blocks staged in pairs");
     static_assert(RR == 8 || RR == 16 || RR == 32, "rows per round");
@@ -178,13 +178,36 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
                     }
             }
             wait_lgkm0();
-            uint16_t *c0 = (uint16_t *)p.C + (size_t)(m_tile + wm * G::WM + i * 32 + half * RR) * p.ldc +
-                           n_tile + wn * G::WN + jp * 64 + rchunk * 8;
+            const int mr = m_tile + wm * G::WM + i * 32 + half * RR;     // the round's first row
+            const int nc = n_tile + wn * G::WN + jp * 64 + rchunk * 8;   // this lane's first column
+            uint16_t *c0 = (uint16_t *)p.C + (size_t)mr * p.ldc + nc;
+            if (full) {
 #pragma unroll
-            for (int s = 0; s < RR / 8; ++s) {
-                const int row = s * 8 + rrow;
-                const intx4 v = *(const intx4 *)(buf + row * EPI_PITCH + rchunk * 16);
-                *(intx4 *)(c0 + (size_t)row * p.ldc) = v;
+                for (int s = 0; s < RR / 8; ++s) {
+                    const int row = s * 8 + rrow;
+                    const intx4 v = *(const intx4 *)(buf + row * EPI_PITCH + rchunk * 16);
+                    *(intx4 *)(c0 + (size_t)row * p.ldc) = v;
+                }
+            } else {
+                // a tile crossing the M or N edge: rows past M are skipped,
+                // a piece crossing N is stored per element
+#pragma unroll
+                for (int s = 0; s < RR / 8; ++s) {
+                    const int row = s * 8 + rrow;
+                    const intx4 v = *(const intx4 *)(buf + row * EPI_PITCH + rchunk * 16);
+                    if (mr + row < p.M) {
+                        uint16_t *dst = c0 + (size_t)row * p.ldc;
+                        if (nc + 8 <= p.N) {
+                            *(intx4 *)dst = v;
+                        } else {
+                            const u16x8 e8 = __builtin_bit_cast(u16x8, v);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (nc + e < p.N)
+                                    dst[e] = e8[e];
+                        }
+                    }
+                }
             }
             // the next round's writes may not overtake these reads
             wait_lgkm0();
@@ -205,7 +228,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs &p, floatx16 (&acc
 template <class G, int BM, int BN, int RR, bool BF16B = false>
 __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs &p, floatx16 (&acc)[G::TI][G::TJ],
                                                    int m_tile, int n_tile, int wm, int wn, int lane,
-                                                   char *buf)
+                                                   char *buf, bool full)
 {
     static_assert(RR == 8 || RR == 16 || RR == 32, "rows per round");
     const int h = lane >> 5, l32 = lane & 31;
@@ -226,27 +249,47 @@ __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs &p, floatx16 (
                 }
             }
             wait_lgkm0();
-            const size_t e0 = (size_t)(m_tile + wm * G::WM + i * 32 + half * RR) * p.ldc + n_tile + wn * G::WN +
-                              j * 32 + rchunk * 4;
+            const int mr = m_tile + wm * G::WM + i * 32 + half * RR;     // the round's first row
+            const int nc = n_tile + wn * G::WN + j * 32 + rchunk * 4;    // this lane's first column
+            const size_t e0 = (size_t)mr * p.ldc + nc;
 #pragma unroll
             for (int s = 0; s < RR / 8; ++s) {
                 const int row = s * 8 + rrow;
                 floatx4 v = *(const floatx4 *)(buf + row * EPI_PITCH + rchunk * 16);
-                if constexpr (BF16B) {
-                    u16x4 *dst = (u16x4 *)((uint16_t *)p.C + e0 + (size_t)row * p.ldc);
-                    const u16x4 c = *dst;
-                    u16x4 o;
+                const bool in = full || (mr + row < p.M && nc + 4 <= p.N);
+                if (in) {
+                    if constexpr (BF16B) {
+                        u16x4 *dst = (u16x4 *)((uint16_t *)p.C + e0 + (size_t)row * p.ldc);
+                        const u16x4 c = *dst;
+                        u16x4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c[e]), v[e]));
-                    *dst = o;
-                } else {
-                    floatx4 *dst = (floatx4 *)((float *)p.C + e0 + (size_t)row * p.ldc);
-                    if (p.beta != 0.0f) {
-                        const floatx4 c = *dst;
-                        v += p.beta * c;
+                        for (int e = 0; e < 4; ++e)
+                            o[e] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c[e]), v[e]));
+                        *dst = o;
+                    } else {
+                        floatx4 *dst = (floatx4 *)((float *)p.C + e0 + (size_t)row * p.ldc);
+                        if (p.beta != 0.0f) {
+                            const floatx4 c = *dst;
+                            v += p.beta * c;
+                        }
+                        *dst = v;
                     }
-                    *dst = v;
+                } else if (mr + row < p.M) {
+                    // a piece crossing the N edge, per element, the same
+                    // operations (store_c: alpha * acc, then fma with C0)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (nc + e >= p.N)
+                            continue;
+                        const size_t idx = e0 + (size_t)row * p.ldc + e;
+                        if constexpr (BF16B) {
+                            uint16_t *c = (uint16_t *)p.C;
+                            c[idx] = f32_to_bf16_rne(__builtin_fmaf(p.beta, bf16_to_f32(c[idx]), v[e]));
+                        } else {
+                            float *c = (float *)p.C;
+                            c[idx] = p.beta != 0.0f ? __builtin_fmaf(p.beta, c[idx], v[e]) : v[e];
+                        }
+                    }
                 }
             }
             // the next round's writes may not overtake these reads
@@ -1056,12 +1099,13 @@ void gemm_early(GemmArgs p, int group_m)
                                         smem + G::LDS_BYTES + SG_BYTES + wave * epi_wave_bytes<EPI_RR>());
         else if constexpr (EPI == EPI_BF16_LDS)
             store_tile_lds<G, BM, BN, EPI_RR>(p, acc, tm * BM, tn * BN, wm, wn, lane_e,
-                                              smem + G::LDS_BYTES + SG_BYTES +
-                                                  wave * epi_wave_bytes<EPI_RR>());
+                                              smem + G::LDS_BYTES + SG_BYTES + wave * epi_wave_bytes<EPI_RR>(),
+                                              (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N);
         else if constexpr (EPI == EPI_F32_LDS || EPI == EPI_BF16B_LDS)
             store_tile_lds_f32<G, BM, BN, EPI_RR, EPI == EPI_BF16B_LDS>(
                 p, acc, tm * BM, tn * BN, wm, wn, lane_e,
-                smem + G::LDS_BYTES + SG_BYTES + wave * epi_wave_bytes<EPI_RR>());
+                smem + G::LDS_BYTES + SG_BYTES + wave * epi_wave_bytes<EPI_RR>(),
+                (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N);
         else
             store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
         // the load side moves one tile ahead
@@ -1349,18 +1393,21 @@ bool whole_bf16(const GemmArgs &p, int bm, int bn)
            p.ldc % 4 == 0 && ((uintptr_t)p.C % 8) == 0;
 }
 
-// fp32 C of whole tiles with 16-byte aligned rows (any beta)
-bool whole_f32(const GemmArgs &p, int bm, int bn)
+// The early-release ring's LDS-staged epilogues (edge tiles masked per row
+// and per piece inside them): bf16 C with beta == 0 and 16-byte aligned
+// rows; fp32 C with 16-byte aligned rows (any beta); bf16 C with beta != 0
+// and 8-byte aligned rows.
+bool staged_bf16(const GemmArgs &p)
 {
-    return p.c_dtype == OUT_F32 && p.M % bm == 0 && p.N % bn == 0 && p.ldc % 4 == 0 &&
-           ((uintptr_t)p.C % 16) == 0;
+    return p.c_dtype == OUT_BF16 && p.beta == 0.0f && p.ldc % 8 == 0 && ((uintptr_t)p.C % 16) == 0;
 }
-
-// bf16 C of whole tiles with beta != 0 and 8-byte aligned rows
-bool whole_bf16_beta(const GemmArgs &p, int bm, int bn)
+bool staged_f32(const GemmArgs &p)
 {
-    return p.c_dtype == OUT_BF16 && p.beta != 0.0f && p.M % bm == 0 && p.N % bn == 0 && p.ldc % 4 == 0 &&
-           ((uintptr_t)p.C % 8) == 0;
+    return p.c_dtype == OUT_F32 && p.ldc % 4 == 0 && ((uintptr_t)p.C % 16) == 0;
+}
+bool staged_bf16_beta(const GemmArgs &p)
+{
+    return p.c_dtype == OUT_BF16 && p.beta != 0.0f && p.ldc % 4 == 0 && ((uintptr_t)p.C % 8) == 0;
 }
 
 template <class Op, int BM, int BN, int STAGES, bool PERSIST>
@@ -1394,16 +1441,16 @@ hipError_t launch_early(const GemmArgs &p, hipStream_t s)
     int grid = ntiles;
     if (PERSIST)
         grid = ntiles < p.ncu ? ntiles : p.ncu;
-    if (whole_bf16(p, BM, BN) && p.ldc % 8 == 0 && (uintptr_t)p.C % 16 == 0)
+    if (staged_bf16(p))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
     else if (whole_bf16(p, BM, BN))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
-    else if (whole_f32(p, BM, BN))
+    else if (staged_f32(p))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_F32_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
-    else if (whole_bf16_beta(p, BM, BN))
+    else if (staged_bf16_beta(p))
         hipLaunchKernelGGL((gemm_early<Op, BM, BN, PERSIST, EPI_BF16B_LDS>), dim3(grid), dim3(64 * Op::WAVES), 0,
                            s, p, group_m);
     else
