@@ -74,7 +74,17 @@ void gemm_mx_mn(GemmArgs p, int group_m)
     using R = MnRing<SG>;
     constexpr int BM = MN_BM, BN = MN_BN, NL = MN_NL, TI = G::TI, TJ = G::TJ;
     constexpr int MN_STAGE = R::STAGE, MN_LOADS = R::LOADS;
-    __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+    // (the LDS-staged epilogue of bf16 C with beta = 0: one buffer per wave
+    // after the ring, of 32, 16 or 8 rows, whatever the ring leaves.  fp32
+    // C, staged a block per round through buffers this small, measured
+    // slower than the register path here and is not launched.)
+    constexpr bool STAGED = EPI == EPI_BF16_LDS;
+    constexpr int ERR = R::LDS + 4 * epi_wave_bytes<32>() <= 160 * 1024   ? 32
+                        : R::LDS + 4 * epi_wave_bytes<16>() <= 160 * 1024 ? 16
+                                                                          : 8;
+    constexpr int EPI_BYTES = STAGED ? 4 * epi_wave_bytes<ERR>() : 0;
+    static_assert(R::LDS + EPI_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[R::LDS + EPI_BYTES];
     char *const groups = smem + MN_S * MN_STAGE;   // scale groups: 2 x R::GROUP
 
     const int lane = threadIdx.x & 63;
@@ -321,7 +331,14 @@ void gemm_mx_mn(GemmArgs p, int group_m)
                 sb_c[j] = sb_n[j];
             stage = nstage;
         }
-        store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+        {
+            const bool full = (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
+            char *ebuf = smem + R::LDS + wave * epi_wave_bytes<ERR>();
+            if constexpr (EPI == EPI_BF16_LDS)
+                store_tile_lds<G, BM, BN, ERR>(p, acc, tm * BM, tn * BN, wm, wn, lane_id_here(), ebuf, full);
+            else
+                store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+        }
         cur = span(r + 1);
     }
     wait_vmcnt<0>();
@@ -336,7 +353,10 @@ hipError_t launch_mn(const GemmArgs &p, hipStream_t s)
     if (PERSIST && ntiles <= p.ncu)
         return launch_mn<FMT, A_MN, B_MN, SG, false>(p, s);
     const int grid = PERSIST ? (ntiles < p.ncu ? ntiles : p.ncu) : ntiles;
-    if (whole_bf16(p, MN_BM, MN_BN))
+    if (staged_bf16(p))
+        hipLaunchKernelGGL((gemm_mx_mn<FMT, A_MN, B_MN, SG, PERSIST, EPI_BF16_LDS>), dim3(grid), dim3(256), 0,
+                           s, p, group_m);
+    else if (whole_bf16(p, MN_BM, MN_BN))
         hipLaunchKernelGGL((gemm_mx_mn<FMT, A_MN, B_MN, SG, PERSIST, EPI_BF16_WHOLE>), dim3(grid), dim3(256), 0,
                            s, p, group_m);
     else
