@@ -336,12 +336,27 @@ __device__ __forceinline__ void store_tile_lds16(const GemmArgs &p, floatx4 (&ac
         }
 }
 
+// Rows per round of an LDS-staged epilogue that fits beside `lds` bytes of
+// ring for four waves (0: none fits).
+constexpr int staged_rr(int lds)
+{
+    return lds + 4 * epi_wave_bytes<32>() <= 160 * 1024   ? 32
+           : lds + 4 * epi_wave_bytes<16>() <= 160 * 1024 ? 16
+           : lds + 4 * epi_wave_bytes<8>() <= 160 * 1024  ? 8
+                                                            : 0;
+}
+
 template <class Op, int BM, int BN, int STAGES, bool PERSIST, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fast(GemmArgs p, int group_m)
 {
     using G = Geometry<Op, BM, BN, STAGES>;
-    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+    // the LDS-staged epilogues' buffers (one per wave) follow the ring
+    constexpr bool STAGED = EPI == EPI_BF16_LDS || EPI == EPI_F32_LDS || EPI == EPI_BF16B_LDS;
+    constexpr int ERR = staged_rr(G::LDS_BYTES);
+    static_assert(!STAGED || ERR > 0, "LDS budget of the staged epilogue");
+    constexpr int EPI_BYTES = STAGED ? 4 * epi_wave_bytes<(ERR > 0 ? ERR : 8)>() : 0;
+    __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES + EPI_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -502,7 +517,18 @@ void gemm_fast(GemmArgs p, int group_m)
     auto epilogue = [&](int tile_id) {
         int tm, tn;
         grouped_tile(tile_id, tiles_m, tiles_n, group_m, tm, tn);
-        store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+        if constexpr (STAGED) {
+            constexpr int RR = ERR > 0 ? ERR : 8;
+            const bool full = (tm + 1) * BM <= p.M && (tn + 1) * BN <= p.N;
+            char *ebuf = smem + G::LDS_BYTES + wave * epi_wave_bytes<RR>();
+            if constexpr (EPI == EPI_BF16_LDS)
+                store_tile_lds<G, BM, BN, RR>(p, acc, tm * BM, tn * BN, wm, wn, lane_id_here(), ebuf, full);
+            else
+                store_tile_lds_f32<G, BM, BN, RR, EPI == EPI_BF16B_LDS>(p, acc, tm * BM, tn * BN, wm, wn,
+                                                                       lane_id_here(), ebuf, full);
+        } else {
+            store_tile<EPI, G, BM, BN>(p, acc, tm * BM, tn * BN, wm, wn, h, l32);
+        }
     };
 
     // ------------------------------------------------------------ K loop
@@ -1419,8 +1445,24 @@ hipError_t launch(const GemmArgs &p, hipStream_t s)
     int grid = ntiles;
     if (PERSIST)
         grid = ntiles < p.ncu ? ntiles : p.ncu;
-    if (whole_bf16(p, BM, BN))
+    // the staged epilogues where their buffers fit (bf16 pairs blocks, so
+    // it needs an even number of 32-column blocks per wave); fp32 with a
+    // beta term stays on the register path, which measured faster here:
+    // it has every C load of the tile in flight at once, while the staged
+    // path waits for C once per round
+    using G = Geometry<Op, BM, BN, STAGES>;
+    constexpr bool fits = staged_rr(G::LDS_BYTES) > 0;
+    if (fits && G::TJ % 2 == 0 && staged_bf16(p))
+        hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, (fits && G::TJ % 2 == 0 ? EPI_BF16_LDS : EPI_ANY)>),
+                           dim3(grid), dim3(256), 0, s, p, group_m);
+    else if (whole_bf16(p, BM, BN))
         hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, EPI_BF16_WHOLE>), dim3(grid),
+                           dim3(256), 0, s, p, group_m);
+    else if (fits && staged_f32(p) && p.beta == 0.0f)
+        hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, (fits ? EPI_F32_LDS : EPI_ANY)>), dim3(grid),
+                           dim3(256), 0, s, p, group_m);
+    else if (fits && staged_bf16_beta(p))
+        hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, (fits ? EPI_BF16B_LDS : EPI_ANY)>), dim3(grid),
                            dim3(256), 0, s, p, group_m);
     else
         hipLaunchKernelGGL((gemm_fast<Op, BM, BN, STAGES, PERSIST, EPI_ANY>), dim3(grid), dim3(256),

@@ -808,6 +808,67 @@ def test_whole_tiles_bf16_output_beta_bitwise(level, fmt, shape, alpha):
     assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
 
 
+def _exact_check(p, r, beta):
+    """The whole result against the float64 A B + beta C0 of an
+    exact-integer problem: fp32 output equal, bf16 output the correctly
+    rounded value."""
+    from helpers import f64_to_bf16_bits, torch_decode_scales
+    M, N = p.M, p.N
+    A = logical(torch_decode_elements(p.A, p.fmt), p.M, p.K, p.a_col_major)
+    B = logical(torch_decode_elements(p.B, p.fmt), p.K, p.N, p.b_col_major)
+    if p.fmt == E4M3FN:
+        A = A * np.repeat(torch_decode_scales(p.SA), 32, axis=1)[:, :p.K]
+        B = B * np.repeat(torch_decode_scales(p.SB), 32, axis=1)[:, :p.K].T
+    expect = A @ B
+    if p.c_dtype == OUT_F32:
+        if beta != 0.0:
+            expect = expect + beta * p.C0[:M, :N].astype(np.float64)
+        bad = np.argwhere(r[0] != expect)
+    else:
+        if beta != 0.0:
+            expect = expect + beta * (p.C0[:M, :N].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bad = np.argwhere(r[1] != f64_to_bf16_bits(expect))
+    assert bad.size == 0, f"{len(bad)} entries differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("level", [4, 5, 6])
+@pytest.mark.parametrize("shape", [(4000, 4100, 1000), (2000, 2100, 1000), (1000, 1800, 1000)],
+                         ids=["256-tiles", "128-tiles", "128x64-tiles"])
+@pytest.mark.parametrize("out,beta", [(OUT_F32, 0.0), (OUT_BF16, 0.0), (OUT_BF16, 1.0), (OUT_F32, 1.0)],
+                         ids=["f32", "bf16", "bf16-beta1", "f32-beta1"])
+def test_partial_k_tile_ragged_bitwise(level, shape, out, beta):
+    """K = 1000 is not a whole number of 64-wide K tiles, so levels 4-6 take
+    the direct-load kernel (256x256, 128x128 or 128x64 tiles by problem
+    size; 272 tiles of 256x256 also run a ragged persistent tail at level 6)
+    with M and N not multiples of the tile: whole tiles stored through the
+    LDS-staged epilogues, edge tiles masked inside them, fp32 with beta on
+    the register path.  Exact-integer inputs, C0 in -1..1."""
+    M, N, K = shape
+    announce(f"partial K tile level {level} {shape} out {out} beta {beta}")
+    p = integer_problem(M, N, K, c_dtype=out, seed=7800 + level + M, beta=beta, c_dist="int",
+                        name="partial_k_tile")
+    r = run_level(p, level)
+    assert r is not None
+    _exact_check(p, r, beta)
+
+
+@pytest.mark.parametrize("level", [5, 6])
+@pytest.mark.parametrize("out,beta", [(OUT_F32, 0.0), (OUT_BF16, 0.0), (OUT_BF16, 1.0)],
+                         ids=["f32", "bf16", "bf16-beta1"])
+def test_partial_k_tile_mx_ragged_bitwise(level, out, beta):
+    """MX E4M3 with K = 1056 (33 scale blocks, not a whole number of
+    128-wide K tiles; scale rows padded to 36 bytes for 4-byte loads):
+    the direct-load kernel with ragged M and N and the staged epilogues, as
+    above."""
+    M, N, K = 4000, 4100, 1056
+    announce(f"partial K tile mx level {level} out {out} beta {beta}")
+    p = integer_problem(M, N, K, fmt=E4M3FN, c_dtype=out, seed=7900 + level, beta=beta, c_dist="int",
+                        ld_sa=36, ld_sb=36, name="partial_k_tile_mx")
+    r = run_level(p, level)
+    assert r is not None
+    _exact_check(p, r, beta)
+
+
 @pytest.mark.parametrize("shape", [mce.MCE_LOOP_BF16_32X32X16, mce.MCE_LOOP_BF16_16X16X32,
                                    mce.MCE_LOOP_MXFP8_32X32X64, mce.MCE_LOOP_MXFP4_32X32X64,
                                    mce.MCE_LOOP_MXFP6_32X32X64])
