@@ -852,6 +852,26 @@ def test_partial_k_tile_ragged_bitwise(level, shape, out, beta):
     _exact_check(p, r, beta)
 
 
+@pytest.mark.parametrize("shape", [(4000, 4100, 1000), (1000, 1800, 1000)], ids=["256-tiles", "128x64-tiles"])
+@pytest.mark.parametrize("out,beta", [(OUT_F32, 0.0), (OUT_BF16, 0.0), (OUT_BF16, 1.0)],
+                         ids=["f32", "bf16", "bf16-beta1"])
+@pytest.mark.parametrize("pad", [4, 1], ids=["aligned-pad", "unaligned-pad"])
+def test_partial_k_tile_padded_c_rows_bitwise(shape, out, beta, pad):
+    """The direct-load kernel (level 6, K = 1000) with padded C rows: a pad
+    of 4 elements keeps 16-byte pieces aligned for fp32 and 8-byte pieces
+    for bf16 (the staged stores at a row pitch other than N; bf16 with
+    beta = 0 needs 8-element rows and takes the register path), a pad of 1
+    does not (the register path).  Guard columns past N keep their C0
+    values (checked by the runner); the result is exact."""
+    M, N, K = shape
+    announce(f"partial K tile padded C {shape} out {out} beta {beta} pad {pad}")
+    p = integer_problem(M, N, K, c_dtype=out, seed=8000 + pad + M, beta=beta, c_dist="int", ldc=N + pad,
+                        name="partial_k_tile_padded_c")
+    r = run_level(p, 6)
+    assert r is not None
+    _exact_check(p, r, beta)
+
+
 @pytest.mark.parametrize("level", [5, 6])
 @pytest.mark.parametrize("out,beta", [(OUT_F32, 0.0), (OUT_BF16, 0.0), (OUT_BF16, 1.0)],
                          ids=["f32", "bf16", "bf16-beta1"])
